@@ -1,0 +1,248 @@
+"""Benchmark of the ZeRO partitioned mixed-precision Adam shard step on one
+MI355X.
+
+A step is the whole hot path on one data-parallel rank's shard:
+flatten (per-layer fp16 grads -> flat partition) -> exact norm/overflow +
+decision -> fused unscale/clip/AdamW/fp16-copy.  Default workload: the
+GPT-2 1.5B-like model (48 layers, hidden 1600, vocab 50257) partitioned over
+Nd = 16, rank 8: 97,350,700 parameters from 39 per-layer gradient segments.
+Inputs (fp32 masters, per-layer fp16 gradients) are synthetic, seeded, and
+resident in HBM before the timed region; four gradient sets are generated up
+front and used in turn.
+
+stdout: one JSON line.  Progress goes to stderr.
+  value            whole-step parameters per second
+  roofline         the Adam kernel (the dominant one): algorithmic bytes per
+                   launch (28 per parameter) / its mean duration, measured with
+                   HIP events on the launch stream inside the timed region,
+                   against the 8 TB/s HBM peak; `traffic` is the measured HBM
+                   bytes per launch from the committed rocprofv3 counter
+                   summary when it was taken on the current kernel source
+  cpu_baseline     the CPU oracle (single thread) on a bounded number of full
+                   steps of the same shard
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shard Adam-step params/sec + achieved HBM GB/s (% of peak) at 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+ADAM_BYTES = 28          # read fp16 g + fp32 p,m,v; write fp32 p,m,v + fp16 p
+NORM_BYTES = 2           # read fp16 g
+FLATTEN_BYTES = 4        # read fp16 source, write fp16 partition
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "adam_step_gpt2_shard_pmc.json")
+ADAM_SOURCE = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc", "adam.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(n):
+    """HBM bytes per Adam launch from the committed counter summary, or None
+    when it is missing, for another shard size, or for another kernel source."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("adam_source_sha256_16") != source_hash(ADAM_SOURCE) or s.get("n") != n:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, p32, grads_host, budget_s):
+    import numpy as np
+    import oracle as O
+    import shardgen
+    hp = O.hparams()
+    st = O.new_state(w.scale0)
+    p = p32.copy()
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    p16 = shardgen.to_f16_bits(p)
+    grad = np.empty(w.n, np.uint16)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        srcs = grads_host[steps % len(grads_host)]
+        O.step(hp, st, srcs, w.layout.segments, grad, p16, p, m, v)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 20:
+            break
+    return {"value": w.n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full step(s) of the same {w.n:,}-parameter shard (flatten + exact norm + "
+                      f"decision + fp32 AdamW + fp16 copy), single-threaded C, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2", choices=["tiny", "gpt2", "100b", "1t"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="run only the streaming-copy reference (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's shard step only: every box here has a single GPU and this "
+              "build has no multi-GPU path (see DESIGN.md for how the step would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import shardgen
+    import zero_partitioned_mixed_flatten_amd as Z
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = shardgen.workload(args.workload)
+    n = w.n
+    stream = torch.cuda.current_stream()
+
+    if args.copy_only:
+        nbytes = (ADAM_BYTES // 2) * n // 16 * 16
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            Z.zero_stream_copy(dst, src, nbytes)
+        torch.cuda.synchronize()
+        log(f"copy-only: {args.warmup + args.steps} copies of {nbytes} bytes done")
+        return
+
+    log(f"workload {shardgen.layout_summary(w.layout)}")
+    t = time.time()
+    p32 = shardgen.master_params(w)
+    nsets = 4
+    grads_host = []
+    for k in range(nsets):
+        gpart = shardgen.grad_partition(w, k + 1, w.scale0)
+        grads_host.append(shardgen.source_tensors(w.layout, gpart))
+        del gpart
+    log(f"inputs generated in {time.time() - t:.1f} s")
+
+    dev = Z.ShardStep(n)
+    dev.p32.copy_(torch.from_numpy(p32))
+    dev.p16.copy_(dev.p32.half())
+    dev.init_state(w.scale0)
+    dev_sets = []
+    for srcs in grads_host:
+        d = [torch.from_numpy(s.view(np.float16)).cuda() for s in srcs]
+        dev_sets.append(d)
+    plans = []
+    for d in dev_sets:
+        dev.set_segments(d, w.layout.segments, w.bucket_elems)
+        plans.append(dev.buckets)
+    hp = Z.hparams(w.hp.lr, w.hp.beta1, w.hp.beta2, w.hp.eps, w.hp.weight_decay, w.hp.max_grad_norm,
+                   w.hp.backoff, w.hp.growth, w.hp.min_scale, w.hp.growth_interval)
+    torch.cuda.synchronize()
+
+    def one_step(k, ev=None):
+        dev.buckets = plans[k % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        dev.flatten()
+        if ev is not None:
+            ev[1].record(stream)
+        dev.norm_overflow(hp)
+        if ev is not None:
+            ev[2].record(stream)
+        dev.adam()
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        one_step(k)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(args.warmup + k, events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    el = t1 - t0
+    st = dev.read_state()
+    flat_ms = [e[0].elapsed_time(e[1]) for e in events]
+    norm_ms = [e[1].elapsed_time(e[2]) for e in events]
+    adam_ms = [e[2].elapsed_time(e[3]) for e in events]
+    mean = lambda xs: sum(xs) / len(xs)
+    adam_s = mean(adam_ms) / 1e3
+    achieved = ADAM_BYTES * n / adam_s / 1e9
+    log(f"step {1e3 * el / args.steps:.3f} ms; flatten {mean(flat_ms) * 1e3:.1f} us, norm {mean(norm_ms) * 1e3:.1f} us,"
+        f" adam {mean(adam_ms) * 1e3:.1f} us ({achieved:.0f} GB/s); skipped={st.skipped_total} scale={st.loss_scale:g}")
+
+    # streaming-copy reference on the same byte count as one Adam launch
+    nbytes = (ADAM_BYTES // 2) * n // 16 * 16
+    csrc = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        Z.zero_stream_copy(cdst, csrc, nbytes)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    reps = 20
+    for _ in range(reps):
+        Z.zero_stream_copy(cdst, csrc, nbytes)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes / (ce[0].elapsed_time(ce[1]) / 1e3 / reps) / 1e9
+    del csrc, cdst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds)
+
+    traffic = measured_traffic(n)
+    step_bytes = (ADAM_BYTES + NORM_BYTES + FLATTEN_BYTES) * n
+    out = {
+        "metric": METRIC,
+        "value": n * args.steps / el,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * el / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard",
+                   "params": n, "segments": len(w.layout.segments), "bucket_elems": w.bucket_elems,
+                   "state": "fp16 p,g + fp32 p,m,v (16 B/param)", "loss_scale0": w.scale0,
+                   "step_bytes_per_param": ADAM_BYTES + NORM_BYTES + FLATTEN_BYTES},
+        "roofline": {"bound": "hbm", "kernel": "adam_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes": ADAM_BYTES * n},
+        "step_gbps": step_bytes / (el / args.steps) / 1e9,
+        "kernels_us": {"flatten": 1e3 * mean(flat_ms), "norm_overflow": 1e3 * mean(norm_ms),
+                       "adam_step": 1e3 * mean(adam_ms)},
+        "kernels_gbps": {"flatten": FLATTEN_BYTES * n / (mean(flat_ms) / 1e3) / 1e9,
+                         "norm_overflow": NORM_BYTES * n / (mean(norm_ms) / 1e3) / 1e9,
+                         "adam_step": achieved},
+        "copy_reference_gbps": copy_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

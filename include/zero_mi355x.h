@@ -1,0 +1,233 @@
+/*
+ * zero_mi355x.h -- C ABI of the ZeRO partitioned mixed-precision Adam step on
+ * one data-parallel rank's flat shard, for AMD Instinct MI355X (gfx950).
+ *
+ * The model state the pages fix (ZeRO paper card, section "Bottleneck"):
+ * fp16 parameters and fp16 gradients plus fp32 master parameters, fp32
+ * momentum and fp32 variance -- 16 bytes per parameter.  ZeRO partitions that
+ * state across the Nd data-parallel ranks instead of replicating it (paper
+ * card, "Method": stage 1 optimizer state, stage 2 gradients, stage 3
+ * parameters).  One rank therefore steps only its own contiguous slice of n
+ * parameters: this library is that step.
+ *
+ * The step is three calls, all asynchronous on one HIP stream, with no host
+ * synchronisation between them:
+ *   1. zero_flatten_bucket      pack per-layer fp16 gradient tensors into the
+ *                               rank's contiguous gradient partition
+ *                               (contiguous, defragmented buffers: paper card,
+ *                               "Method", ZeRO-R paragraph);
+ *   2. zero_shard_norm_overflow exact squared L2 norm + inf/NaN flag of that
+ *                               partition, then the step decision (dynamic
+ *                               loss scale, skip, clip factor, bias
+ *                               corrections) kept in device memory;
+ *   3. zero_shard_adam_step     one fused pass: unscale + clip + Adam with
+ *                               bias correction and decoupled weight decay,
+ *                               fp32 master/momentum/variance update and the
+ *                               fp16 parameter copy (28 bytes per parameter).
+ * zero_state_bytes gives the per-rank model-state bytes for each ZeRO stage.
+ *
+ * Conventions for every entry point:
+ *   - pointers named dev_* or documented as device memory are HIP device
+ *     pointers; everything else is host memory;
+ *   - the caller owns and allocates every buffer; the library allocates
+ *     nothing and keeps no pointer after a call returns;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     device work is enqueued there and the call returns without waiting;
+ *   - return value: ZERO_OK (0) or a negative ZERO_E* code; argument errors
+ *     are detected on the host before any device work is enqueued; a fault
+ *     inside a kernel surfaces at the caller's next synchronisation;
+ *   - calls on different streams with disjoint buffers may run concurrently;
+ *     two calls that share a zero_step_state_t must be ordered on one stream.
+ */
+#ifndef ZERO_MI355X_H
+#define ZERO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------- */
+#define ZERO_OK       0
+#define ZERO_EINVAL  (-1)   /* null pointer, bad dtype/stage/hyperparameter */
+#define ZERO_EALIGN  (-2)   /* a buffer is not aligned as required */
+#define ZERO_ERANGE  (-3)   /* a size or segment is out of the allowed range */
+#define ZERO_EHIP    (-4)   /* the HIP runtime refused a launch */
+
+/* Human-readable text for a status code (static storage; never NULL).
+ * For ZERO_EHIP the text of the last HIP error seen by this thread. */
+const char* zero_status_string(int code);
+
+/* ---- element types of a flatten destination ------------------------- */
+#define ZERO_F16 1          /* IEEE binary16, stored as uint16_t bit patterns */
+#define ZERO_F32 2          /* IEEE binary32 */
+
+/* One piece of a per-layer gradient tensor that lands in the partition:
+ * count elements from src[src_off ...] go to dst[dst_off ...].
+ * src is a DEVICE pointer to binary16 data; offsets and count are elements. */
+typedef struct {
+    const uint16_t* src;
+    uint64_t src_off;
+    uint64_t dst_off;
+    uint64_t count;
+} zero_segment_t;
+
+/* Hyperparameters of one step (host struct, passed by pointer).
+ * lr, beta1, beta2, eps, weight_decay: AdamW (Kingma & Ba 2015 with the
+ *   decoupled decay of Loshchilov & Hutter 2019, schedule multiplier = lr);
+ * max_grad_norm: clip threshold on the unscaled gradient norm, <= 0 = off;
+ * backoff, growth, growth_interval, min_scale: dynamic loss scaling
+ *   (Micikevicius et al. 2018) -- on an inf/NaN gradient the step is skipped
+ *   and S <- max(S*backoff, min_scale); after growth_interval consecutive
+ *   clean steps S <- S*growth (growth_interval <= 0: never grow). */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    double max_grad_norm;
+    double backoff, growth, min_scale;
+    int32_t growth_interval;
+    int32_t reserved;
+} zero_hparams_t;
+
+/* Step state in DEVICE memory (128 bytes, 8-byte aligned).  Initialise it
+ * with zero_step_state_init.  It carries the loss scaler and the Adam step
+ * count between steps, and the last decision from zero_shard_norm_overflow to
+ * zero_shard_adam_step.  The caller may copy it to the host to read it (after
+ * synchronising the stream) and may save/restore it bytewise. */
+typedef struct {
+    /* carried from step to step */
+    double   loss_scale;        /* S: gradients arrive multiplied by S */
+    double   beta1_pow;         /* beta1^t, running binary64 product */
+    double   beta2_pow;         /* beta2^t */
+    int64_t  step;              /* t: applied (not skipped) steps */
+    int32_t  good_steps;        /* clean steps since the last scale change */
+    int32_t  skipped_total;     /* skipped steps so far */
+    /* written by the last zero_shard_norm_overflow */
+    double   sumsq;             /* exact sum of squares of the scaled fp16
+                                   gradient, rounded once to binary64;
+                                   +inf when overflow is set */
+    double   grad_norm;         /* sqrt(sumsq) / S (unscaled norm); +inf on overflow */
+    int32_t  overflow;          /* 1 if any gradient element is inf or NaN */
+    int32_t  skip;              /* 1 if this step is skipped (== overflow) */
+    float    gmul;              /* fp32(coef / S): unscale and clip factor */
+    float    bc1, bc2;          /* fp32(1 - beta1^t), fp32(1 - beta2^t) */
+    float    lr, beta1, beta2;  /* fp32 hyperparameters of this step */
+    float    omb1, omb2;        /* fp32(1 - beta1), fp32(1 - beta2) */
+    float    eps, wd;
+    uint32_t done_blocks;       /* internal arrival counter; 0 between calls */
+    uint32_t reserved;
+    uint64_t sumsq_units[2];    /* the exact sum in units of 2^-48 (low, high) */
+} zero_step_state_t;
+
+/* ---- model-state arithmetic (host only, no device work) ------------- */
+
+/* Per-rank model-state bytes for a model of psi parameters over nd
+ * data-parallel ranks, with k optimizer bytes per parameter (k = 12 for the
+ * fp32 master, momentum and variance of mixed-precision Adam; paper card,
+ * "Bottleneck").  A rank owns P = ceil(psi/nd) parameters.
+ *   stage 0 (plain data parallel): (2 + 2 + k) * psi
+ *   stage 1 (optimizer state):     4 * psi + k * P
+ *   stage 2 (+ gradients):         2 * psi + (2 + k) * P
+ *   stage 3 (+ parameters):        (2 + 2 + k) * P
+ * (paper card, "Method": 4x, 8x and Nd-proportional reductions; "Evidence":
+ * 1T parameters -> about 16 TB, about 16 GB per GPU over 1024 GPUs.)
+ * Errors: ZERO_EINVAL (out_bytes NULL, nd == 0, stage not 0..3),
+ *         ZERO_ERANGE (the result does not fit in 64 bits). */
+int zero_state_bytes(uint64_t psi, uint32_t nd, uint32_t k, int stage, uint64_t* out_bytes);
+
+/* Cut a segment list (sorted or not) to the destination window
+ * [begin, end): every part of a segment whose dst range falls inside the
+ * window is written to out (host array of cap entries), in input order.
+ * This is how a partition is flattened in fixed-size buckets (paper card,
+ * "Method": temporary buffers sized to balance memory and throughput).
+ * Errors: ZERO_EINVAL (NULL pointers, begin > end), ZERO_ERANGE (more than
+ * cap pieces; *out_n then holds the number needed). */
+int zero_bucket_segments(const zero_segment_t* segs, uint32_t nsegs, uint64_t begin,
+                         uint64_t end, zero_segment_t* out, uint32_t cap, uint32_t* out_n);
+
+/* ---- device step ----------------------------------------------------- */
+
+/* Enqueue the initialisation of a step state: loss_scale = initial_scale,
+ * beta powers 1, step and all counters 0.  dev_state: device, 8-byte aligned.
+ * Errors: ZERO_EINVAL (NULL, initial_scale not finite and > 0),
+ *         ZERO_EALIGN, ZERO_EHIP. */
+int zero_step_state_init(zero_step_state_t* dev_state, double initial_scale, void* stream);
+
+/* Flatten: for each segment, dst[dst_off + i] <- src[src_off + i], i < count.
+ *   dst_dtype ZERO_F16, accumulate 0: bit copy of the binary16 values;
+ *   dst_dtype ZERO_F16, accumulate 1: dst = fp16(dst + src) (correctly
+ *                                     rounded binary16 addition);
+ *   dst_dtype ZERO_F32, accumulate 0: dst = fp32(src) (exact);
+ *   dst_dtype ZERO_F32, accumulate 1: dst = dst + fp32(src) (binary32 add).
+ * segs: HOST array of nsegs entries (the src pointers inside are device
+ * pointers); dst: device, dst_len elements, 16-byte aligned.  Destination
+ * elements no segment covers are not touched.  Segment destinations must not
+ * overlap each other (the result of overlapping segments is unspecified).
+ * Any number of segments; the library may split them over several launches.
+ * Errors: ZERO_EINVAL (NULL dst/segs with nsegs > 0, NULL src, bad dtype),
+ *         ZERO_ERANGE (dst_off + count > dst_len), ZERO_EALIGN (dst base or
+ *         a src pointer not 2-byte aligned, dst base not 16-byte aligned),
+ *         ZERO_EHIP. */
+int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, void* dst, uint64_t dst_len,
+                        int dst_dtype, int accumulate, void* stream);
+
+/* Bytes of device workspace zero_shard_norm_overflow needs for n elements
+ * (per-block partial sums; fixed for a given n). */
+size_t zero_norm_workspace_bytes(uint64_t n);
+
+/* Reduce and decide.  Over the n binary16 gradient elements at grad16:
+ *   overflow = 1 if any element has an all-ones exponent (inf or NaN);
+ *   sumsq    = the exact sum of squares, rounded once to binary64
+ *              (+inf on overflow);
+ * then, from the state in dev_state and the hyperparameters in hp:
+ *   overflow -> skip = 1, S <- max(S*backoff, min_scale), good_steps <- 0;
+ *   otherwise -> skip = 0, t += 1, beta powers advance,
+ *               grad_norm = sqrt(sumsq)/S,
+ *               coef = grad_norm > max_grad_norm > 0 ? max_grad_norm/grad_norm : 1,
+ *               gmul = fp32(coef/S), bc1/bc2 = fp32(1 - beta^t),
+ *               good_steps += 1 and S <- S*growth every growth_interval.
+ * All of it is written into dev_state for zero_shard_adam_step.  Result bits
+ * do not depend on the launch configuration (the sum is exact).
+ * grad16: device, 16-byte aligned; n may be 0; hp: host;
+ * dev_state: device, 8-byte aligned, initialised by zero_step_state_init;
+ * workspace: device, 16-byte aligned, >= zero_norm_workspace_bytes(n),
+ * contents need no initialisation.
+ * Errors: ZERO_EINVAL (NULL, hyperparameters out of range: lr < 0,
+ *         beta not in [0,1), eps <= 0, weight_decay < 0, backoff not in
+ *         (0,1], growth < 1, min_scale <= 0, any non-finite value),
+ *         ZERO_EALIGN, ZERO_ERANGE (workspace too small), ZERO_EHIP. */
+int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hparams_t* hp,
+                             zero_step_state_t* dev_state, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* The fused element update, in binary32 with one rounding per operation and
+ * this order (unless dev_state says skip, in which case nothing is written):
+ *   g  = fp32(grad16[i]) * gmul
+ *   m  = beta1*m32[i] + omb1*g
+ *   v  = beta2*v32[i] + omb2*(g*g)
+ *   u  = (m/bc1) / (sqrt(v/bc2) + eps) + wd*p32[i]
+ *   p  = p32[i] - lr*u
+ *   m32[i] = m; v32[i] = v; p32[i] = p; p16[i] = fp16(p) (round to nearest even)
+ * It reads 2 + 12 bytes and writes 12 + 2 bytes per parameter.
+ * All five arrays: device, n elements, 16-byte aligned, index-aligned with
+ * each other and with the grad16 the decision was made on; n may be 0.
+ * dev_state: as left by zero_shard_norm_overflow (read only here).
+ * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_EHIP. */
+int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32,
+                         const uint16_t* grad16, uint64_t n,
+                         const zero_step_state_t* dev_state, void* stream);
+
+/* ---- measurement reference ------------------------------------------ */
+
+/* A plain streaming copy of `bytes` bytes (dst and src device, 16-byte
+ * aligned, bytes a multiple of 16), used to measure the attainable HBM
+ * bandwidth next to the step's kernels.  Errors: ZERO_EINVAL, ZERO_EALIGN,
+ * ZERO_EHIP. */
+int zero_stream_copy(void* dst, const void* src, uint64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_MI355X_H */

@@ -265,14 +265,36 @@ def injection_position(w: Workload, step: int) -> int:
     return int(np.random.default_rng(np.random.SeedSequence([w.seed, 3, step])).integers(w.n))
 
 
+def scaled_f16_normals(n: int, words: Sequence[int], sigma: float, scale: float) -> np.ndarray:
+    """f16(z * sigma * scale) bit patterns for the standard normals z of
+    stream `words` (same draws as standard_normal_f32); the fp32 products and
+    the numpy round-to-nearest-even cast are done chunk by chunk in threads."""
+    out = np.empty(n, np.uint16)
+    sig, sc = np.float32(sigma), np.float32(scale)
+
+    def fill(j: int) -> None:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([*words, j])))
+        lo, hi = j * CHUNK, min(n, (j + 1) * CHUNK)
+        z = g.standard_normal(hi - lo, dtype=np.float32)
+        z *= sig
+        z *= sc
+        out[lo:hi] = to_f16_bits(z)
+
+    chunks = range(-(-n // CHUNK))
+    if n > CHUNK and _THREADS > 1:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for j in chunks:
+            fill(j)
+    return out
+
+
 def grad_partition(w: Workload, step: int, scale: float) -> np.ndarray:
     """The rank's flat binary16 gradient for 1-based `step`, scaled by the
     current loss scale: f16(g_true * S) with g_true ~ N(0, sigma_g) in fp32.
     Injected inf/NaN patterns are written after the conversion."""
-    g = standard_normal_f32(w.n, [w.seed, 2, step])
-    g *= np.float32(w.sigma_g)
-    g *= np.float32(scale)
-    bits = to_f16_bits(g)
+    bits = scaled_f16_normals(w.n, [w.seed, 2, step], w.sigma_g, scale)
     if step in w.inject:
         bits[injection_position(w, step)] = w.inject[step]
     return bits

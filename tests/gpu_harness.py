@@ -1,0 +1,191 @@
+"""Parity harness for the GPU tests: runs the HIP path and the oracle on the
+same seeded inputs, step by step, and compares.
+
+Full mode keeps the oracle's whole state.  Sampled mode (full-size shards)
+keeps the oracle's state only at a fixed set of indices: the update is
+elementwise, so the oracle computes those elements exactly as it would in a
+full run, while the decision that drives them (exact norm, overflow, loss
+scale, clip factor, bias corrections) still comes from the oracle's own pass
+over the whole flattened gradient.
+
+Contract checked every step:
+  * flattened gradient: bitwise equal to the oracle's flatten;
+  * step state: overflow, skip, loss scale, counters, exact sum (as a
+    128-bit integer), sumsq, grad_norm and every fp32 factor bitwise;
+  * fp16 parameters: bitwise; fp32 p, m, v: max relative error <= 1e-6
+    (the count of elements that are not bitwise equal is reported; 0 is
+    expected since both sides perform the same IEEE operations in the same
+    order);
+  * over the whole shard, p16 == fp16(p32) (torch's own cast).
+"""
+from __future__ import annotations
+
+import math
+import time
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle as O
+import shardgen
+import zero_partitioned_mixed_flatten_amd as Z
+
+FP32_REL_TOL = 1e-6
+TINY = float(np.finfo(np.float32).tiny)
+
+
+def log(msg: str) -> None:
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def to_dev16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(a.view(np.float16)).cuda()
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    if got.size == 0:
+        return 0.0
+    d = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    return float(np.max(d / np.maximum(np.abs(ref.astype(np.float64)), TINY)))
+
+
+def oracle_hparams(hp: shardgen.HParams) -> O.OracleHParams:
+    return O.hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_grad_norm, hp.backoff,
+                     hp.growth, hp.min_scale, hp.growth_interval)
+
+
+def device_hparams(hp: shardgen.HParams) -> Z.HParams:
+    return Z.hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_grad_norm, hp.backoff,
+                     hp.growth, hp.min_scale, hp.growth_interval)
+
+
+STATE_FIELDS = ("loss_scale", "beta1_pow", "beta2_pow", "step", "good_steps", "skipped_total", "overflow",
+                "skip")
+STEP_FIELDS = ("sumsq", "grad_norm", "gmul", "bc1", "bc2", "lr", "beta1", "beta2", "omb1", "omb2", "eps", "wd")
+
+
+def compare_state(dev: Z.StepState, ref: O.OracleState, exact_units: Optional[int]) -> None:
+    for f in STATE_FIELDS:
+        assert getattr(dev, f) == getattr(ref, f), (f, getattr(dev, f), getattr(ref, f))
+    fields = STEP_FIELDS if not ref.skip else ("sumsq", "grad_norm")
+    for f in fields:
+        a, b = getattr(dev, f), getattr(ref, f)
+        if isinstance(a, float) and math.isnan(a):
+            assert math.isnan(b), f
+        else:
+            assert np.float64(a).tobytes() == np.float64(b).tobytes(), (f, a, b)
+    if exact_units is not None and not ref.skip:
+        assert dev.as_dict()["sumsq_units"] == exact_units
+
+
+def exact_units(grad: np.ndarray) -> int:
+    """sum of squares of finite binary16 values in units of 2^-48, as a Python
+    integer: each square * 2^48 is an integer below 2^80, split exactly into
+    40-bit halves that numpy can add in int64 chunk by chunk."""
+    total = 0
+    for lo in range(0, grad.size, 1 << 22):
+        x = grad[lo:lo + (1 << 22)].view(np.float16).astype(np.float64)
+        v = x * x * 2.0 ** 48
+        hi = np.floor(v / 2.0 ** 40)
+        total += (int(hi.astype(np.int64).sum()) << 40) + int((v - hi * 2.0 ** 40).astype(np.int64).sum())
+    return total
+
+
+@dataclass
+class Run:
+    w: shardgen.Workload
+    sample: Optional[np.ndarray] = None          # None: full oracle state
+    dev: Z.ShardStep = None
+    st: O.OracleState = None
+    hp_o: O.OracleHParams = None
+    hp_d: Z.HParams = None
+    p16: np.ndarray = None
+    p32: np.ndarray = None
+    m32: np.ndarray = None
+    v32: np.ndarray = None
+    k: int = 0
+    stats: dict = field(default_factory=lambda: {"fp32_not_bitwise": 0, "fp32_max_rel": 0.0})
+
+    @property
+    def n(self) -> int:
+        return self.w.n
+
+    def idx(self) -> np.ndarray:
+        return np.arange(self.n) if self.sample is None else self.sample
+
+
+def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77) -> Run:
+    r = Run(w)
+    n = w.n
+    if sample is not None and sample < n:
+        rng = np.random.default_rng(seed)
+        edges = []
+        for _, _, do, c in w.layout.segments:          # both ends of every segment
+            edges += [do, do + 1, do + c - 1, do + c - 2]
+        edges += list(range(min(n, 64))) + list(range(max(0, n - 64), n))
+        r.sample = np.unique(np.clip(np.concatenate([rng.integers(0, n, sample), np.array(edges)]), 0, n - 1))
+    p32 = shardgen.master_params(w)
+    r.dev = Z.ShardStep(n)
+    if n:
+        r.dev.p32.copy_(torch.from_numpy(p32))
+        r.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
+    r.dev.init_state(w.scale0)
+    i = r.idx()
+    r.p32 = np.ascontiguousarray(p32[i])
+    r.p16 = shardgen.to_f16_bits(r.p32)
+    r.m32 = np.zeros_like(r.p32)
+    r.v32 = np.zeros_like(r.p32)
+    r.st = O.new_state(w.scale0)
+    r.hp_o = oracle_hparams(w.hp)
+    r.hp_d = device_hparams(w.hp)
+    return r
+
+
+def step(r: Run, check: bool = True, check_full_cast: bool = True, exact: bool = True) -> dict:
+    """One step on both sides; returns a few timings/values for the log."""
+    r.k += 1
+    k, w = r.k, r.w
+    t0 = time.time()
+    gpart = shardgen.grad_partition(w, k, r.st.loss_scale)
+    srcs = shardgen.source_tensors(w.layout, gpart)
+    del gpart
+    dsrcs = [to_dev16(s) for s in srcs]
+    t1 = time.time()
+    log(f"{w.name} n={w.n} step {k}: launch (segments={len(w.layout.segments)}, bucket={w.bucket_elems})")
+    r.dev.set_segments(dsrcs, w.layout.segments, w.bucket_elems)
+    r.dev.step(r.hp_d)
+    # oracle: its own flatten of the same sources, then the exact reduction and decision
+    grad = np.empty(w.n, np.uint16)
+    O.flatten(srcs, w.layout.segments, grad)
+    sumsq, ovf = O.norm_overflow(grad)
+    O.decide(r.st, r.hp_o, sumsq, ovf)
+    i = r.idx()
+    O.adam_update(r.st, r.p16, r.p32, r.m32, r.v32, np.ascontiguousarray(grad[i]))
+    torch.cuda.synchronize()
+    t2 = time.time()
+    log(f"{w.name} step {k}: gpu done, overflow={ovf} norm={r.st.grad_norm:.6g} scale={r.st.loss_scale:g}")
+    if not check:
+        return {}
+    dstate = r.dev.read_state()
+    exact = exact_units(grad) if (exact and not ovf and w.n <= (1 << 27)) else None
+    compare_state(dstate, r.st, exact)
+    assert np.array_equal(bits16(r.dev.grad16)[:w.n], grad), "flattened gradient differs"
+    it = torch.from_numpy(i).cuda()
+    d16 = bits16(r.dev.p16[it])
+    assert np.array_equal(d16, r.p16), f"p16 differs at {int(np.sum(d16 != r.p16))} elements"
+    for name, dt, ref in (("p32", r.dev.p32, r.p32), ("m32", r.dev.m32, r.m32), ("v32", r.dev.v32, r.v32)):
+        got = dt[it].cpu().numpy()
+        e = rel_err(got, ref)
+        r.stats["fp32_max_rel"] = max(r.stats["fp32_max_rel"], e)
+        r.stats["fp32_not_bitwise"] += int(np.sum(got.view(np.uint32) != ref.view(np.uint32)))
+        assert e <= FP32_REL_TOL, (name, e)
+    if check_full_cast and w.n:
+        assert torch.equal(r.dev.p16[:w.n].view(torch.int16), r.dev.p32[:w.n].half().view(torch.int16))
+    del dsrcs
+    return {"gen_s": t1 - t0, "step_s": t2 - t1}

@@ -1,0 +1,183 @@
+"""CPU checks of the C-ABI library: it loads, exports exactly what the header
+declares, its host-only functions agree with the oracle, and argument errors
+are reported before any device work (so nothing here touches a GPU)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import shardgen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def Z():
+    from zero_partitioned_mixed_flatten_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    import zero_partitioned_mixed_flatten_amd as Z
+    return Z
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(zero_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_match_header(Z):
+    declared = _declared()
+    assert declared == sorted(Z.EXPORTS), declared
+    L = C.CDLL(Z._lib.LIB_PATH)
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_status_strings(Z):
+    for code in (0, -1, -2, -3):
+        assert Z.zero_status_string(code)
+    assert "unknown" in Z.zero_status_string(-99)
+
+
+def test_struct_sizes(Z):
+    assert C.sizeof(Z.StepState) == 128 and C.sizeof(Z.Segment) == 32 and C.sizeof(Z.HParams) == 80
+
+
+def test_state_bytes_matches_oracle(Z, oracle):
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        psi = int(rng.integers(0, 2 ** 50))
+        nd = int(rng.integers(1, 5000))
+        k = int(rng.integers(0, 20))
+        st = int(rng.integers(0, 4))
+        assert Z.zero_state_bytes(psi, nd, k, st) == oracle.state_bytes(psi, nd, k, st)
+    assert Z.zero_state_bytes(10 ** 12, 1024, 12, 3) == 15_625_000_000
+
+
+def test_state_bytes_errors(Z):
+    L = Z.lib()
+    out = C.c_uint64()
+    assert L.zero_state_bytes(10, 0, 12, 3, C.byref(out)) == Z._lib.ZERO_EINVAL
+    assert L.zero_state_bytes(10, 1, 12, 5, C.byref(out)) == Z._lib.ZERO_EINVAL
+    assert L.zero_state_bytes(10, 1, 12, 3, None) == Z._lib.ZERO_EINVAL
+    assert L.zero_state_bytes(2 ** 63, 1, 12, 0, C.byref(out)) == Z._lib.ZERO_ERANGE
+
+
+@pytest.mark.parametrize("bucket", [1, 7, 1000, 25_000_000])
+def test_bucket_segments_cover_exactly(Z, bucket):
+    L = shardgen.workload("1t").layout if bucket == 25_000_000 else shardgen.single_tensor_layout(5000)
+    if bucket != 25_000_000:
+        rng = np.random.default_rng(bucket)
+        numels, segs = shardgen.random_segments(rng, 5000, 333)
+        L = shardgen.ShardLayout("r", 5000, 1, 0, 0, 5000, ["t"] * len(numels), numels, segs)
+    arr, nseg = Z.make_segments([((t + 1) << 40, so, do, c) for t, so, do, c in L.segments])
+    pieces = []
+    for b in range(0, L.n, bucket):
+        out, k = Z.zero_bucket_segments(arr, nseg, b, min(L.n, b + bucket))
+        got = [(out[i].src, out[i].src_off, out[i].dst_off, out[i].count) for i in range(k)]
+        for src, so, do, c in got:
+            assert b <= do and do + c <= min(L.n, b + bucket) and c > 0
+        pieces += got
+    # the pieces reassemble the original segments exactly
+    d = 0
+    for src, so, do, c in pieces:
+        assert do == d
+        d += c
+    assert d == L.n
+    for t, so, do, c in L.segments:
+        mine = [p for p in pieces if p[0] == (t + 1) << 40]
+        assert mine[0][1] == so and sum(p[3] for p in mine) == c
+        for a, b in zip(mine, mine[1:]):
+            assert b[1] == a[1] + a[3]
+    if bucket == 25_000_000:
+        assert -(-L.n // bucket) == 40
+
+
+def test_bucket_segments_capacity_error(Z):
+    arr, nseg = Z.make_segments([(4096, 0, 0, 10), (8192, 0, 10, 10)])
+    L = Z.lib()
+    out = (Z.Segment * 1)()
+    got = C.c_uint32()
+    assert L.zero_bucket_segments(arr, nseg, 0, 20, out, 1, C.byref(got)) == Z._lib.ZERO_ERANGE
+    assert got.value == 2
+    assert L.zero_bucket_segments(arr, nseg, 5, 4, out, 1, C.byref(got)) == Z._lib.ZERO_EINVAL
+
+
+def test_workspace_size_is_stable_and_bounded(Z):
+    for n in (0, 1, 8, 8191, 1 << 20, 97_350_700, 976_562_500):
+        b = Z.zero_norm_workspace_bytes(n)
+        assert b == Z.zero_norm_workspace_bytes(n) and 32 <= b <= 2048 * 32
+    assert Z.zero_norm_workspace_bytes(1 << 40) > 2048 * 32       # per-thread bound grows the grid
+
+
+# ---- argument validation: every case returns before any device work ---------
+
+FAKE = 1 << 20          # a 16-byte-aligned address that is never dereferenced
+
+
+def test_adam_validation(Z):
+    L, E = Z.lib(), Z._lib
+    ok = dict(p16=FAKE, p32=FAKE, m32=FAKE, v32=FAKE, g=FAKE, st=FAKE)
+    call = lambda **kw: L.zero_shard_adam_step(kw["p16"], kw["p32"], kw["m32"], kw["v32"], kw["g"], kw.get("n", 8),
+                                               kw["st"], None)
+    assert call(**{**ok, "st": 0}) == E.ZERO_EINVAL
+    assert call(**{**ok, "p32": 0}) == E.ZERO_EINVAL
+    assert call(**{**ok, "m32": FAKE + 4}) == E.ZERO_EALIGN
+    assert call(**{**ok, "g": FAKE + 2}) == E.ZERO_EALIGN
+    assert call(**{**ok, "st": FAKE + 4}) == E.ZERO_EALIGN
+    assert call(**{**ok, "p16": 0, "n": 0}) == E.ZERO_OK                 # n == 0: nothing to do
+
+
+def _hp(Z, **kw):
+    hp = Z.hparams()
+    for k, v in kw.items():
+        setattr(hp, k, v)
+    return hp
+
+
+def test_norm_validation(Z):
+    L, E = Z.lib(), Z._lib
+    ws = Z.zero_norm_workspace_bytes(1000)
+
+    def call(hp=None, g=FAKE, n=1000, st=FAKE, w=FAKE, wsb=ws):
+        return L.zero_shard_norm_overflow(g, n, C.byref(hp or Z.hparams()), st, w, wsb, None)
+
+    assert L.zero_shard_norm_overflow(FAKE, 8, None, FAKE, FAKE, ws, None) == E.ZERO_EINVAL
+    assert call(st=0) == E.ZERO_EINVAL and call(w=0) == E.ZERO_EINVAL and call(g=0) == E.ZERO_EINVAL
+    for bad in (dict(lr=-1.0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(weight_decay=-1e-3),
+                dict(backoff=0.0), dict(backoff=1.5), dict(growth=0.5), dict(min_scale=0.0),
+                dict(lr=float("nan")), dict(max_grad_norm=float("inf"))):
+        assert call(hp=_hp(Z, **bad)) == E.ZERO_EINVAL, bad
+    assert call(g=FAKE + 8) == E.ZERO_EALIGN
+    assert call(st=FAKE + 2) == E.ZERO_EALIGN
+    assert call(w=FAKE + 8) == E.ZERO_EALIGN
+    assert call(wsb=ws - 1) == E.ZERO_ERANGE
+    assert call(n=1 << 48, wsb=1 << 40) == E.ZERO_ERANGE
+
+
+def test_flatten_validation(Z):
+    L, E = Z.lib(), Z._lib
+    arr, k = Z.make_segments([(FAKE, 0, 0, 100), (FAKE, 0, 100, 100)])
+    assert L.zero_flatten_bucket(arr, k, FAKE, 200, 3, 0, None) == E.ZERO_EINVAL          # dtype
+    assert L.zero_flatten_bucket(arr, k, 0, 200, E.ZERO_F16, 0, None) == E.ZERO_EINVAL
+    assert L.zero_flatten_bucket(arr, k, FAKE + 2, 200, E.ZERO_F16, 0, None) == E.ZERO_EALIGN
+    assert L.zero_flatten_bucket(arr, k, FAKE, 199, E.ZERO_F16, 0, None) == E.ZERO_ERANGE
+    bad, k2 = Z.make_segments([(FAKE + 1, 0, 0, 10)])
+    assert L.zero_flatten_bucket(bad, k2, FAKE, 200, E.ZERO_F16, 0, None) == E.ZERO_EALIGN
+    nul, k3 = Z.make_segments([(0, 0, 0, 10)])
+    assert L.zero_flatten_bucket(nul, k3, FAKE, 200, E.ZERO_F16, 0, None) == E.ZERO_EINVAL
+    assert L.zero_flatten_bucket(None, 0, 0, 0, E.ZERO_F16, 0, None) == E.ZERO_OK
+
+
+def test_state_init_and_copy_validation(Z):
+    L, E = Z.lib(), Z._lib
+    assert L.zero_step_state_init(0, 1.0, None) == E.ZERO_EINVAL
+    assert L.zero_step_state_init(FAKE, 0.0, None) == E.ZERO_EINVAL
+    assert L.zero_step_state_init(FAKE, float("inf"), None) == E.ZERO_EINVAL
+    assert L.zero_step_state_init(FAKE + 4, 1.0, None) == E.ZERO_EALIGN
+    assert L.zero_stream_copy(0, FAKE, 16, None) == E.ZERO_EINVAL
+    assert L.zero_stream_copy(FAKE, FAKE, 15, None) == E.ZERO_EALIGN

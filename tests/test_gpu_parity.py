@@ -1,0 +1,235 @@
+"""GPU parity tests: the HIP path through the C ABI against the CPU oracle on
+the same seeded inputs (contract in tests/gpu_harness.py).
+
+Small and ragged shards are compared element by element over every element;
+the full-size shards of the five workloads are compared on sampled elements
+(plus every segment boundary and both ends of the shard), with the flattened
+gradient, the step state and the fp16 copy checked over the whole shard."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import shardgen
+
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as H  # noqa: E402  (tests/ is on sys.path under pytest)
+import zero_partitioned_mixed_flatten_amd as Z  # noqa: E402
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.float16 else t.view(torch.int32)
+
+
+def _small(name, n, seed, max_seg=None, misalign=True):
+    w = shardgen.workload("tiny")
+    w.name = name
+    rng = np.random.default_rng(seed)
+    numels, segs = shardgen.random_segments(rng, n, max_seg or max(1, n // 5), misalign)
+    w.layout = shardgen.ShardLayout(name, n, 1, 0, 0, n, [f"t{i}" for i in range(len(numels))], numels, segs)
+    return w
+
+
+def test_tiny_workload_ten_steps_full_parity():
+    w = shardgen.workload("tiny")
+    r = H.start(w)
+    for _ in range(w.steps):
+        H.step(r)
+    assert r.st.step == 10 and r.stats["fp32_not_bitwise"] == 0, r.stats
+    H.log(f"tiny: {r.stats}")
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 63, 4099, 65_536 * 3 + 5, (1 << 20) + 3])
+def test_ragged_sizes_misaligned_segments(n):
+    w = _small(f"ragged{n}", n, seed=n)
+    r = H.start(w)
+    for _ in range(3):
+        H.step(r)
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+def test_many_segments_over_launch_limit():
+    # > 64 segments forces several flatten launches in one call
+    w = _small("many", 300_000, seed=3, max_seg=2000, misalign=False)
+    assert len(w.layout.segments) > 64
+    r = H.start(w)
+    for _ in range(2):
+        H.step(r)
+
+
+def test_empty_shard():
+    w = _small("empty", 0, seed=0)
+    w.layout = shardgen.ShardLayout("empty", 0, 1, 0, 0, 0, [], [], [])
+    r = H.start(w)
+    H.step(r)
+    s = r.dev.read_state()
+    assert s.sumsq == 0.0 and s.step == 1 and s.overflow == 0
+
+
+def test_gpt2_shard_full_size():
+    w = shardgen.workload("gpt2")
+    r = H.start(w, sample=1 << 20)
+    for _ in range(3):
+        t = H.step(r)
+        H.log(f"gpt2 timings {t}")
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+@pytest.mark.timeout(900)
+def test_stress_loss_scale_trajectory_full_size():
+    w = shardgen.workload("stress")
+    r = H.start(w, sample=1 << 16)
+    snap = None
+    for k in range(1, w.steps + 1):
+        if k in w.inject:
+            snap = [t.clone() for t in (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.v32)]
+        H.step(r, check_full_cast=(k % 10 == 0), exact=(k % 25 == 0))
+        if k in w.inject:
+            s = r.dev.read_state()
+            assert s.skip == 1 and s.overflow == 1
+            for a, b in zip(snap, (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.v32)):
+                assert torch.equal(_bits(a), _bits(b))
+            snap = None
+    s = r.dev.read_state()
+    assert (s.loss_scale, s.good_steps, s.step, s.skipped_total) == (2.0 ** 26, 13, 98, 2)
+
+
+def test_100b_shard_full_size():
+    w = shardgen.workload("100b")
+    r = H.start(w, sample=1 << 20)
+    for _ in range(2):
+        H.step(r)
+
+
+@pytest.mark.timeout(900)
+def test_1t_shard_full_size_bucketed():
+    w = shardgen.workload("1t")
+    r = H.start(w, sample=1 << 20)
+    assert len(r.dev.buckets) == 0
+    for _ in range(2):
+        H.step(r)
+        assert len(r.dev.buckets) == 40
+
+
+@pytest.mark.parametrize("dtype,acc", [(Z.ZERO_F16, False), (Z.ZERO_F16, True), (Z.ZERO_F32, False),
+                                       (Z.ZERO_F32, True)])
+def test_flatten_modes(dtype, acc):
+    rng = np.random.default_rng(dtype * 10 + acc)
+    n = 200_003
+    numels, segs = shardgen.random_segments(rng, n, 30_000)
+    holes = [s for i, s in enumerate(segs) if i % 4 != 2]           # leave some destination untouched
+    srcs = [shardgen.to_f16_bits((rng.standard_normal(k) * 300).astype(np.float32)) for k in numels]
+    if dtype == Z.ZERO_F16:
+        dst0 = shardgen.to_f16_bits((rng.standard_normal(n) * 300).astype(np.float32))
+        dev_dst = H.to_dev16(dst0.copy())
+    else:
+        dst0 = (rng.standard_normal(n) * 300).astype(np.float32)
+        dev_dst = torch.from_numpy(dst0.copy()).cuda()
+    ref = dst0.copy()
+    O.flatten(srcs, holes, ref, accumulate=acc)
+    dsrcs = [H.to_dev16(s) for s in srcs]
+    arr, k = Z.make_segments([(dsrcs[t].data_ptr(), so, do, c) for t, so, do, c in holes])
+    H.log(f"flatten mode dtype={dtype} acc={acc} segments={k}")
+    Z.zero_flatten_bucket(arr, k, dev_dst, n, dtype, acc)
+    torch.cuda.synchronize()
+    got = dev_dst.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16) if dtype == Z.ZERO_F16 else got.view(np.uint32),
+                          ref.view(np.uint16) if dtype == Z.ZERO_F16 else ref.view(np.uint32))
+
+
+def test_fp16_copy_rounding_sweep():
+    """lr = wd = 0 and a zero gradient leave p32 unchanged, so p16 = fp16(p32)
+    for every finite fp32 pattern of a stratified sweep (all exponents, and
+    every low-bit pattern around the binary16 subnormal/normal/overflow
+    boundaries), compared with the oracle's own converter."""
+    rng = np.random.default_rng(5)
+    parts = [(np.repeat(np.arange(255, dtype=np.uint32), 1 << 14) << 23) |
+             rng.integers(0, 1 << 23, 255 << 14, dtype=np.uint32)]
+    low = np.arange(1 << 15, dtype=np.uint32)
+    for e in range(127 - 27, 127 + 17):
+        parts.append((np.uint32(e) << np.uint32(23)) | (np.uint32(rng.integers(0, 256)) << np.uint32(15)) | low)
+    bits = np.concatenate(parts)
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    p = bits.view(np.float32)
+    n = p.size
+    dev = Z.ShardStep(n)
+    dev.p32.copy_(torch.from_numpy(p))
+    dev.init_state(1.0)
+    hp = Z.hparams(lr=0.0, weight_decay=0.0)
+    H.log(f"fp16 sweep n={n}")
+    dev.norm_overflow(hp)
+    dev.adam()
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.p32.cpu().numpy().view(np.uint32), bits)
+    assert np.array_equal(H.bits16(dev.p16), O.f16_from_f32(p))
+
+
+def test_skip_and_resume_bitwise():
+    w = _small("resume", 100_000, seed=9)
+    w.inject = {2: 0xFC00}
+    straight = H.start(w)
+    for _ in range(6):
+        H.step(straight)
+    a = H.start(w)
+    for _ in range(3):
+        H.step(a)
+    saved = [t.cpu() for t in (a.dev.p16, a.dev.p32, a.dev.m32, a.dev.v32, a.dev.state)]
+    b = H.start(w)                                  # fresh buffers, then restore
+    for t, s in zip((b.dev.p16, b.dev.p32, b.dev.m32, b.dev.v32, b.dev.state), saved):
+        t.copy_(s)
+    b.st, b.p16, b.p32, b.m32, b.v32, b.k = a.st, a.p16, a.p32, a.m32, a.v32, a.k
+    for _ in range(3):
+        H.step(b)
+    for x, y in zip((straight.dev.p16, straight.dev.p32, straight.dev.m32, straight.dev.v32, straight.dev.state),
+                    (b.dev.p16, b.dev.p32, b.dev.m32, b.dev.v32, b.dev.state)):
+        assert x.cpu().numpy().tobytes() == y.cpu().numpy().tobytes()
+    assert straight.dev.read_state().skipped_total == 1
+
+
+def test_norm_special_values_everywhere():
+    """inf/NaN patterns in the vector body, in the ragged tail and at the
+    first element all raise the flag; the largest finite values do not."""
+    n = 8 * 5000 + 5
+    rng = np.random.default_rng(4)
+    base = shardgen.to_f16_bits((rng.standard_normal(n) * 100).astype(np.float32))
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    cases = [(0, 0x7C00), (n - 1, 0xFC00), (n - 3, 0x7E00), (12345, 0x7C01), (8 * 4999, 0xFFFF),
+             (None, 0x7BFF)]
+    for pos, val in cases:
+        g = base.copy()
+        if pos is None:
+            g[::7] = val
+        else:
+            g[pos] = val
+        Z.zero_step_state_init(st, 1024.0)
+        H.log(f"norm special pos={pos} val={val:#x}")
+        Z.zero_shard_norm_overflow(H.to_dev16(g), n, Z.hparams(), st, ws)
+        s = Z.read_state(st)
+        sumsq, ovf = O.norm_overflow(g)
+        assert s.overflow == ovf == (1 if pos is not None else 0)
+        assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+        if not ovf:
+            assert s.as_dict()["sumsq_units"] == H.exact_units(g)
+
+
+def test_determinism_two_runs():
+    w = _small("det", 777_777, seed=12)
+    outs = []
+    for _ in range(2):
+        r = H.start(w)
+        for _ in range(2):
+            H.step(r, check=False)
+        torch.cuda.synchronize()
+        outs.append(b"".join(t.cpu().numpy().tobytes() for t in (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.v32,
+                                                                r.dev.state)))
+    assert outs[0] == outs[1]
+
+
+def test_stream_copy():
+    x = torch.randint(0, 2 ** 31 - 1, ((1 << 22) + 4,), dtype=torch.int32, device="cuda")
+    y = torch.zeros_like(x)
+    Z.zero_stream_copy(y, x, x.numel() * 4)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)

@@ -1,0 +1,188 @@
+"""ctypes binding of libzero_mi355x.so: one Python function per C entry point,
+with the same names.  Argument marshalling only -- torch tensors supply device
+memory and the current HIP stream; every step of the path runs in the HIP
+kernels behind the C ABI.  There is no fallback: if the library is missing
+the import fails loudly."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzero_mi355x.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP = 0, -1, -2, -3, -4
+ZERO_F16, ZERO_F32 = 1, 2
+
+# Every function the public header declares (checked against the header by a test).
+EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "zero_step_state_init",
+           "zero_flatten_bucket", "zero_norm_workspace_bytes", "zero_shard_norm_overflow",
+           "zero_shard_adam_step", "zero_stream_copy")
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, fn: str, code: int, text: str):
+        super().__init__(f"{fn} failed: {code} ({text})")
+        self.code = code
+
+
+class Segment(C.Structure):
+    _fields_ = [("src", C.c_void_p), ("src_off", C.c_uint64), ("dst_off", C.c_uint64),
+                ("count", C.c_uint64)]
+
+
+class HParams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double), ("eps", C.c_double),
+                ("weight_decay", C.c_double), ("max_grad_norm", C.c_double), ("backoff", C.c_double),
+                ("growth", C.c_double), ("min_scale", C.c_double), ("growth_interval", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class StepState(C.Structure):
+    _fields_ = [("loss_scale", C.c_double), ("beta1_pow", C.c_double), ("beta2_pow", C.c_double),
+                ("step", C.c_int64), ("good_steps", C.c_int32), ("skipped_total", C.c_int32),
+                ("sumsq", C.c_double), ("grad_norm", C.c_double), ("overflow", C.c_int32),
+                ("skip", C.c_int32), ("gmul", C.c_float), ("bc1", C.c_float), ("bc2", C.c_float),
+                ("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("omb1", C.c_float),
+                ("omb2", C.c_float), ("eps", C.c_float), ("wd", C.c_float), ("done_blocks", C.c_uint32),
+                ("reserved", C.c_uint32), ("sumsq_units", C.c_uint64 * 2)]
+
+    def as_dict(self):
+        d = {name: getattr(self, name) for name, _ in self._fields_ if name != "sumsq_units"}
+        d["sumsq_units"] = (int(self.sumsq_units[1]) << 64) | int(self.sumsq_units[0])
+        return d
+
+
+STATE_BYTES = C.sizeof(StepState)
+assert STATE_BYTES == 128 and C.sizeof(Segment) == 32 and C.sizeof(HParams) == 80
+
+_lib = None
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, u64, u32, i32 = C.c_void_p, C.c_uint64, C.c_uint32, C.c_int
+        L.zero_status_string.argtypes = [i32]
+        L.zero_status_string.restype = C.c_char_p
+        L.zero_state_bytes.argtypes = [u64, u32, u32, i32, C.POINTER(u64)]
+        L.zero_bucket_segments.argtypes = [C.POINTER(Segment), u32, u64, u64, C.POINTER(Segment), u32,
+                                           C.POINTER(u32)]
+        L.zero_step_state_init.argtypes = [vp, C.c_double, vp]
+        L.zero_flatten_bucket.argtypes = [C.POINTER(Segment), u32, vp, u64, i32, i32, vp]
+        L.zero_norm_workspace_bytes.argtypes = [u64]
+        L.zero_norm_workspace_bytes.restype = C.c_size_t
+        L.zero_shard_norm_overflow.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
+        L.zero_shard_adam_step.argtypes = [vp, vp, vp, vp, vp, u64, vp, vp]
+        L.zero_stream_copy.argtypes = [vp, vp, u64, vp]
+        for name in EXPORTS:
+            if name not in ("zero_status_string", "zero_norm_workspace_bytes"):
+                getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != ZERO_OK:
+        raise ZeroError(fn, rc, zero_status_string(rc))
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t, dtype=None) -> int:
+    import torch
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+# ---- host-only entry points ---------------------------------------------------
+
+def zero_status_string(code: int) -> str:
+    return lib().zero_status_string(code).decode()
+
+
+def zero_state_bytes(psi: int, nd: int, k: int = 12, stage: int = 3) -> int:
+    out = C.c_uint64()
+    _check("zero_state_bytes", lib().zero_state_bytes(psi, nd, k, stage, C.byref(out)))
+    return out.value
+
+
+def make_segments(segs: Sequence[Tuple[int, int, int, int]]):
+    """(src_device_ptr, src_off, dst_off, count) tuples -> ctypes array."""
+    arr = (Segment * max(1, len(segs)))()
+    for i, (p, so, do, cnt) in enumerate(segs):
+        arr[i] = Segment(p, so, do, cnt)
+    return arr, len(segs)
+
+
+def zero_bucket_segments(segs, nsegs: int, begin: int, end: int):
+    """Cut a ctypes Segment array to the destination window [begin, end)."""
+    need = C.c_uint32()
+    rc = lib().zero_bucket_segments(segs, nsegs, begin, end, None, 0, C.byref(need))
+    if rc not in (ZERO_OK, ZERO_ERANGE):
+        _check("zero_bucket_segments", rc)
+    out = (Segment * max(1, need.value))()
+    got = C.c_uint32()
+    _check("zero_bucket_segments",
+           lib().zero_bucket_segments(segs, nsegs, begin, end, out, need.value, C.byref(got)))
+    return out, got.value
+
+
+def zero_norm_workspace_bytes(n: int) -> int:
+    return int(lib().zero_norm_workspace_bytes(n))
+
+
+# ---- device entry points (asynchronous on the current torch stream) ---------------
+
+def zero_step_state_init(dev_state, initial_scale: float, stream=None) -> None:
+    _check("zero_step_state_init", lib().zero_step_state_init(_ptr(dev_state), initial_scale, _stream(stream)))
+
+
+def zero_flatten_bucket(segs, nsegs: int, dst, dst_len: Optional[int] = None, dst_dtype: int = ZERO_F16,
+                        accumulate: bool = False, stream=None) -> None:
+    if dst_len is None:
+        dst_len = dst.numel()
+    _check("zero_flatten_bucket", lib().zero_flatten_bucket(segs, nsegs, _ptr(dst), dst_len, dst_dtype,
+                                                            int(bool(accumulate)), _stream(stream)))
+
+
+def zero_shard_norm_overflow(grad16, n: int, hp: HParams, dev_state, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_shard_norm_overflow",
+           lib().zero_shard_norm_overflow(_ptr(grad16), n, C.byref(hp), _ptr(dev_state), _ptr(workspace),
+                                          ws_bytes, _stream(stream)))
+
+
+def zero_shard_adam_step(p16, p32, m32, v32, grad16, n: int, dev_state, stream=None) -> None:
+    _check("zero_shard_adam_step",
+           lib().zero_shard_adam_step(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(grad16), n,
+                                      _ptr(dev_state), _stream(stream)))
+
+
+def zero_stream_copy(dst, src, nbytes: int, stream=None) -> None:
+    _check("zero_stream_copy", lib().zero_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
+
+
+def read_state(dev_state) -> StepState:
+    """Copy a device step state to the host (synchronises the current stream)."""
+    raw = dev_state.detach().to("cpu").numpy().tobytes()
+    return StepState.from_buffer_copy(raw)

@@ -1,0 +1,52 @@
+// zero_internal.hpp -- definitions shared by the library's translation units
+// (never installed; the public interface is include/zero_mi355x.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "zero_mi355x.h"
+
+static_assert(sizeof(zero_step_state_t) == 128, "zero_step_state_t is a 128-byte ABI struct");
+static_assert(offsetof(zero_step_state_t, sumsq) == 40, "state layout");
+static_assert(offsetof(zero_step_state_t, gmul) == 64, "state layout");
+static_assert(offsetof(zero_step_state_t, done_blocks) == 104, "state layout");
+static_assert(offsetof(zero_step_state_t, sumsq_units) == 112, "state layout");
+static_assert(sizeof(zero_segment_t) == 32, "segment layout");
+static_assert(sizeof(zero_hparams_t) == 80, "hparams layout");
+
+namespace zero {
+
+// 16-byte register vectors: one global_load/store_dwordx4 each.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__host__ __device__ inline bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Records a HIP error for zero_status_string and maps it to ZERO_EHIP.
+int hip_fail(hipError_t e);
+// Checks the launch that was just enqueued.
+int launch_status();
+
+// ---- norm/overflow reduction geometry (shared by the host size query and
+// the launch) ----------------------------------------------------------------
+constexpr int kNormBlock = 256;
+constexpr uint64_t kNormMaxBlocks = 2048;
+constexpr uint64_t kNormMaxPerThread = uint64_t(1) << 15;   // keeps a thread's sum < 2^95
+constexpr uint64_t kNormMaxElems = uint64_t(1) << 47;       // keeps the total < 2^127
+
+// One block's exact partial: sum of squares in units of 2^-48 as a 128-bit
+// integer, plus the OR-ed exponent test bits.
+struct alignas(16) NormPartial {
+    uint64_t lo, hi;
+    uint32_t flag;
+    uint32_t pad[3];
+};
+static_assert(sizeof(NormPartial) == 32, "partial layout");
+
+uint64_t norm_grid(uint64_t n);
+
+}  // namespace zero

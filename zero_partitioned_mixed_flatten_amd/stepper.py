@@ -1,0 +1,76 @@
+"""ShardStep: the three C-ABI calls of one ZeRO shard step, wired to torch-owned
+device buffers.  Allocation and call order only; the arithmetic is in the HIP
+kernels behind the C ABI.
+
+One data-parallel rank owns n parameters of the flat model state (ZeRO paper
+card, "Method").  For them it keeps, index-aligned and contiguous: the fp16
+parameter copy, the flat fp16 gradient partition, and the fp32 master
+parameters, momentum and variance (16 bytes per parameter, "Bottleneck"),
+plus the 128-byte step state and the reduction workspace.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+from . import _lib as Z
+
+
+class ShardStep:
+    def __init__(self, n: int, device="cuda"):
+        import torch
+        self.n = int(n)
+        alloc = max(1, self.n)
+        self.device = torch.device(device)
+        self.p16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
+        self.grad16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
+        self.p32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.m32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.v32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
+        ws = Z.zero_norm_workspace_bytes(self.n)
+        self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
+        self.buckets: List[Tuple[object, int]] = []
+        self._sources: Sequence = ()
+
+    # ---- set-up ----------------------------------------------------------------
+    def init_state(self, initial_scale: float) -> None:
+        Z.zero_step_state_init(self.state, initial_scale)
+
+    def set_segments(self, sources: Sequence, segments: Sequence[Tuple[int, int, int, int]],
+                     bucket_elems: int = 0) -> None:
+        """sources: device fp16 tensors; segments: (tensor index, src_off,
+        dst_off, count).  With bucket_elems > 0 the partition is flattened in
+        windows of that many destination elements, one call each."""
+        self._sources = list(sources)                  # keep the tensors alive
+        segs, nsegs = Z.make_segments([(self._sources[t].data_ptr(), so, do, c)
+                                       for t, so, do, c in segments])
+        if bucket_elems and bucket_elems < self.n:
+            self.buckets = [Z.zero_bucket_segments(segs, nsegs, b, min(self.n, b + bucket_elems))
+                            for b in range(0, self.n, bucket_elems)]
+        else:
+            self.buckets = [(segs, nsegs)]
+
+    # ---- the step ---------------------------------------------------------------
+    def flatten(self) -> None:
+        for segs, nsegs in self.buckets:
+            Z.zero_flatten_bucket(segs, nsegs, self.grad16, self.n, Z.ZERO_F16, False)
+
+    def norm_overflow(self, hp: Z.HParams) -> None:
+        Z.zero_shard_norm_overflow(self.grad16, self.n, hp, self.state, self.workspace)
+
+    def adam(self) -> None:
+        Z.zero_shard_adam_step(self.p16, self.p32, self.m32, self.v32, self.grad16, self.n, self.state)
+
+    def step(self, hp: Z.HParams) -> None:
+        self.flatten()
+        self.norm_overflow(hp)
+        self.adam()
+
+    def read_state(self) -> Z.StepState:
+        return Z.read_state(self.state)
+
+
+def hparams(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=1.0,
+            backoff=0.5, growth=2.0, min_scale=1.0, growth_interval=20) -> Z.HParams:
+    return Z.HParams(lr, beta1, beta2, eps, weight_decay, max_grad_norm, backoff, growth, min_scale,
+                     growth_interval, 0)
