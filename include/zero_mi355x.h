@@ -196,7 +196,8 @@ size_t zero_norm_workspace_bytes(uint64_t n);
  * Errors: ZERO_EINVAL (NULL, hyperparameters out of range: lr < 0,
  *         beta not in [0,1), eps <= 0, weight_decay < 0, backoff not in
  *         (0,1], growth < 1, min_scale <= 0, any non-finite value),
- *         ZERO_EALIGN, ZERO_ERANGE (workspace too small), ZERO_EHIP. */
+ *         ZERO_EALIGN, ZERO_ERANGE (workspace too small, n > 2^40),
+ *         ZERO_EHIP. */
 int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hparams_t* hp,
                              zero_step_state_t* dev_state, void* workspace,
                              size_t workspace_bytes, void* stream);
@@ -213,7 +214,8 @@ int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hpar
  * All five arrays: device, n elements, 16-byte aligned, index-aligned with
  * each other and with the grad16 the decision was made on; n may be 0.
  * dev_state: as left by zero_shard_norm_overflow (read only here).
- * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_EHIP. */
+ * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_ERANGE (n >= 2^44),
+ *         ZERO_EHIP. */
 int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32,
                          const uint16_t* grad16, uint64_t n,
                          const zero_step_state_t* dev_state, void* stream);
@@ -223,7 +225,7 @@ int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32,
 /* A plain streaming copy of `bytes` bytes (dst and src device, 16-byte
  * aligned, bytes a multiple of 16), used to measure the attainable HBM
  * bandwidth next to the step's kernels.  Errors: ZERO_EINVAL, ZERO_EALIGN,
- * ZERO_EHIP. */
+ * ZERO_ERANGE (more than 2^31 - 1 workgroups), ZERO_EHIP. */
 int zero_stream_copy(void* dst, const void* src, uint64_t bytes, void* stream);
 
 #ifdef __cplusplus

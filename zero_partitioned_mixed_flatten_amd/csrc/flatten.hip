@@ -14,7 +14,10 @@
 // 16-byte phase the body loads are 16-byte vector loads; otherwise each
 // thread gathers its 8 source elements with 2-byte loads (still coalesced
 // across the wavefront).  The work is pure streaming: 4 bytes per element
-// for the fp16 copy, so no LDS and no MFMA.
+// for the fp16 copy, so no LDS and no MFMA.  Measured on MI355X inside the
+// whole step: one 16-byte vector per thread; nontemporal loads (the per-layer
+// sources are read once); plain stores, so the fresh partition is still in
+// the 256 MB Infinity Cache when the norm reads it next.
 #include "zero_internal.hpp"
 
 namespace zero {
@@ -22,7 +25,7 @@ namespace {
 
 constexpr uint32_t kMaxSegs = 64;
 constexpr int kBlock = 256;
-constexpr int kVecsPerThread = 4;                          // 4 x 16 B in flight per thread
+constexpr int kVecsPerThread = 1;
 constexpr uint64_t kVecsPerBlock = uint64_t(kBlock) * kVecsPerThread;
 
 enum Mode { kCopy16 = 0, kAcc16 = 1, kTo32 = 2, kAcc32 = 3 };
@@ -62,7 +65,7 @@ template <int MODE>
 __device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s)
 {
     if (MODE == kCopy16) {
-        __builtin_nontemporal_store(s, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i));
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i) = s;
     } else if (MODE == kAcc16) {
         u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i);
         f16x8 a = __builtin_bit_cast(f16x8, *d);

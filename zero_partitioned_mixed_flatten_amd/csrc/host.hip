@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "zero_internal.hpp"
 
 namespace zero {
@@ -24,10 +26,10 @@ int launch_status()
 
 uint64_t norm_grid(uint64_t n)
 {
-    // At least four 8-element vectors per thread, at most kNormMaxBlocks
-    // blocks, unless a thread would then sum more than kNormMaxPerThread
-    // elements.  A function of n alone, so workspace sizes are stable.
-    const uint64_t per_block = uint64_t(kNormBlock) * 8 * 4;
+    // At least two 8-element vectors per thread, at most one workgroup per
+    // CU, unless a thread would then sum more than kNormMaxPerThread elements.
+    // A function of n alone, so workspace sizes are stable.
+    const uint64_t per_block = uint64_t(kNormBlock) * 8 * 2;
     uint64_t g = (n + per_block - 1) / per_block;
     if (g < 1) g = 1;
     if (g > kNormMaxBlocks) g = kNormMaxBlocks;
@@ -49,24 +51,37 @@ __global__ void state_init_kernel(zero_step_state_t* st, double scale)
     *st = s;
 }
 
+// ---- occupancy cap ----------------------------------------------------------------
+
+uint32_t lds_reservation(int blocks_per_cu)
+{
+    // Per-device LDS bytes per CU, looked up once (160 KiB on gfx950).
+    static std::atomic<int> lds_per_cu[64];
+    static std::atomic<bool> init[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || blocks_per_cu < 1)
+        return 0;
+    if (!init[dev].load(std::memory_order_acquire)) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+            v = 0;
+        lds_per_cu[dev].store(v, std::memory_order_relaxed);
+        init[dev].store(true, std::memory_order_release);
+    }
+    uint32_t r = uint32_t(lds_per_cu[dev].load(std::memory_order_relaxed)) / uint32_t(blocks_per_cu);
+    if (r > 65536) r = 65536;
+    return r & ~255u;
+}
+
 // ---- streaming copy (bandwidth reference) --------------------------------------
 
+// One 16-byte vector per thread, one-shot grid, nontemporal both ways: the
+// fastest plain copy shape measured on MI355X.
 __global__ __launch_bounds__(256) void stream_copy_kernel(u32x4* __restrict__ dst,
                                                           const u32x4* __restrict__ src, uint64_t nvec)
 {
-    const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
-    uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        u32x4 a = __builtin_nontemporal_load(src + i);
-        u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-        __builtin_nontemporal_store(a, dst + i);
-        __builtin_nontemporal_store(b, dst + i + stride);
-        __builtin_nontemporal_store(c, dst + i + 2 * stride);
-        __builtin_nontemporal_store(d, dst + i + 3 * stride);
-    }
-    for (; i < nvec; i += stride)
+    const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < nvec)
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
@@ -152,8 +167,9 @@ extern "C" int zero_stream_copy(void* dst, const void* src, uint64_t bytes, void
     const uint64_t nvec = bytes / 16;
     if (nvec == 0)
         return ZERO_OK;
-    uint64_t grid = (nvec + 255) / 256;
-    if (grid > 8192) grid = 8192;
+    const uint64_t grid = (nvec + 255) / 256;
+    if (grid > 0x7fffffffull)
+        return ZERO_ERANGE;
     hipLaunchKernelGGL(stream_copy_kernel, dim3(uint32_t(grid)), dim3(256), 0, (hipStream_t)stream,
                        (u32x4*)dst, (const u32x4*)src, nvec);
     return launch_status();

@@ -5,24 +5,26 @@
 // The pages fix the gradient as fp16 and the optimizer state as fp32 (ZeRO
 // paper card, "Bottleneck"); the rest of this step is the published methods.
 //
-// Exactness instead of a floating-point sum.  A finite binary16 value is
-// M * 2^(E'-25) with an 11-bit integer M and E' = max(E, 1), so its square is
-// M^2 * 2^(2E'-2) units of 2^-48: an integer below 2^80.  Each thread adds
-// these integers into a 96-bit accumulator, workgroups fold them into 128
-// bits, and the last workgroup converts the total to binary64 with a single
-// round-to-nearest-even.  The result is therefore the exactly rounded sum,
-// independent of the grid, the wavefront schedule and the device -- which is
-// what lets the clip factor derived from it be bitwise reproducible.
+// Exactness instead of a rounded floating-point sum.  Every square of a
+// finite binary16 value is an integer multiple of 2^-48 below 2^32.  Each
+// thread keeps two binary64 accumulators that stay exact by construction:
+//   hh = x^2 rounded to a multiple of 2^-8   (fma(x, x, C) - C, C = 1.5*2^44)
+//   lo = x^2 - hh, exactly                    (fma(x, x, -hh), |lo| <= 2^-9)
+// With at most kNormMaxPerThread = 2^12 elements per thread, sum(hh) stays a
+// multiple of 2^-8 below 2^44 and sum(lo) a multiple of 2^-48 below 2^3, so
+// neither addition ever rounds.  The two sums become integers of 2^-48 units,
+// split into signed base-2^32 limbs that workgroups and the grid add without
+// carries; one thread propagates the carries at the end and converts the
+// 128-bit total to binary64 with a single round-to-nearest-even.  The result
+// is the exactly rounded sum, independent of grid shape and schedule, so the
+// clip factor derived from it is bitwise reproducible.
 //
-// Pass structure (one launch, no host synchronisation):
-//   every workgroup: grid-stride over 16-byte vectors (8 elements), integer
-//     square-accumulate + exponent test, wavefront shuffle reduction, then an
-//     LDS fold across the 4 wavefronts; thread 0 stores the block partial and
-//     increments an arrival counter with agent-scope acquire/release;
-//   the last workgroup to arrive folds all partials (integer addition, so
-//     the order is irrelevant), converts, takes the decision in binary64 on one
-//     thread and writes it to the step state, then re-arms the counter.
-// Pure streaming (2 bytes per element read): no MFMA.
+// Shape for gfx950: 1024-thread workgroups, at most one per CU (256), each
+// thread streaming 16-byte vectors (8 elements) with four nontemporal loads
+// in flight; about 8 VALU operations per element.  The last workgroup to arrive
+// (agent-scope acq_rel counter, one increment per workgroup) folds the
+// partials, takes the decision in binary64 on one thread and writes it into
+// the step state.  Pure streaming (2 bytes per element read): no MFMA.
 #include <math.h>
 
 #include "zero_internal.hpp"
@@ -35,56 +37,63 @@ struct DecideArgs {
     int32_t growth_interval;
 };
 
-struct U128 {
-    uint64_t lo, hi;
+constexpr double kSplit = 0x1.8p44;           // 1.5 * 2^44: its ulp is 2^-8
+
+// The exponent test adds 0x0400 to each masked exponent field of a word that
+// holds two binary16 values: only an all-ones field carries into bit 15
+// (resp. 31), and the low half never carries into the high half.
+__device__ __forceinline__ uint32_t exp_test(u32x4 v)
+{
+    return ((v.x & 0x7C007C00u) + 0x04000400u) | ((v.y & 0x7C007C00u) + 0x04000400u) |
+           ((v.z & 0x7C007C00u) + 0x04000400u) | ((v.w & 0x7C007C00u) + 0x04000400u);
+}
+
+__device__ __forceinline__ void acc_square(_Float16 h, double& ah, double& al)
+{
+    const double x = double(float(h));                       // exact
+    const double hh = __builtin_fma(x, x, kSplit) - kSplit;  // x^2 to a multiple of 2^-8
+    ah += hh;
+    al += __builtin_fma(x, x, -hh);                          // x^2 - hh, exact
+}
+
+__device__ __forceinline__ void acc_vec(u32x4 v, double& ah, double& al, uint32_t& flag)
+{
+    flag |= exp_test(v);
+    const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        acc_square(h[k], ah, al);
+}
+
+// Signed base-2^32 limbs of an integer count of 2^-48 units.
+struct Limbs {
+    int64_t l0, l1, l2;
 };
 
-__device__ __forceinline__ U128 add128(U128 a, U128 b)
+__device__ __forceinline__ Limbs to_limbs(double ah, double al)
 {
-    U128 r;
-    r.lo = a.lo + b.lo;
-    r.hi = a.hi + b.hi + (r.lo < a.lo ? 1 : 0);
-    return r;
+    const int64_t hu = int64_t(ah * 256.0);       // sum(hh) / 2^-8, < 2^52
+    const int64_t lu = int64_t(al * 0x1p48);      // sum(lo) / 2^-48, |.| < 2^51
+    const int64_t hs = hu << 8;                   // hu * 2^40 = hs * 2^32
+    return Limbs{lu & 0xFFFFFFFFll, (hs & 0xFFFFFFFFll) + (lu >> 32), hs >> 32};
 }
 
-// Adds the square of the binary16 value in the low 16 bits of h, in units
-// of 2^-48, to the 96-bit (lo, hi) accumulator.  Exponent 31 (inf/NaN)
-// contributes an arbitrary finite amount; the flag makes the sum irrelevant.
-__device__ __forceinline__ void acc_square(uint32_t h, uint64_t& lo, uint32_t& hi)
+// Carries the limbs into an unsigned 128-bit value (the total is >= 0).
+__device__ __forceinline__ void limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& lo)
 {
-    const uint32_t e = (h >> 10) & 31u;
-    const uint32_t m = (h & 1023u) | (e ? 1024u : 0u);
-    const uint32_t s = e ? 2u * e - 2u : 0u;                 // 2*max(e,1) - 2, 0..60
-    const uint64_t sq = uint64_t(m * m);                     // < 2^22
-    const uint64_t l = sq << s;                              // bits 0..63
-    const uint32_t h2 = uint32_t((sq << (s > 32u ? s - 32u : 0u)) >> 32);  // bits 64..95
-    const uint64_t nl = lo + l;
-    hi += h2 + (nl < l ? 1u : 0u);
-    lo = nl;
+    const int64_t c0 = s.l0 >> 32;
+    const uint64_t w0 = uint64_t(s.l0) & 0xFFFFFFFFull;
+    const int64_t t1 = s.l1 + c0;
+    const uint64_t w1 = uint64_t(t1) & 0xFFFFFFFFull;
+    const int64_t t2 = s.l2 + (t1 >> 32);        // limbs 2 and up, < 2^63
+    lo = w0 | (w1 << 32);
+    hi = uint64_t(t2);
 }
 
-// Two binary16 values per 32-bit word.  The exponent test adds 0x0400 to
-// each masked exponent field: only an all-ones field carries into bit 15
-// (resp. 31), and the low half never carries into the high half.
-__device__ __forceinline__ void acc_word(uint32_t w, uint64_t& lo, uint32_t& hi, uint32_t& flag)
-{
-    flag |= (w & 0x7C007C00u) + 0x04000400u;
-    acc_square(w & 0xFFFFu, lo, hi);
-    acc_square(w >> 16, lo, hi);
-}
-
-__device__ __forceinline__ void acc_vec(u32x4 v, uint64_t& lo, uint32_t& hi, uint32_t& flag)
-{
-    acc_word(v.x, lo, hi, flag);
-    acc_word(v.y, lo, hi, flag);
-    acc_word(v.z, lo, hi, flag);
-    acc_word(v.w, lo, hi, flag);
-}
-
-// Exact unsigned 128-bit integer -> binary64, round to nearest even.  The
-// top 64 significant bits go through the (correctly rounded) 64-bit
-// conversion with every lower nonzero bit folded into bit 0 as a sticky bit;
-// bit 0 lies far below the rounding position, so the rounding is exact.
+// Exact unsigned 128-bit integer -> binary64, round to nearest even: the top
+// 64 significant bits go through the (correctly rounded) 64-bit conversion
+// with every lower nonzero bit folded into bit 0 as a sticky bit, far below
+// the rounding position.
 __device__ double u128_to_f64(uint64_t hi, uint64_t lo)
 {
     if (hi == 0)
@@ -95,11 +104,11 @@ __device__ double u128_to_f64(uint64_t hi, uint64_t lo)
     return ldexp(double(top | (rest != 0 ? 1u : 0u)), 64 - lz);
 }
 
-__device__ void decide(zero_step_state_t* st, const DecideArgs& d, U128 units, bool ovf)
+__device__ void decide(zero_step_state_t* st, const DecideArgs& d, uint64_t hi, uint64_t lo, bool ovf)
 {
     const double S = st->loss_scale;
-    st->sumsq_units[0] = units.lo;
-    st->sumsq_units[1] = units.hi;
+    st->sumsq_units[0] = lo;
+    st->sumsq_units[1] = hi;
     st->overflow = ovf ? 1 : 0;
     if (ovf) {
         const double s2 = S * d.backoff;
@@ -112,7 +121,7 @@ __device__ void decide(zero_step_state_t* st, const DecideArgs& d, U128 units, b
         st->gmul = 0.0f;
         return;
     }
-    const double sumsq = ldexp(u128_to_f64(units.hi, units.lo), -48);
+    const double sumsq = ldexp(u128_to_f64(hi, lo), -48);
     const double norm = sqrt(sumsq) / S;
     st->skip = 0;
     st->sumsq = sumsq;
@@ -141,72 +150,80 @@ __device__ void decide(zero_step_state_t* st, const DecideArgs& d, U128 units, b
     st->good_steps = good;
 }
 
-// Folds (lo, hi, flag) over the workgroup; the result is valid in thread 0.
-__device__ __forceinline__ void block_fold(U128& acc, uint32_t& flag)
+// Sums limbs and ORs flags over the workgroup; the result is valid in thread 0.
+__device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
 {
-    __shared__ uint64_t s_lo[kNormBlock / 64], s_hi[kNormBlock / 64];
-    __shared__ uint32_t s_flag[kNormBlock / 64];
+    __shared__ int64_t s0[kNormBlock / 64], s1[kNormBlock / 64], s2[kNormBlock / 64];
+    __shared__ uint32_t sf[kNormBlock / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-        U128 o;
-        o.lo = __shfl_xor(acc.lo, off, 64);
-        o.hi = __shfl_xor(acc.hi, off, 64);
+        s.l0 += __shfl_xor(s.l0, off, 64);
+        s.l1 += __shfl_xor(s.l1, off, 64);
+        s.l2 += __shfl_xor(s.l2, off, 64);
         flag |= __shfl_xor(flag, off, 64);
-        acc = add128(acc, o);
     }
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
-        s_lo[wave] = acc.lo;
-        s_hi[wave] = acc.hi;
-        s_flag[wave] = flag;
+        s0[wave] = s.l0;
+        s1[wave] = s.l1;
+        s2[wave] = s.l2;
+        sf[wave] = flag;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int w = 1; w < kNormBlock / 64; ++w) {
-            acc = add128(acc, U128{s_lo[w], s_hi[w]});
-            flag |= s_flag[w];
+            s.l0 += s0[w];
+            s.l1 += s1[w];
+            s.l2 += s2[w];
+            flag |= sf[w];
         }
     }
+    __syncthreads();                               // the arrays are reused by the last workgroup
 }
 
 __global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const uint16_t* __restrict__ g, uint64_t n,
                                                                    zero_step_state_t* __restrict__ st,
                                                                    NormPartial* __restrict__ ws, DecideArgs d)
 {
-    uint64_t lo = 0;
-    uint32_t hi = 0, flag = 0;
+    double ah = 0.0, al = 0.0;
+    uint32_t flag = 0;
     const uint64_t nvec = n >> 3;
     const u32x4* __restrict__ gv = reinterpret_cast<const u32x4*>(g);
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
     uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
-    for (; j + 3 * stride < nvec; j += 4 * stride) {
+    for (; j + 3 * stride < nvec; j += 4 * stride) {      // four 16-byte loads in flight
         const u32x4 a = __builtin_nontemporal_load(gv + j);
         const u32x4 b = __builtin_nontemporal_load(gv + j + stride);
         const u32x4 c = __builtin_nontemporal_load(gv + j + 2 * stride);
         const u32x4 e = __builtin_nontemporal_load(gv + j + 3 * stride);
-        acc_vec(a, lo, hi, flag);
-        acc_vec(b, lo, hi, flag);
-        acc_vec(c, lo, hi, flag);
-        acc_vec(e, lo, hi, flag);
+        acc_vec(a, ah, al, flag);
+        acc_vec(b, ah, al, flag);
+        acc_vec(c, ah, al, flag);
+        acc_vec(e, ah, al, flag);
     }
     for (; j < nvec; j += stride)
-        acc_vec(__builtin_nontemporal_load(gv + j), lo, hi, flag);
-    if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {        // the last n % 8 elements
-        const uint32_t h = g[(nvec << 3) + threadIdx.x];
+        acc_vec(__builtin_nontemporal_load(gv + j), ah, al, flag);
+    if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {         // the last n % 8 elements
+        const uint16_t h = g[(nvec << 3) + threadIdx.x];
         flag |= (h & 0x7C00u) + 0x0400u;
-        acc_square(h, lo, hi);
+        acc_square(__builtin_bit_cast(_Float16, h), ah, al);
+    }
+    if (flag & 0x80008000u) {                              // an inf/NaN: the sum is void
+        ah = 0.0;
+        al = 0.0;
     }
 
-    U128 acc{lo, hi};
-    block_fold(acc, flag);
+    Limbs s = to_limbs(ah, al);
+    block_fold(s, flag);
 
     __shared__ uint32_t s_last;
     if (threadIdx.x == 0) {
         NormPartial p;
-        p.lo = acc.lo;
-        p.hi = acc.hi;
+        p.l0 = s.l0;
+        p.l1 = s.l1;
+        p.l2 = s.l2;
         p.flag = flag;
-        p.pad[0] = p.pad[1] = p.pad[2] = 0;
+        p.pad = 0;
         ws[blockIdx.x] = p;
         // release this block's partial / acquire everyone else's
         const uint32_t prev = __hip_atomic_fetch_add(&st->done_blocks, 1u, __ATOMIC_ACQ_REL,
@@ -217,18 +234,22 @@ __global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const uint16_
     if (!s_last)
         return;
 
-    // Last workgroup: fold every partial.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");      // acquire for every thread of this block
-    U128 tot{0, 0};
+    // Last workgroup: fold every partial (integer limbs: order is irrelevant).
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    Limbs t{0, 0, 0};
     uint32_t tflag = 0;
     for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock) {
         const NormPartial p = ws[b];
-        tot = add128(tot, U128{p.lo, p.hi});
+        t.l0 += p.l0;
+        t.l1 += p.l1;
+        t.l2 += p.l2;
         tflag |= p.flag;
     }
-    block_fold(tot, tflag);
+    block_fold(t, tflag);
     if (threadIdx.x == 0) {
-        decide(st, d, tot, (tflag & 0x80008000u) != 0);
+        uint64_t hi, lo;
+        limbs_to_u128(t, hi, lo);
+        decide(st, d, hi, lo, (tflag & 0x80008000u) != 0);
         st->done_blocks = 0;                                 // re-arm for the next call
     }
 }

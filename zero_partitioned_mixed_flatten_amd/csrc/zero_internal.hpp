@@ -31,19 +31,24 @@ int hip_fail(hipError_t e);
 // Checks the launch that was just enqueued.
 int launch_status();
 
+// Bytes of dynamic LDS that, reserved by each workgroup of a kernel that
+// uses none, limit the current device to blocks_per_cu resident workgroups
+// per CU (0 if the device cannot be queried).
+uint32_t lds_reservation(int blocks_per_cu);
+
 // ---- norm/overflow reduction geometry (shared by the host size query and
 // the launch) ----------------------------------------------------------------
-constexpr int kNormBlock = 256;
-constexpr uint64_t kNormMaxBlocks = 2048;
-constexpr uint64_t kNormMaxPerThread = uint64_t(1) << 15;   // keeps a thread's sum < 2^95
-constexpr uint64_t kNormMaxElems = uint64_t(1) << 47;       // keeps the total < 2^127
+constexpr int kNormBlock = 1024;                            // 16 wavefronts, one workgroup per CU
+constexpr uint64_t kNormMaxBlocks = 256;                    // one per CU of an MI355X
+constexpr uint64_t kNormMaxPerThread = uint64_t(1) << 12;   // keeps the binary64 partial sums exact
+constexpr uint64_t kNormMaxElems = uint64_t(1) << 40;       // keeps the limb sums inside int64
 
-// One block's exact partial: sum of squares in units of 2^-48 as a 128-bit
-// integer, plus the OR-ed exponent test bits.
+// One workgroup's exact partial: the sum of squares in 2^-48 units as signed
+// base-2^32 limbs (l0 + l1*2^32 + l2*2^64), plus the OR-ed exponent test bits.
 struct alignas(16) NormPartial {
-    uint64_t lo, hi;
+    int64_t l0, l1, l2;
     uint32_t flag;
-    uint32_t pad[3];
+    uint32_t pad;
 };
 static_assert(sizeof(NormPartial) == 32, "partial layout");
 
