@@ -3,7 +3,10 @@ MI355X.
 
 A step is the whole hot path on one data-parallel rank's shard:
 flatten (per-layer fp16 grads -> flat partition) -> exact norm/overflow +
-decision -> fused unscale/clip/AdamW/fp16-copy.  Default workload: the
+decision -> fused unscale/clip/AdamW/fp16-copy.  By default the flatten
+computes the exact-norm partials while it copies and a decide-only pass
+folds them (--path fused); --path separate runs the standalone norm pass
+over the partition instead.  Both take bit-identical decisions.  Default workload: the
 GPT-2 1.5B-like model (48 layers, hidden 1600, vocab 50257) partitioned over
 Nd = 16, rank 8: 97,350,700 parameters from 39 per-layer gradient segments.
 Inputs (fp32 masters, per-layer fp16 gradients) are synthetic, seeded, and
@@ -92,6 +95,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2", choices=["tiny", "gpt2", "100b", "1t"])
+    ap.add_argument("--path", default="fused", choices=["fused", "separate"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
@@ -135,7 +139,8 @@ def main():
         del gpart
     log(f"inputs generated in {time.time() - t:.1f} s")
 
-    dev = Z.ShardStep(n)
+    fused = args.path == "fused"
+    dev = Z.ShardStep(n, fused=fused)
     dev.p32.copy_(torch.from_numpy(p32))
     dev.p16.copy_(dev.p32.half())
     dev.init_state(w.scale0)
@@ -155,10 +160,16 @@ def main():
         dev.buckets = plans[k % nsets]
         if ev is not None:
             ev[0].record(stream)
-        dev.flatten()
+        if fused:
+            dev.flatten_norm()
+        else:
+            dev.flatten()
         if ev is not None:
             ev[1].record(stream)
-        dev.norm_overflow(hp)
+        if fused:
+            dev.decide(hp)
+        else:
+            dev.norm_overflow(hp)
         if ev is not None:
             ev[2].record(stream)
         dev.adam()
@@ -186,7 +197,8 @@ def main():
     mean = lambda xs: sum(xs) / len(xs)
     adam_s = mean(adam_ms) / 1e3
     achieved = ADAM_BYTES * n / adam_s / 1e9
-    log(f"step {1e3 * el / args.steps:.3f} ms; flatten {mean(flat_ms) * 1e3:.1f} us, norm {mean(norm_ms) * 1e3:.1f} us,"
+    k1, k2 = ("flatten_norm", "decide") if fused else ("flatten", "norm_overflow")
+    log(f"step {1e3 * el / args.steps:.3f} ms; {k1} {mean(flat_ms) * 1e3:.1f} us, {k2} {mean(norm_ms) * 1e3:.1f} us,"
         f" adam {mean(adam_ms) * 1e3:.1f} us ({achieved:.0f} GB/s); skipped={st.skipped_total} scale={st.loss_scale:g}")
 
     # streaming-copy reference on the same byte count as one Adam launch
@@ -211,7 +223,8 @@ def main():
         cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds)
 
     traffic = measured_traffic(n)
-    step_bytes = (ADAM_BYTES + NORM_BYTES + FLATTEN_BYTES) * n
+    step_bpp = ADAM_BYTES + FLATTEN_BYTES + (0 if fused else NORM_BYTES)
+    step_bytes = step_bpp * n
     out = {
         "metric": METRIC,
         "value": n * args.steps / el,
@@ -228,15 +241,14 @@ def main():
         "config": {"workload": f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard",
                    "params": n, "segments": len(w.layout.segments), "bucket_elems": w.bucket_elems,
                    "state": "fp16 p,g + fp32 p,m,v (16 B/param)", "loss_scale0": w.scale0,
-                   "step_bytes_per_param": ADAM_BYTES + NORM_BYTES + FLATTEN_BYTES},
+                   "path": args.path, "step_bytes_per_param": step_bpp},
         "roofline": {"bound": "hbm", "kernel": "adam_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": ADAM_BYTES * n},
         "step_gbps": step_bytes / (el / args.steps) / 1e9,
-        "kernels_us": {"flatten": 1e3 * mean(flat_ms), "norm_overflow": 1e3 * mean(norm_ms),
-                       "adam_step": 1e3 * mean(adam_ms)},
-        "kernels_gbps": {"flatten": FLATTEN_BYTES * n / (mean(flat_ms) / 1e3) / 1e9,
-                         "norm_overflow": NORM_BYTES * n / (mean(norm_ms) / 1e3) / 1e9,
+        "kernels_us": {k1: 1e3 * mean(flat_ms), k2: 1e3 * mean(norm_ms), "adam_step": 1e3 * mean(adam_ms)},
+        "kernels_gbps": {k1: FLATTEN_BYTES * n / (mean(flat_ms) / 1e3) / 1e9,
+                         **({} if fused else {k2: NORM_BYTES * n / (mean(norm_ms) / 1e3) / 1e9}),
                          "adam_step": achieved},
         "copy_reference_gbps": copy_gbps,
         "cpu_baseline": cpu,

@@ -172,6 +172,42 @@ int zero_step_state_init(zero_step_state_t* dev_state, double initial_scale, voi
 int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, void* dst, uint64_t dst_len,
                         int dst_dtype, int accumulate, void* stream);
 
+/* ---- fused flatten + norm (the norm without a second pass) ----------- */
+
+/* Bytes of one per-workgroup partial of the exact sum (opaque contents). */
+#define ZERO_NORM_PARTIAL_BYTES 32
+
+/* Number of partials zero_flatten_norm_bucket writes for this segment list
+ * (one per workgroup it launches; host only, no device work).  0 for NULL. */
+uint64_t zero_flatten_norm_partials(const zero_segment_t* segs, uint32_t nsegs);
+
+/* The fp16 flatten of zero_flatten_bucket (bit copy, or fp16 accumulate),
+ * which also computes, for every value it stores, the exact square and the
+ * inf/NaN test, and writes one partial per workgroup to partials[0 ..
+ * zero_flatten_norm_partials(segs, nsegs)).  For a step flattened in several
+ * buckets, give each call its own stretch of one partials buffer and fold all
+ * of them with zero_shard_decide.  The norm so obtained covers exactly the
+ * elements the segments write (the whole partition when the segments cover
+ * it, as in a ZeRO shard; paper card, "Method": contiguous buffers).
+ * dst: device binary16, dst_len elements, 16-byte aligned; partials: device,
+ * 16-byte aligned, partials_capacity entries of ZERO_NORM_PARTIAL_BYTES.
+ * Errors: those of zero_flatten_bucket, and ZERO_EINVAL (NULL partials),
+ *         ZERO_EALIGN, ZERO_ERANGE (partials_capacity too small). */
+int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nsegs, uint16_t* dst, uint64_t dst_len,
+                             int accumulate, void* partials, uint64_t partials_capacity, void* stream);
+
+/* Bytes of device workspace zero_shard_decide needs to fold `count` partials. */
+size_t zero_decide_workspace_bytes(uint64_t count);
+
+/* Folds `count` partials written by zero_flatten_norm_bucket into the exact
+ * sum and overflow flag, then takes exactly the decision that
+ * zero_shard_norm_overflow takes (same fields of dev_state, bit for bit).
+ * partials, workspace: device, 16-byte aligned; hp: host.
+ * Errors: as zero_shard_norm_overflow (ZERO_ERANGE: count > 2^30 or
+ *         workspace too small). */
+int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,
+                      zero_step_state_t* dev_state, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace zero_shard_norm_overflow needs for n elements
  * (per-block partial sums; fixed for a given n). */
 size_t zero_norm_workspace_bytes(uint64_t n);

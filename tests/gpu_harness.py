@@ -120,7 +120,8 @@ class Run:
         return np.arange(self.n) if self.sample is None else self.sample
 
 
-def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77) -> Run:
+def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77, fused: bool = False) -> Run:
+    """fused: run the step as flatten-with-norm-partials + decide + Adam."""
     r = Run(w)
     n = w.n
     if sample is not None and sample < n:
@@ -131,7 +132,7 @@ def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77) ->
         edges += list(range(min(n, 64))) + list(range(max(0, n - 64), n))
         r.sample = np.unique(np.clip(np.concatenate([rng.integers(0, n, sample), np.array(edges)]), 0, n - 1))
     p32 = shardgen.master_params(w)
-    r.dev = Z.ShardStep(n)
+    r.dev = Z.ShardStep(n, fused=fused)
     if n:
         r.dev.p32.copy_(torch.from_numpy(p32))
         r.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
@@ -157,7 +158,8 @@ def step(r: Run, check: bool = True, check_full_cast: bool = True, exact: bool =
     del gpart
     dsrcs = [to_dev16(s) for s in srcs]
     t1 = time.time()
-    log(f"{w.name} n={w.n} step {k}: launch (segments={len(w.layout.segments)}, bucket={w.bucket_elems})")
+    log(f"{w.name} n={w.n} step {k}: launch (segments={len(w.layout.segments)}, bucket={w.bucket_elems}, "
+        f"fused={r.dev.fused})")
     r.dev.set_segments(dsrcs, w.layout.segments, w.bucket_elems)
     r.dev.step(r.hp_d)
     # oracle: its own flatten of the same sources, then the exact reduction and decision

@@ -181,3 +181,36 @@ def test_state_init_and_copy_validation(Z):
     assert L.zero_step_state_init(FAKE + 4, 1.0, None) == E.ZERO_EALIGN
     assert L.zero_stream_copy(0, FAKE, 16, None) == E.ZERO_EINVAL
     assert L.zero_stream_copy(FAKE, FAKE, 15, None) == E.ZERO_EALIGN
+
+
+def test_flatten_norm_partial_count(Z):
+    rng = np.random.default_rng(8)
+    numels, segs = shardgen.random_segments(rng, 50_000, 9000)
+    arr, k = Z.make_segments([(FAKE, so, do, c) for _, so, do, c in segs] + [(FAKE, 0, 0, 0)])
+    want = 0
+    for _, _, do, c in segs:                      # one workgroup per 1024 aligned 8-vectors, at least one
+        head = min((8 - do % 8) % 8, c)
+        nv = (c - head) // 8
+        want += -(-nv // 1024) if nv else 1
+    assert Z.zero_flatten_norm_partials(arr, k) == want          # the empty segment needs none
+    assert Z.lib().zero_flatten_norm_partials(None, 3) == 0
+
+
+def test_fused_and_decide_validation(Z):
+    L, E = Z.lib(), Z._lib
+    arr, k = Z.make_segments([(FAKE, 0, 0, 5000)])
+    need = Z.zero_flatten_norm_partials(arr, k)
+    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 5000, 0, 0, need, None) == E.ZERO_EINVAL
+    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 5000, 0, FAKE + 8, need, None) == E.ZERO_EALIGN
+    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 5000, 0, FAKE, need - 1, None) == E.ZERO_ERANGE
+    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 4999, 0, FAKE, need, None) == E.ZERO_ERANGE
+    assert L.zero_flatten_norm_bucket(arr, k, FAKE + 2, 5000, 0, FAKE, need, None) == E.ZERO_EALIGN
+    assert L.zero_flatten_norm_bucket(None, 0, 0, 0, 0, 0, 0, None) == E.ZERO_OK
+    ws = Z.zero_decide_workspace_bytes(1000)
+    hp = Z.hparams()
+    assert L.zero_shard_decide(0, 10, C.byref(hp), FAKE, FAKE, ws, None) == E.ZERO_EINVAL
+    assert L.zero_shard_decide(FAKE + 8, 10, C.byref(hp), FAKE, FAKE, ws, None) == E.ZERO_EALIGN
+    assert L.zero_shard_decide(FAKE, 1000, C.byref(hp), FAKE, FAKE, 0, None) == E.ZERO_ERANGE
+    assert L.zero_shard_decide(FAKE, (1 << 30) + 1, C.byref(hp), FAKE, FAKE, 1 << 20, None) == E.ZERO_ERANGE
+    bad = Z.hparams(beta2=1.0)
+    assert L.zero_shard_decide(FAKE, 10, C.byref(bad), FAKE, FAKE, ws, None) == E.ZERO_EINVAL

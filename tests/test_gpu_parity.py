@@ -31,45 +31,50 @@ def _small(name, n, seed, max_seg=None, misalign=True):
     return w
 
 
-def test_tiny_workload_ten_steps_full_parity():
+@pytest.mark.parametrize("fused", [False, True])
+def test_tiny_workload_ten_steps_full_parity(fused):
     w = shardgen.workload("tiny")
-    r = H.start(w)
+    r = H.start(w, fused=fused)
     for _ in range(w.steps):
         H.step(r)
     assert r.st.step == 10 and r.stats["fp32_not_bitwise"] == 0, r.stats
     H.log(f"tiny: {r.stats}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 63, 4099, 65_536 * 3 + 5, (1 << 20) + 3])
-def test_ragged_sizes_misaligned_segments(n):
+def test_ragged_sizes_misaligned_segments(n, fused):
     w = _small(f"ragged{n}", n, seed=n)
-    r = H.start(w)
+    r = H.start(w, fused=fused)
     for _ in range(3):
         H.step(r)
     assert r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
-def test_many_segments_over_launch_limit():
+@pytest.mark.parametrize("fused", [False, True])
+def test_many_segments_over_launch_limit(fused):
     # > 64 segments forces several flatten launches in one call
     w = _small("many", 300_000, seed=3, max_seg=2000, misalign=False)
     assert len(w.layout.segments) > 64
-    r = H.start(w)
+    r = H.start(w, fused=fused)
     for _ in range(2):
         H.step(r)
 
 
-def test_empty_shard():
+@pytest.mark.parametrize("fused", [False, True])
+def test_empty_shard(fused):
     w = _small("empty", 0, seed=0)
     w.layout = shardgen.ShardLayout("empty", 0, 1, 0, 0, 0, [], [], [])
-    r = H.start(w)
+    r = H.start(w, fused=fused)
     H.step(r)
     s = r.dev.read_state()
     assert s.sumsq == 0.0 and s.step == 1 and s.overflow == 0
 
 
-def test_gpt2_shard_full_size():
+@pytest.mark.parametrize("fused", [False, True])
+def test_gpt2_shard_full_size(fused):
     w = shardgen.workload("gpt2")
-    r = H.start(w, sample=1 << 20)
+    r = H.start(w, sample=1 << 20, fused=fused)
     for _ in range(3):
         t = H.step(r)
         H.log(f"gpt2 timings {t}")
@@ -79,7 +84,7 @@ def test_gpt2_shard_full_size():
 @pytest.mark.timeout(900)
 def test_stress_loss_scale_trajectory_full_size():
     w = shardgen.workload("stress")
-    r = H.start(w, sample=1 << 16)
+    r = H.start(w, sample=1 << 16, fused=True)
     snap = None
     for k in range(1, w.steps + 1):
         if k in w.inject:
@@ -105,7 +110,7 @@ def test_100b_shard_full_size():
 @pytest.mark.timeout(900)
 def test_1t_shard_full_size_bucketed():
     w = shardgen.workload("1t")
-    r = H.start(w, sample=1 << 20)
+    r = H.start(w, sample=1 << 20, fused=True)
     assert len(r.dev.buckets) == 0
     for _ in range(2):
         H.step(r)
@@ -233,3 +238,48 @@ def test_stream_copy():
     Z.zero_stream_copy(y, x, x.numel() * 4)
     torch.cuda.synchronize()
     assert torch.equal(x, y)
+
+
+def test_fused_and_separate_paths_decide_identically():
+    """The fused flatten + decide and the flatten + standalone norm take the
+    same decision bit for bit (both sums are exact), and write the same
+    partition, on a bucketed layout with misaligned segments."""
+    w = _small("fused-vs-separate", 3_000_017, seed=21, max_seg=400_000)
+    w.bucket_elems = 1_000_000
+    runs = [H.start(w, fused=f) for f in (False, True)]
+    for _ in range(3):
+        for r in runs:
+            H.step(r)
+        a, b = (r.dev.read_state() for r in runs)
+        assert bytes(a) == bytes(b)
+        assert torch.equal(runs[0].dev.grad16.view(torch.int16), runs[1].dev.grad16.view(torch.int16))
+    for x, y in zip((runs[0].dev.p16, runs[0].dev.p32), (runs[1].dev.p16, runs[1].dev.p32)):
+        assert torch.equal(_bits(x), _bits(y))
+
+
+def test_fused_flatten_accumulate_norm():
+    """Gradient accumulation in fp16: the fused flatten's partials describe the
+    accumulated values it stores."""
+    rng = np.random.default_rng(33)
+    n = 100_003
+    numels, segs = shardgen.random_segments(rng, n, 20_000)
+    srcs = [shardgen.to_f16_bits((rng.standard_normal(k) * 50).astype(np.float32)) for k in numels]
+    dst0 = shardgen.to_f16_bits((rng.standard_normal(n) * 50).astype(np.float32))
+    ref = dst0.copy()
+    O.flatten(srcs, segs, ref, accumulate=True)
+    dsrcs = [H.to_dev16(s) for s in srcs]
+    arr, k = Z.make_segments([(dsrcs[t].data_ptr(), so, do, c) for t, so, do, c in segs])
+    count = Z.zero_flatten_norm_partials(arr, k)
+    partials = torch.empty(count * Z.NORM_PARTIAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = H.to_dev16(dst0.copy())
+    H.log(f"fused accumulate n={n} partials={count}")
+    Z.zero_flatten_norm_bucket(arr, k, dst, partials, n, True)
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st, 1.0)
+    ws = torch.empty(max(16, Z.zero_decide_workspace_bytes(count)), dtype=torch.uint8, device="cuda")
+    Z.zero_shard_decide(partials, count, Z.hparams(), st, ws)
+    s = Z.read_state(st)
+    assert np.array_equal(H.bits16(dst), ref)
+    sumsq, ovf = O.norm_overflow(ref)
+    assert s.overflow == ovf == 0 and np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+    assert s.as_dict()["sumsq_units"] == H.exact_units(ref)

@@ -6,16 +6,18 @@ ctypes binding with the same entry-point names plus a small helper that wires
 them to torch-owned device buffers.  Importing it loads the library and fails
 loudly if it has not been built -- there is no CPU fallback.
 """
-from ._lib import (EXPORTS, STATE_BYTES, ZERO_F16, ZERO_F32, HParams, Segment, StepState, ZeroError, lib,
-                   make_segments, read_state, zero_bucket_segments, zero_flatten_bucket,
-                   zero_norm_workspace_bytes, zero_shard_adam_step, zero_shard_norm_overflow,
+from ._lib import (EXPORTS, NORM_PARTIAL_BYTES, STATE_BYTES, ZERO_F16, ZERO_F32, HParams, Segment, StepState,
+                   ZeroError, lib, make_segments, read_state, zero_bucket_segments, zero_decide_workspace_bytes,
+                   zero_flatten_bucket, zero_flatten_norm_bucket, zero_flatten_norm_partials,
+                   zero_norm_workspace_bytes, zero_shard_adam_step, zero_shard_decide, zero_shard_norm_overflow,
                    zero_state_bytes, zero_status_string, zero_step_state_init, zero_stream_copy)
 from .stepper import ShardStep, hparams
 
 lib()
 
-__all__ = ["EXPORTS", "STATE_BYTES", "ZERO_F16", "ZERO_F32", "HParams", "Segment", "ShardStep", "StepState",
-           "ZeroError", "hparams", "lib", "make_segments", "read_state", "zero_bucket_segments",
-           "zero_flatten_bucket", "zero_norm_workspace_bytes", "zero_shard_adam_step",
-           "zero_shard_norm_overflow", "zero_state_bytes", "zero_status_string", "zero_step_state_init",
-           "zero_stream_copy"]
+__all__ = ["EXPORTS", "NORM_PARTIAL_BYTES", "STATE_BYTES", "ZERO_F16", "ZERO_F32", "HParams", "Segment",
+           "ShardStep", "StepState", "ZeroError", "hparams", "lib", "make_segments", "read_state",
+           "zero_bucket_segments", "zero_decide_workspace_bytes", "zero_flatten_bucket",
+           "zero_flatten_norm_bucket", "zero_flatten_norm_partials", "zero_norm_workspace_bytes",
+           "zero_shard_adam_step", "zero_shard_decide", "zero_shard_norm_overflow", "zero_state_bytes",
+           "zero_status_string", "zero_step_state_init", "zero_stream_copy"]

@@ -18,7 +18,9 @@ ZERO_F16, ZERO_F32 = 1, 2
 # Every function the public header declares (checked against the header by a test).
 EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "zero_step_state_init",
            "zero_flatten_bucket", "zero_norm_workspace_bytes", "zero_shard_norm_overflow",
-           "zero_shard_adam_step", "zero_stream_copy")
+           "zero_shard_adam_step", "zero_stream_copy", "zero_flatten_norm_partials", "zero_flatten_norm_bucket",
+           "zero_decide_workspace_bytes", "zero_shard_decide")
+NORM_PARTIAL_BYTES = 32
 
 
 class ZeroError(RuntimeError):
@@ -81,8 +83,15 @@ def lib():
         L.zero_shard_norm_overflow.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
         L.zero_shard_adam_step.argtypes = [vp, vp, vp, vp, vp, u64, vp, vp]
         L.zero_stream_copy.argtypes = [vp, vp, u64, vp]
+        L.zero_flatten_norm_partials.argtypes = [C.POINTER(Segment), u32]
+        L.zero_flatten_norm_partials.restype = u64
+        L.zero_flatten_norm_bucket.argtypes = [C.POINTER(Segment), u32, vp, u64, i32, vp, u64, vp]
+        L.zero_decide_workspace_bytes.argtypes = [u64]
+        L.zero_decide_workspace_bytes.restype = C.c_size_t
+        L.zero_shard_decide.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
         for name in EXPORTS:
-            if name not in ("zero_status_string", "zero_norm_workspace_bytes"):
+            if name not in ("zero_status_string", "zero_norm_workspace_bytes", "zero_flatten_norm_partials",
+                            "zero_decide_workspace_bytes"):
                 getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -180,6 +189,34 @@ def zero_shard_adam_step(p16, p32, m32, v32, grad16, n: int, dev_state, stream=N
 
 def zero_stream_copy(dst, src, nbytes: int, stream=None) -> None:
     _check("zero_stream_copy", lib().zero_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
+
+
+def zero_flatten_norm_partials(segs, nsegs: int) -> int:
+    return int(lib().zero_flatten_norm_partials(segs, nsegs))
+
+
+def zero_flatten_norm_bucket(segs, nsegs: int, dst, partials, dst_len: Optional[int] = None,
+                             accumulate: bool = False, partials_offset: int = 0, stream=None) -> None:
+    """Fused fp16 flatten + exact-norm partials; writes them from entry
+    `partials_offset` of the uint8 device buffer `partials`."""
+    if dst_len is None:
+        dst_len = dst.numel()
+    cap = partials.numel() // NORM_PARTIAL_BYTES - partials_offset
+    ptr = _ptr(partials) + partials_offset * NORM_PARTIAL_BYTES
+    _check("zero_flatten_norm_bucket",
+           lib().zero_flatten_norm_bucket(segs, nsegs, _ptr(dst), dst_len, int(bool(accumulate)), ptr, cap,
+                                          _stream(stream)))
+
+
+def zero_decide_workspace_bytes(count: int) -> int:
+    return int(lib().zero_decide_workspace_bytes(count))
+
+
+def zero_shard_decide(partials, count: int, hp: HParams, dev_state, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_shard_decide",
+           lib().zero_shard_decide(_ptr(partials), count, C.byref(hp), _ptr(dev_state), _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
 
 
 def read_state(dev_state) -> StepState:

@@ -17,16 +17,29 @@
 // for the fp16 copy, so no LDS and no MFMA.  Measured on MI355X inside the
 // whole step: one 16-byte vector per thread; nontemporal loads (the per-layer
 // sources are read once); plain stores, so the fresh partition is still in
-// the 256 MB Infinity Cache when the norm reads it next.
-#include "zero_internal.hpp"
+// the 256 MB Infinity Cache when the norm pass reads it next.
+//
+// The fused form (NORM) also accumulates the exact sum of squares and the
+// inf/NaN test of every value it stores (exact_norm.hpp) and writes one
+// partial per workgroup, so the norm needs no second pass over the
+// partition: zero_shard_decide folds the partials and takes the decision.
+// It takes four vectors per thread (the workgroup fold is amortised over
+// 8192 elements) and nontemporal stores (nothing reads the partition before
+// the Adam pass, and draining dirty cache lines during it costs more).
+#include "exact_norm.hpp"
 
 namespace zero {
 namespace {
 
 constexpr uint32_t kMaxSegs = 64;
 constexpr int kBlock = 256;
-constexpr int kVecsPerThread = 1;
-constexpr uint64_t kVecsPerBlock = uint64_t(kBlock) * kVecsPerThread;
+
+// 16-byte vectors per thread: 1 for the plain flatten, 4 for the fused one.
+template <bool NORM>
+struct Geometry {
+    static constexpr int kVecsPerThread = NORM ? 4 : 1;
+    static constexpr uint64_t kVecsPerBlock = uint64_t(kBlock) * kVecsPerThread;
+};
 
 enum Mode { kCopy16 = 0, kAcc16 = 1, kTo32 = 2, kAcc32 = 3 };
 
@@ -36,43 +49,59 @@ struct FlatArgs {
     uint64_t count[kMaxSegs];
     uint32_t first_block[kMaxSegs + 1]; // prefix sum of blocks per segment
     uint32_t nsegs;
+    NormPartial* partials;              // fused form: one per workgroup of this launch
 };
 
-__device__ __forceinline__ uint64_t head_len(uint64_t dst_off, uint64_t count)
+__host__ __device__ inline uint64_t head_len(uint64_t dst_off, uint64_t count)
 {
     const uint64_t h = (8 - (dst_off & 7)) & 7;
     return h < count ? h : count;
 }
 
+// Stores one element; returns the binary16 bits stored (fp16 destinations).
 template <int MODE>
-__device__ __forceinline__ void put_scalar(void* dst, uint64_t i, uint16_t s)
+__device__ __forceinline__ uint16_t put_scalar(void* dst, uint64_t i, uint16_t s)
 {
     if (MODE == kCopy16) {
         static_cast<uint16_t*>(dst)[i] = s;
+        return s;
     } else if (MODE == kAcc16) {
         _Float16* d = static_cast<_Float16*>(dst);
-        d[i] = d[i] + __builtin_bit_cast(_Float16, s);        // correctly rounded binary16 add
+        const _Float16 r = d[i] + __builtin_bit_cast(_Float16, s);   // correctly rounded binary16 add
+        d[i] = r;
+        return __builtin_bit_cast(uint16_t, r);
     } else if (MODE == kTo32) {
         static_cast<float*>(dst)[i] = float(__builtin_bit_cast(_Float16, s));
+        return 0;
     } else {
         float* d = static_cast<float*>(dst);
         d[i] = d[i] + float(__builtin_bit_cast(_Float16, s));
+        return 0;
     }
 }
 
-// dst index i is a multiple of 8.
-template <int MODE>
-__device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s)
+// Stores 8 elements at dst index i (a multiple of 8), nontemporally if NTS;
+// returns the binary16 bits stored (fp16 destinations).
+template <int MODE, bool NTS>
+__device__ __forceinline__ u32x4 put_vector(void* dst, uint64_t i, u32x4 s)
 {
     if (MODE == kCopy16) {
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i) = s;
+        u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i);
+        if (NTS)
+            __builtin_nontemporal_store(s, d);
+        else
+            *d = s;
+        return s;
     } else if (MODE == kAcc16) {
         u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i);
-        f16x8 a = __builtin_bit_cast(f16x8, *d);
-        f16x8 b = __builtin_bit_cast(f16x8, s);
-        *d = __builtin_bit_cast(u32x4, a + b);
+        const u32x4 r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, *d) + __builtin_bit_cast(f16x8, s));
+        if (NTS)
+            __builtin_nontemporal_store(r, d);
+        else
+            *d = r;
+        return r;
     } else {
-        f16x8 h = __builtin_bit_cast(f16x8, s);
+        const f16x8 h = __builtin_bit_cast(f16x8, s);
         f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(dst) + i);
         f32x4 lo = {float(h[0]), float(h[1]), float(h[2]), float(h[3])};
         f32x4 hi = {float(h[4]), float(h[5]), float(h[6]), float(h[7])};
@@ -82,12 +111,15 @@ __device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s)
         }
         d[0] = lo;
         d[1] = hi;
+        return u32x4{0, 0, 0, 0};
     }
 }
 
-template <int MODE>
+template <int MODE, bool NORM>
 __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __restrict__ dst)
 {
+    constexpr int kVecsPerThread = Geometry<NORM>::kVecsPerThread;
+    constexpr uint64_t kVecsPerBlock = Geometry<NORM>::kVecsPerBlock;
     // Segment of this workgroup: the last s with first_block[s] <= blockIdx.x.
     const uint32_t b = blockIdx.x;
     uint32_t lo = 0, hi = a.nsegs;
@@ -102,6 +134,9 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     const uint64_t nv = (cnt - head) >> 3;
     const uint64_t local = b - a.first_block[lo];
     const bool vec_src = is_aligned(src + head, 16);
+
+    double ah = 0.0, al = 0.0;                 // fused form: this thread's exact sum
+    uint32_t flag = 0;
 
     // body: vectors [v0, v1) of this segment
     const uint64_t v0 = local * kVecsPerBlock;
@@ -119,8 +154,11 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
 #pragma unroll
         for (int k = 0; k < kVecsPerThread; ++k) {
             const uint64_t v = v0 + threadIdx.x + uint64_t(k) * kBlock;
-            if (v < v1)
-                put_vector<MODE>(dst, dbody + 8 * v, r[k]);
+            if (v < v1) {
+                const u32x4 stored = put_vector<MODE, NORM>(dst, dbody + 8 * v, r[k]);
+                if (NORM)
+                    exact::acc_vec(stored, ah, al, flag);
+            }
         }
     } else {
         for (uint64_t v = v0 + threadIdx.x; v < v1; v += kBlock) {
@@ -130,7 +168,9 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
             r.y = uint32_t(s[2]) | (uint32_t(s[3]) << 16);
             r.z = uint32_t(s[4]) | (uint32_t(s[5]) << 16);
             r.w = uint32_t(s[6]) | (uint32_t(s[7]) << 16);
-            put_vector<MODE>(dst, dbody + 8 * v, r);
+            const u32x4 stored = put_vector<MODE, NORM>(dst, dbody + 8 * v, r);
+            if (NORM)
+                exact::acc_vec(stored, ah, al, flag);
         }
     }
 
@@ -138,37 +178,53 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     if (local == 0) {
         const uint64_t t0 = head + 8 * nv;
         const uint64_t t = threadIdx.x;
-        if (t < head)
-            put_scalar<MODE>(dst, doff + t, src[t]);
-        if (t < cnt - t0)
-            put_scalar<MODE>(dst, doff + t0 + t, src[t0 + t]);
+        if (t < head) {
+            const uint16_t stored = put_scalar<MODE>(dst, doff + t, src[t]);
+            if (NORM)
+                exact::acc_bits(stored, ah, al, flag);
+        }
+        if (t < cnt - t0) {
+            const uint16_t stored = put_scalar<MODE>(dst, doff + t0 + t, src[t0 + t]);
+            if (NORM)
+                exact::acc_bits(stored, ah, al, flag);
+        }
+    }
+
+    if (NORM) {                                 // every thread reaches this point
+        exact::Limbs s = exact::to_limbs(ah, al, flag);
+        exact::block_fold<kBlock>(s, flag);
+        if (threadIdx.x == 0)
+            a.partials[blockIdx.x] = exact::make_partial(s, flag);
     }
 }
 
+template <bool NORM>
 int launch(const FlatArgs& a, uint32_t blocks, int mode, void* dst, hipStream_t s)
 {
     switch (mode) {
-    case kCopy16: hipLaunchKernelGGL(flatten_kernel<kCopy16>, dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    case kAcc16: hipLaunchKernelGGL(flatten_kernel<kAcc16>, dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    case kTo32: hipLaunchKernelGGL(flatten_kernel<kTo32>, dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    default: hipLaunchKernelGGL(flatten_kernel<kAcc32>, dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    case kCopy16: hipLaunchKernelGGL((flatten_kernel<kCopy16, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    case kAcc16: hipLaunchKernelGGL((flatten_kernel<kAcc16, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    case kTo32: hipLaunchKernelGGL((flatten_kernel<kTo32, false>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    default: hipLaunchKernelGGL((flatten_kernel<kAcc32, false>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
     }
     return launch_status();
 }
 
-}  // namespace
-}  // namespace zero
-
-using namespace zero;
-
-extern "C" int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, void* dst, uint64_t dst_len,
-                                   int dst_dtype, int accumulate, void* stream)
+// Workgroups a segment needs: one per kVecsPerBlock body vectors, at least one.
+template <bool NORM>
+uint64_t blocks_for(const zero_segment_t& sg)
 {
-    if ((dst_dtype != ZERO_F16 && dst_dtype != ZERO_F32) || (nsegs && (!segs || !dst)))
+    constexpr uint64_t vpb = Geometry<NORM>::kVecsPerBlock;
+    const uint64_t head = head_len(sg.dst_off, sg.count);
+    const uint64_t nv = (sg.count - head) / 8;
+    return nv ? (nv + vpb - 1) / vpb : 1;
+}
+
+int validate(const zero_segment_t* segs, uint32_t nsegs, const void* dst, uint64_t dst_len)
+{
+    if (nsegs && (!segs || !dst))
         return ZERO_EINVAL;
-    if (nsegs == 0)
-        return ZERO_OK;
-    if (!is_aligned(dst, 16))
+    if (nsegs && !is_aligned(dst, 16))
         return ZERO_EALIGN;
     for (uint32_t i = 0; i < nsegs; ++i) {
         if (segs[i].count == 0)
@@ -181,27 +237,27 @@ extern "C" int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, v
             return ZERO_ERANGE;
         if (segs[i].src_off > (UINT64_MAX >> 2) - segs[i].count)
             return ZERO_ERANGE;
+        if (blocks_for<false>(segs[i]) > 0x7fffffffull)      // the larger of the two counts
+            return ZERO_ERANGE;
     }
-    const int mode = (dst_dtype == ZERO_F16 ? kCopy16 : kTo32) + (accumulate ? 1 : 0);
-    hipStream_t s = (hipStream_t)stream;
+    return ZERO_OK;
+}
 
+// Splits the call into launches of at most kMaxSegs segments and 2^31 - 1
+// workgroups; `fn(args, blocks)` is called once per launch, in order.
+template <bool NORM, typename F>
+int for_each_launch(const zero_segment_t* segs, uint32_t nsegs, F&& fn)
+{
     FlatArgs a;
+    a.partials = nullptr;
     uint32_t k = 0;
     uint64_t blocks = 0;
     for (uint32_t i = 0; i <= nsegs; ++i) {
-        uint64_t need = 0;
-        if (i < nsegs && segs[i].count) {
-            const uint64_t head = (8 - (segs[i].dst_off & 7)) & 7;
-            const uint64_t nv = segs[i].count > head ? (segs[i].count - head) / 8 : 0;
-            need = nv ? (nv + kVecsPerBlock - 1) / kVecsPerBlock : 1;
-            if (need > 0x7fffffffull)
-                return ZERO_ERANGE;
-        }
-        // flush the batch when it is full, would overflow the grid, or at the end
+        const uint64_t need = (i < nsegs && segs[i].count) ? blocks_for<NORM>(segs[i]) : 0;
         if (k && (i == nsegs || k == kMaxSegs || blocks + need > 0x7fffffffull)) {
             a.first_block[k] = uint32_t(blocks);
             a.nsegs = k;
-            int rc = launch(a, uint32_t(blocks), mode, dst, s);
+            const int rc = fn(a, uint32_t(blocks));
             if (rc != ZERO_OK)
                 return rc;
             k = 0;
@@ -217,4 +273,58 @@ extern "C" int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, v
         ++k;
     }
     return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zero
+
+using namespace zero;
+
+extern "C" int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, void* dst, uint64_t dst_len,
+                                   int dst_dtype, int accumulate, void* stream)
+{
+    if (dst_dtype != ZERO_F16 && dst_dtype != ZERO_F32)
+        return ZERO_EINVAL;
+    const int rc = validate(segs, nsegs, dst, dst_len);
+    if (rc != ZERO_OK)
+        return rc;
+    const int mode = (dst_dtype == ZERO_F16 ? kCopy16 : kTo32) + (accumulate ? 1 : 0);
+    hipStream_t s = (hipStream_t)stream;
+    return for_each_launch<false>(segs, nsegs,
+                                  [&](FlatArgs& a, uint32_t blocks) { return launch<false>(a, blocks, mode, dst, s); });
+}
+
+extern "C" uint64_t zero_flatten_norm_partials(const zero_segment_t* segs, uint32_t nsegs)
+{
+    if (!segs)
+        return 0;
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < nsegs; ++i)
+        if (segs[i].count)
+            total += blocks_for<true>(segs[i]);
+    return total;
+}
+
+extern "C" int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nsegs, uint16_t* dst,
+                                        uint64_t dst_len, int accumulate, void* partials,
+                                        uint64_t partials_capacity, void* stream)
+{
+    const int rc = validate(segs, nsegs, dst, dst_len);
+    if (rc != ZERO_OK)
+        return rc;
+    const uint64_t need = zero_flatten_norm_partials(segs, nsegs);
+    if (need && !partials)
+        return ZERO_EINVAL;
+    if (need && !is_aligned(partials, 16))
+        return ZERO_EALIGN;
+    if (need > partials_capacity)
+        return ZERO_ERANGE;
+    const int mode = accumulate ? kAcc16 : kCopy16;
+    hipStream_t s = (hipStream_t)stream;
+    NormPartial* next = static_cast<NormPartial*>(partials);
+    return for_each_launch<true>(segs, nsegs, [&](FlatArgs& a, uint32_t blocks) {
+        a.partials = next;
+        next += blocks;
+        return launch<true>(a, blocks, mode, dst, s);
+    });
 }

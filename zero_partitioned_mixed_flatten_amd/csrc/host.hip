@@ -51,6 +51,16 @@ __global__ void state_init_kernel(zero_step_state_t* st, double scale)
     *st = s;
 }
 
+uint64_t decide_grid(uint64_t count)
+{
+    // Four partials per thread at least, at most one workgroup per CU.
+    const uint64_t per_block = uint64_t(kNormBlock) * 4;
+    uint64_t g = (count + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > kNormMaxBlocks) g = kNormMaxBlocks;
+    return g;
+}
+
 // ---- occupancy cap ----------------------------------------------------------------
 
 uint32_t lds_reservation(int blocks_per_cu)
@@ -145,6 +155,11 @@ extern "C" int zero_bucket_segments(const zero_segment_t* segs, uint32_t nsegs, 
 extern "C" size_t zero_norm_workspace_bytes(uint64_t n)
 {
     return size_t(norm_grid(n)) * sizeof(NormPartial);
+}
+
+extern "C" size_t zero_decide_workspace_bytes(uint64_t count)
+{
+    return size_t(decide_grid(count)) * sizeof(NormPartial);
 }
 
 extern "C" int zero_step_state_init(zero_step_state_t* dev_state, double initial_scale, void* stream)

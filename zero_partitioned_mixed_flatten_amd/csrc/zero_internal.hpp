@@ -54,4 +54,9 @@ static_assert(sizeof(NormPartial) == 32, "partial layout");
 
 uint64_t norm_grid(uint64_t n);
 
+// Partials folded by the decide-only pass (the fused flatten writes one per
+// workgroup); stored partials are normalised, so 2^30 of them fit in int64 sums.
+constexpr uint64_t kMaxPartials = uint64_t(1) << 30;
+uint64_t decide_grid(uint64_t count);
+
 }  // namespace zero

@@ -16,7 +16,12 @@ from . import _lib as Z
 
 
 class ShardStep:
-    def __init__(self, n: int, device="cuda"):
+    """fused=False: flatten, then the standalone exact-norm pass over the
+    partition.  fused=True: the flatten computes the exact-norm partials while
+    it copies and a decide-only pass folds them (no second read of the
+    partition).  Both take bit-identical decisions."""
+
+    def __init__(self, n: int, device="cuda", fused: bool = False):
         import torch
         self.n = int(n)
         alloc = max(1, self.n)
@@ -31,6 +36,11 @@ class ShardStep:
         self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
         self.buckets: List[Tuple[object, int]] = []
         self._sources: Sequence = ()
+        self.fused = bool(fused)
+        self.partials = None            # fused form: one 32-byte partial per flatten workgroup
+        self.partial_offsets: List[int] = []
+        self.partial_count = 0
+        self.decide_ws = None
 
     # ---- set-up ----------------------------------------------------------------
     def init_state(self, initial_scale: float) -> None:
@@ -49,6 +59,22 @@ class ShardStep:
                             for b in range(0, self.n, bucket_elems)]
         else:
             self.buckets = [(segs, nsegs)]
+        if self.fused:
+            self._plan_partials()
+
+    def _plan_partials(self) -> None:
+        import torch
+        offsets, total = [], 0
+        for segs, nsegs in self.buckets:
+            offsets.append(total)
+            total += Z.zero_flatten_norm_partials(segs, nsegs)
+        self.partial_offsets, self.partial_count = offsets, total
+        need = max(1, total) * Z.NORM_PARTIAL_BYTES
+        if self.partials is None or self.partials.numel() < need:
+            self.partials = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws = max(16, Z.zero_decide_workspace_bytes(total))
+        if self.decide_ws is None or self.decide_ws.numel() < ws:
+            self.decide_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
 
     # ---- the step ---------------------------------------------------------------
     def flatten(self) -> None:
@@ -61,9 +87,20 @@ class ShardStep:
     def adam(self) -> None:
         Z.zero_shard_adam_step(self.p16, self.p32, self.m32, self.v32, self.grad16, self.n, self.state)
 
+    def flatten_norm(self) -> None:
+        for (segs, nsegs), off in zip(self.buckets, self.partial_offsets):
+            Z.zero_flatten_norm_bucket(segs, nsegs, self.grad16, self.partials, self.n, False, off)
+
+    def decide(self, hp: Z.HParams) -> None:
+        Z.zero_shard_decide(self.partials, self.partial_count, hp, self.state, self.decide_ws)
+
     def step(self, hp: Z.HParams) -> None:
-        self.flatten()
-        self.norm_overflow(hp)
+        if self.fused:
+            self.flatten_norm()
+            self.decide(hp)
+        else:
+            self.flatten()
+            self.norm_overflow(hp)
         self.adam()
 
     def read_state(self) -> Z.StepState:
