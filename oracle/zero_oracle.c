@@ -198,30 +198,79 @@ void oracle_flatten(const oracle_segment_t* segs, uint32_t nsegs, void* dst,
 }
 
 /* ------------------------------------------------------------------ */
+/* Exact sums of squares are held as integer counts of 2^-48 units in   */
+/* 128 bits.  A sum that reaches 2^128 units (2^80) cannot be held; it  */
+/* is reported like an inf/NaN gradient (overflow, step skipped, scale  */
+/* backed off).  Neither gradient type can get there on a real shard:   */
+/* binary16 squares stay below 2^80 units, so it takes 2^48 elements.   */
+/* ------------------------------------------------------------------ */
+static int add_units(unsigned __int128* acc, unsigned __int128 u)
+{
+    unsigned __int128 t = *acc + u;
+    if (t < *acc)
+        return 1;                                       /* wrapped: >= 2^128 */
+    *acc = t;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Squared L2 norm and the inf/NaN test of the flat binary16 gradient.  */
 /* overflow = some element has an all-ones exponent (inf or NaN).       */
 /* sumsq    = sum over i of g_i^2, computed EXACTLY and rounded once to  */
 /*            binary64.  Each g_i^2 is an integer multiple of 2^-48 (the */
-/*            square of the smallest subnormal, 2^-24) below 2^32, so the */
-/*            sum is held as an integer count of 2^-48 units in 128 bits */
-/*            (exact for n < 2^48) and converted with one rounding.      */
-/*            When overflow is set the sum has no meaning and is +inf.   */
+/*            square of the smallest subnormal, 2^-24) below 2^32, so   */
+/*            the sum is an integer count of 2^-48 units, converted     */
+/*            with one rounding.  When overflow is set the sum has no   */
+/*            meaning and is +inf.                                      */
 /* ------------------------------------------------------------------ */
 void oracle_norm_overflow(const uint16_t* g, uint64_t n, double* sumsq, int32_t* overflow)
 {
     unsigned __int128 units = 0;
     int32_t ovf = 0;
-    for (uint64_t i = 0; i < n; ++i) {
+    for (uint64_t i = 0; i < n && !ovf; ++i) {
         if ((g[i] & 0x7c00u) == 0x7c00u) {
             ovf = 1;
-            continue;
+            break;
         }
         double x = (double)oracle_f32_from_f16(g[i]);
         double sq = x * x;                              /* exact: 22 bits */
-        units += (unsigned __int128)(sq * 0x1p48);      /* exact integer < 2^80 */
+        ovf = add_units(&units, (unsigned __int128)(sq * 0x1p48));   /* integer < 2^80 */
     }
     *overflow = ovf;
     *sumsq = ovf ? INFINITY : (double)units * 0x1p-48;  /* one rounding */
+}
+
+/* ------------------------------------------------------------------ */
+/* The same reduction over an fp32 gradient partition (the gradient-    */
+/* accumulation form: micro-batch fp16 gradients summed in fp32; the    */
+/* DeepSpeed article leaves gradient accumulation to the library).      */
+/* overflow = some element is inf or NaN or has |x| >= 2^24.  A sum of  */
+/*            at most 256 binary16 values stays below 2^24, so on the   */
+/*            accumulation domain this is the inf/NaN test; larger      */
+/*            values are treated as an overflow of the scaled gradient. */
+/* sumsq    = sum over i of x_i^2, each square rounded to the nearest   */
+/*            multiple of 2^-48, summed exactly and rounded once to     */
+/*            binary64.  A binary32 sum of binary16 values is a        */
+/*            multiple of 2^-24, so on the accumulation domain every    */
+/*            square is already on that grid and this is the exact sum. */
+/*            (A square x^2 = M^2 2^(2E) never lies exactly halfway     */
+/*            between two multiples of 2^-48, so no tie rule is needed.)*/
+/* ------------------------------------------------------------------ */
+void oracle_norm_overflow_f32(const float* g, uint64_t n, double* sumsq, int32_t* overflow)
+{
+    unsigned __int128 units = 0;
+    int32_t ovf = 0;
+    for (uint64_t i = 0; i < n && !ovf; ++i) {
+        double x = (double)g[i];
+        if (!(fabs(x) < 0x1p24)) {                      /* inf, NaN or out of domain */
+            ovf = 1;
+            break;
+        }
+        double sq = x * x;                              /* exact: 48 bits, < 2^48 */
+        ovf = add_units(&units, (unsigned __int128)nearbyint(sq * 0x1p48));   /* < 2^96 */
+    }
+    *overflow = ovf;
+    *sumsq = ovf ? INFINITY : (double)units * 0x1p-48;
 }
 
 /* ------------------------------------------------------------------ */
@@ -331,6 +380,28 @@ void oracle_adam_update(const oracle_state_t* st, uint16_t* p16, float* p32, flo
         return;
     for (uint64_t i = 0; i < n; ++i) {
         float g = oracle_f32_from_f16(g16[i]) * st->gmul;
+        float m = st->beta1 * m32[i] + st->omb1 * g;
+        float v = st->beta2 * v32[i] + st->omb2 * (g * g);
+        float mh = m / st->bc1;
+        float vh = v / st->bc2;
+        float u = mh / (sqrtf(vh) + st->eps) + st->wd * p32[i];
+        float p = p32[i] - st->lr * u;
+        m32[i] = m;
+        v32[i] = v;
+        p32[i] = p;
+        p16[i] = oracle_f16_from_f32(p);
+    }
+}
+
+/* The element update with an fp32 gradient (the accumulation form): the
+ * same operations in the same order, with g = grad32[i] * gmul. */
+void oracle_adam_update_f32(const oracle_state_t* st, uint16_t* p16, float* p32, float* m32,
+                            float* v32, const float* g32, uint64_t n)
+{
+    if (st->skip)
+        return;
+    for (uint64_t i = 0; i < n; ++i) {
+        float g = g32[i] * st->gmul;
         float m = st->beta1 * m32[i] + st->omb1 * g;
         float v = st->beta2 * v32[i] + st->omb2 * (g * g);
         float mh = m / st->bc1;

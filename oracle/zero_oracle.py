@@ -59,6 +59,8 @@ def lib():
         L.oracle_state_bytes.restype = C.c_int
         L.oracle_flatten.argtypes = [C.POINTER(OracleSegment), u32, vp, C.c_int, C.c_int]
         L.oracle_norm_overflow.argtypes = [vp, u64, C.POINTER(C.c_double), C.POINTER(i32)]
+        L.oracle_norm_overflow_f32.argtypes = [vp, u64, C.POINTER(C.c_double), C.POINTER(i32)]
+        L.oracle_adam_update_f32.argtypes = [C.POINTER(OracleState), vp, vp, vp, vp, vp, u64]
         L.oracle_state_init.argtypes = [C.POINTER(OracleState), C.c_double]
         L.oracle_decide.argtypes = [C.POINTER(OracleState), C.POINTER(OracleHParams),
                                     C.c_double, i32]
@@ -130,6 +132,16 @@ def norm_overflow(g16: np.ndarray):
     return s.value, o.value
 
 
+def norm_overflow_f32(g32: np.ndarray):
+    """-> (sumsq, overflow) of a flat fp32 gradient: each square rounded to the
+    2^-48 grid, summed exactly, rounded once; |x| >= 2^31, inf, NaN overflow."""
+    g32 = np.ascontiguousarray(g32, dtype=np.float32)
+    s = C.c_double()
+    o = C.c_int32()
+    lib().oracle_norm_overflow_f32(_ptr(g32, np.float32), g32.size, C.byref(s), C.byref(o))
+    return s.value, o.value
+
+
 # ---- decision + update ----------------------------------------------------------
 
 def hparams(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01,
@@ -155,6 +167,13 @@ def adam_update(st: OracleState, p16, p32, m32, v32, g16) -> None:
     lib().oracle_adam_update(C.byref(st), _ptr(p16, np.uint16), _ptr(p32, np.float32),
                              _ptr(m32, np.float32), _ptr(v32, np.float32),
                              _ptr(g16, np.uint16), n)
+
+
+def adam_update_f32(st: OracleState, p16, p32, m32, v32, g32) -> None:
+    n = p32.size
+    assert p16.size == m32.size == v32.size == g32.size == n
+    lib().oracle_adam_update_f32(C.byref(st), _ptr(p16, np.uint16), _ptr(p32, np.float32),
+                                 _ptr(m32, np.float32), _ptr(v32, np.float32), _ptr(g32, np.float32), n)
 
 
 def step(hp: OracleHParams, st: OracleState, srcs, segments, grad16, p16, p32, m32, v32) -> None:
