@@ -6,7 +6,12 @@ flatten (per-layer fp16 grads -> flat partition) -> exact norm/overflow +
 decision -> fused unscale/clip/AdamW/fp16-copy.  By default the flatten
 computes the exact-norm partials while it copies and a decide-only pass
 folds them (--path fused); --path separate runs the standalone norm pass
-over the partition instead.  Both take bit-identical decisions.  Default workload: the
+over the partition instead.  Both take bit-identical decisions.
+--path accum32 runs the gradient-accumulation form: --micro-batches K
+per-layer fp16 gradient sets added into an fp32 partition (the last one with
+the exact-norm partials), decide, and the update reading the fp32 gradient
+(30 bytes per parameter); a step is then one optimizer step over K
+micro-batches.  Default workload: the
 GPT-2 1.5B-like model (48 layers, hidden 1600, vocab 50257) partitioned over
 Nd = 16, rank 8: 97,350,700 parameters from 39 per-layer gradient segments.
 Inputs (fp32 masters, per-layer fp16 gradients) are synthetic, seeded, and
@@ -37,8 +42,11 @@ sys.path.insert(0, ROOT)
 METRIC = "shard Adam-step params/sec + achieved HBM GB/s (% of peak) at 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 ADAM_BYTES = 28          # read fp16 g + fp32 p,m,v; write fp32 p,m,v + fp16 p
+ADAM32_BYTES = 30        # the same with an fp32 g
 NORM_BYTES = 2           # read fp16 g
 FLATTEN_BYTES = 4        # read fp16 source, write fp16 partition
+WIDEN_BYTES = 6          # read fp16 source, write fp32 partition
+ACCUM_BYTES = 10         # read fp16 source and fp32 partition, write fp32 partition
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "adam_step_gpt2_shard_pmc.json")
 ADAM_SOURCE = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc", "adam.hip")
 
@@ -65,7 +73,10 @@ def measured_traffic(n):
     return s.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, p32, grads_host, budget_s):
+def cpu_baseline(w, p32, grads_host, budget_s, micro=0):
+    """The oracle on whole steps of the same shard until budget_s has passed
+    (at most 20 steps).  micro > 0: the gradient-accumulation step over that
+    many micro-batches."""
     import numpy as np
     import oracle as O
     import shardgen
@@ -75,18 +86,26 @@ def cpu_baseline(w, p32, grads_host, budget_s):
     m = np.zeros_like(p)
     v = np.zeros_like(p)
     p16 = shardgen.to_f16_bits(p)
-    grad = np.empty(w.n, np.uint16)
+    grad = np.empty(w.n, np.float32 if micro else np.uint16)
     steps, t0 = 0, time.perf_counter()
     while True:
-        srcs = grads_host[steps % len(grads_host)]
-        O.step(hp, st, srcs, w.layout.segments, grad, p16, p, m, v)
+        if micro:
+            for j in range(micro):
+                O.flatten(grads_host[j], w.layout.segments, grad, accumulate=(j > 0))
+            O.decide(st, hp, *O.norm_overflow_f32(grad))
+            O.adam_update_f32(st, p16, p, m, v, grad)
+        else:
+            srcs = grads_host[steps % len(grads_host)]
+            O.step(hp, st, srcs, w.layout.segments, grad, p16, p, m, v)
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 20:
             break
+    what = (f"{micro} fp16 micro-batches accumulated in fp32 + exact fp32 norm + decision + fp32 AdamW + "
+            f"fp16 copy" if micro else "flatten + exact norm + decision + fp32 AdamW + fp16 copy")
     return {"value": w.n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full step(s) of the same {w.n:,}-parameter shard (flatten + exact norm + "
-                      f"decision + fp32 AdamW + fp16 copy), single-threaded C, {el:.1f} s"}
+            "sample": f"{steps} full step(s) of the same {w.n:,}-parameter shard ({what}), "
+                      f"single-threaded C, {el:.1f} s"}
 
 
 def main():
@@ -95,7 +114,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2", choices=["tiny", "gpt2", "100b", "1t"])
-    ap.add_argument("--path", default="fused", choices=["fused", "separate"])
+    ap.add_argument("--path", default="fused", choices=["fused", "separate", "accum32"])
+    ap.add_argument("--micro-batches", type=int, default=4,
+                    help="micro-batches per optimizer step for --path accum32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
@@ -139,49 +160,63 @@ def main():
         del gpart
     log(f"inputs generated in {time.time() - t:.1f} s")
 
-    fused = args.path == "fused"
-    dev = Z.ShardStep(n, fused=fused)
+    hp = Z.hparams(w.hp.lr, w.hp.beta1, w.hp.beta2, w.hp.eps, w.hp.weight_decay, w.hp.max_grad_norm,
+                   w.hp.backoff, w.hp.growth, w.hp.min_scale, w.hp.growth_interval)
+    dev_sets = [[torch.from_numpy(s.view(np.float16)).cuda() for s in srcs] for srcs in grads_host]
+    accum = args.path == "accum32"
+    fused = args.path in ("fused", "accum32")
+    K = args.micro_batches if accum else 1
+    if accum:
+        if not 1 <= K <= nsets:
+            sys.exit(f"--micro-batches must be 1..{nsets}")
+        dev = Z.AccumStep(n, fused=True)
+        plans = [dev.plan(d, w.layout.segments, w.bucket_elems)[1] for d in dev_sets[:K]]
+    else:
+        dev = Z.ShardStep(n, fused=fused)
+        plans = []
+        for d in dev_sets:
+            dev.set_segments(d, w.layout.segments, w.bucket_elems)
+            plans.append(dev.buckets)
     dev.p32.copy_(torch.from_numpy(p32))
     dev.p16.copy_(dev.p32.half())
     dev.init_state(w.scale0)
-    dev_sets = []
-    for srcs in grads_host:
-        d = [torch.from_numpy(s.view(np.float16)).cuda() for s in srcs]
-        dev_sets.append(d)
-    plans = []
-    for d in dev_sets:
-        dev.set_segments(d, w.layout.segments, w.bucket_elems)
-        plans.append(dev.buckets)
-    hp = Z.hparams(w.hp.lr, w.hp.beta1, w.hp.beta2, w.hp.eps, w.hp.weight_decay, w.hp.max_grad_norm,
-                   w.hp.backoff, w.hp.growth, w.hp.min_scale, w.hp.growth_interval)
     torch.cuda.synchronize()
 
+    # events: [start, after each flatten ..., after decide/norm, after adam]
+    nev = K + 3
+
     def one_step(k, ev=None):
-        dev.buckets = plans[k % nsets]
-        if ev is not None:
-            ev[0].record(stream)
-        if fused:
-            dev.flatten_norm()
-        else:
-            dev.flatten()
-        if ev is not None:
-            ev[1].record(stream)
-        if fused:
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        if accum:
+            for j in range(K):
+                if j == K - 1:
+                    dev.accumulate_norm(plans[j], first=(j == 0))
+                else:
+                    dev.accumulate(plans[j], first=(j == 0))
+                rec(1 + j)
             dev.decide(hp)
         else:
-            dev.norm_overflow(hp)
-        if ev is not None:
-            ev[2].record(stream)
+            dev.buckets = plans[k % nsets]
+            if fused:
+                dev.flatten_norm()
+            else:
+                dev.flatten()
+            rec(1)
+            if fused:
+                dev.decide(hp)
+            else:
+                dev.norm_overflow(hp)
+        rec(nev - 2)
         dev.adam()
-        if ev is not None:
-            ev[3].record(stream)
+        rec(nev - 1)
 
     log(f"warmup {args.warmup} steps")
     for k in range(args.warmup):
         one_step(k)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -191,15 +226,30 @@ def main():
     t1 = time.perf_counter()
     el = t1 - t0
     st = dev.read_state()
-    flat_ms = [e[0].elapsed_time(e[1]) for e in events]
-    norm_ms = [e[1].elapsed_time(e[2]) for e in events]
-    adam_ms = [e[2].elapsed_time(e[3]) for e in events]
     mean = lambda xs: sum(xs) / len(xs)
-    adam_s = mean(adam_ms) / 1e3
-    achieved = ADAM_BYTES * n / adam_s / 1e9
-    k1, k2 = ("flatten_norm", "decide") if fused else ("flatten", "norm_overflow")
-    log(f"step {1e3 * el / args.steps:.3f} ms; {k1} {mean(flat_ms) * 1e3:.1f} us, {k2} {mean(norm_ms) * 1e3:.1f} us,"
-        f" adam {mean(adam_ms) * 1e3:.1f} us ({achieved:.0f} GB/s); skipped={st.skipped_total} scale={st.loss_scale:g}")
+    seg_ms = [mean([e[i].elapsed_time(e[i + 1]) for e in events]) for i in range(nev - 1)]
+    adam_s = seg_ms[-1] / 1e3
+    adam_bpp = ADAM32_BYTES if accum else ADAM_BYTES
+    achieved = adam_bpp * n / adam_s / 1e9
+    if accum:
+        names = [("widen" if j == 0 else "accumulate") + ("_norm" if j == K - 1 else "") for j in range(K)]
+        flat_bpp = [WIDEN_BYTES if j == 0 else ACCUM_BYTES for j in range(K)]
+        names += ["decide", "adam_step_f32"]
+    else:
+        names = ["flatten_norm" if fused else "flatten", "decide" if fused else "norm_overflow", "adam_step"]
+        flat_bpp = [FLATTEN_BYTES]
+    kernels_us = {}
+    kernels_gbps = {}
+    for i, name in enumerate(names):
+        key = name if name not in kernels_us else f"{name}_{i}"
+        kernels_us[key] = 1e3 * seg_ms[i]
+        if i < len(flat_bpp):
+            kernels_gbps[key] = flat_bpp[i] * n / (seg_ms[i] / 1e3) / 1e9
+    if not fused:
+        kernels_gbps["norm_overflow"] = NORM_BYTES * n / (seg_ms[1] / 1e3) / 1e9
+    kernels_gbps[names[-1]] = achieved
+    log(f"step {1e3 * el / args.steps:.3f} ms; " + ", ".join(f"{k} {v:.1f} us" for k, v in kernels_us.items())
+        + f"; adam {achieved:.0f} GB/s; skipped={st.skipped_total} scale={st.loss_scale:g}")
 
     # streaming-copy reference on the same byte count as one Adam launch
     nbytes = (ADAM_BYTES // 2) * n // 16 * 16
@@ -220,11 +270,17 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds)
+        cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds, K if accum else 0)
 
-    traffic = measured_traffic(n)
-    step_bpp = ADAM_BYTES + FLATTEN_BYTES + (0 if fused else NORM_BYTES)
+    traffic = measured_traffic(n) if args.path == "fused" else None
+    if accum:
+        step_bpp = WIDEN_BYTES + ACCUM_BYTES * (K - 1) + ADAM32_BYTES
+    else:
+        step_bpp = ADAM_BYTES + FLATTEN_BYTES + (0 if fused else NORM_BYTES)
     step_bytes = step_bpp * n
+    workload = f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard"
+    if accum:
+        workload += f", {K} fp16 micro-batches accumulated in fp32"
     out = {
         "metric": METRIC,
         "value": n * args.steps / el,
@@ -238,18 +294,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard",
+        "config": {"workload": workload,
                    "params": n, "segments": len(w.layout.segments), "bucket_elems": w.bucket_elems,
-                   "state": "fp16 p,g + fp32 p,m,v (16 B/param)", "loss_scale0": w.scale0,
-                   "path": args.path, "step_bytes_per_param": step_bpp},
-        "roofline": {"bound": "hbm", "kernel": "adam_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                   "state": "fp16 p,g + fp32 p,m,v (16 B/param)" if not accum else
+                            "fp16 p + fp32 g,p,m,v (18 B/param)", "loss_scale0": w.scale0,
+                   "path": args.path, "micro_batches": K, "step_bytes_per_param": step_bpp},
+        "roofline": {"bound": "hbm", "kernel": names[-1], "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": ADAM_BYTES * n},
+                     "traffic": traffic, "algorithmic_bytes": adam_bpp * n},
         "step_gbps": step_bytes / (el / args.steps) / 1e9,
-        "kernels_us": {k1: 1e3 * mean(flat_ms), k2: 1e3 * mean(norm_ms), "adam_step": 1e3 * mean(adam_ms)},
-        "kernels_gbps": {k1: FLATTEN_BYTES * n / (mean(flat_ms) / 1e3) / 1e9,
-                         **({} if fused else {k2: NORM_BYTES * n / (mean(norm_ms) / 1e3) / 1e9}),
-                         "adam_step": achieved},
+        "kernels_us": kernels_us,
+        "kernels_gbps": kernels_gbps,
         "copy_reference_gbps": copy_gbps,
         "cpu_baseline": cpu,
     }

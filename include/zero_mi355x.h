@@ -26,6 +26,17 @@
  *                               fp16 parameter copy (28 bytes per parameter).
  * zero_state_bytes gives the per-rank model-state bytes for each ZeRO stage.
  *
+ * Two further forms of the same step:
+ *   - fused: zero_flatten_norm_bucket computes the exact-norm partials while
+ *     it flattens and zero_shard_decide folds them, so the norm needs no
+ *     second pass over the partition;
+ *   - gradient accumulation (the DeepSpeed article leaves gradient
+ *     accumulation to the library): micro-batch fp16 gradients are added
+ *     into an fp32 partition (zero_flatten_bucket with ZERO_F32, or the
+ *     fused zero_flatten_norm_bucket_f32 for the last micro-batch), and the
+ *     *_f32 reduction and update read that fp32 gradient (30 bytes per
+ *     parameter in the update).
+ *
  * Conventions for every entry point:
  *   - pointers named dev_* or documented as device memory are HIP device
  *     pointers; everything else is host memory;
@@ -103,12 +114,14 @@ typedef struct {
     int64_t  step;              /* t: applied (not skipped) steps */
     int32_t  good_steps;        /* clean steps since the last scale change */
     int32_t  skipped_total;     /* skipped steps so far */
-    /* written by the last zero_shard_norm_overflow */
-    double   sumsq;             /* exact sum of squares of the scaled fp16
+    /* written by the last reduction (zero_shard_norm_overflow, its fp32
+       form, or zero_shard_decide) */
+    double   sumsq;             /* exact sum of squares of the scaled
                                    gradient, rounded once to binary64;
                                    +inf when overflow is set */
     double   grad_norm;         /* sqrt(sumsq) / S (unscaled norm); +inf on overflow */
-    int32_t  overflow;          /* 1 if any gradient element is inf or NaN */
+    int32_t  overflow;          /* 1 if the gradient holds an inf or NaN (or,
+                                   in fp32, a value of magnitude >= 2^24) */
     int32_t  skip;              /* 1 if this step is skipped (== overflow) */
     float    gmul;              /* fp32(coef / S): unscale and clip factor */
     float    bc1, bc2;          /* fp32(1 - beta1^t), fp32(1 - beta2^t) */
@@ -196,12 +209,26 @@ uint64_t zero_flatten_norm_partials(const zero_segment_t* segs, uint32_t nsegs);
 int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nsegs, uint16_t* dst, uint64_t dst_len,
                              int accumulate, void* partials, uint64_t partials_capacity, void* stream);
 
+/* The fp32 flatten of zero_flatten_bucket (dst = fp32(src), or with
+ * accumulate dst = dst + fp32(src) in binary32), which also computes the
+ * exact-norm partials of every fp32 value it stores, under the rules of
+ * zero_shard_norm_overflow_f32.  Used for the last micro-batch of a
+ * gradient-accumulation step: the partials it writes, folded by
+ * zero_shard_decide, give exactly the decision zero_shard_norm_overflow_f32
+ * takes on the finished partition.  It writes
+ * zero_flatten_norm_partials(segs, nsegs) partials, like the fp16 form.
+ * dst: device binary32, dst_len elements, 16-byte aligned; the rest as for
+ * zero_flatten_norm_bucket.  Errors: as zero_flatten_norm_bucket. */
+int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t nsegs, float* dst, uint64_t dst_len,
+                                 int accumulate, void* partials, uint64_t partials_capacity, void* stream);
+
 /* Bytes of device workspace zero_shard_decide needs to fold `count` partials. */
 size_t zero_decide_workspace_bytes(uint64_t count);
 
-/* Folds `count` partials written by zero_flatten_norm_bucket into the exact
- * sum and overflow flag, then takes exactly the decision that
- * zero_shard_norm_overflow takes (same fields of dev_state, bit for bit).
+/* Folds `count` partials written by zero_flatten_norm_bucket (or its fp32
+ * form) into the exact sum and overflow flag, then takes exactly the
+ * decision that zero_shard_norm_overflow (resp. its fp32 form) takes (same
+ * fields of dev_state, bit for bit).
  * partials, workspace: device, 16-byte aligned; hp: host.
  * Errors: as zero_shard_norm_overflow (ZERO_ERANGE: count > 2^30 or
  *         workspace too small). */
@@ -238,6 +265,25 @@ int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hpar
                              zero_step_state_t* dev_state, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Reduce and decide over an fp32 gradient partition (gradient
+ * accumulation: a binary32 sum of micro-batch fp16 gradients).
+ *   overflow = 1 if any element is inf or NaN or has |x| >= 2^24 (a sum of
+ *              at most 256 binary16 values stays below 2^24; larger values
+ *              count as an overflow of the scaled gradient);
+ *   sumsq    = sum of x^2 with each square rounded to the nearest multiple
+ *              of 2^-48, summed exactly and rounded once to binary64 (for
+ *              sums of binary16 values every square is already on that
+ *              grid, so this is the exact sum of squares);
+ * then the same decision as zero_shard_norm_overflow.  An exact sum of
+ * 2^80 or more (more than 2^128 units of 2^-48) also counts as overflow in
+ * both forms; only a partition of billions of elements near 2^24 gets there.
+ * grad32: device, 16-byte aligned; everything else as for
+ * zero_shard_norm_overflow, including the workspace size
+ * (zero_norm_workspace_bytes(n)) and the errors. */
+int zero_shard_norm_overflow_f32(const float* grad32, uint64_t n, const zero_hparams_t* hp,
+                                 zero_step_state_t* dev_state, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* The fused element update, in binary32 with one rounding per operation and
  * this order (unless dev_state says skip, in which case nothing is written):
  *   g  = fp32(grad16[i]) * gmul
@@ -250,11 +296,22 @@ int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hpar
  * All five arrays: device, n elements, 16-byte aligned, index-aligned with
  * each other and with the grad16 the decision was made on; n may be 0.
  * dev_state: as left by zero_shard_norm_overflow (read only here).
- * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_ERANGE (n >= 2^44),
- *         ZERO_EHIP. */
+ * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_ERANGE (n above about 2^42:
+ *         more than 2^31 - 1 workgroups of 2048 parameters), ZERO_EHIP. */
 int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32,
                          const uint16_t* grad16, uint64_t n,
                          const zero_step_state_t* dev_state, void* stream);
+
+/* The same update reading an fp32 gradient (gradient accumulation):
+ *   g = grad32[i] * gmul, then exactly as zero_shard_adam_step.
+ * It reads 4 + 12 bytes and writes 12 + 2 bytes per parameter (30).
+ * dev_state: as left by zero_shard_norm_overflow_f32, or by
+ * zero_shard_decide over zero_flatten_norm_bucket_f32 partials.
+ * grad32: device, n elements, 16-byte aligned; the rest and the errors as
+ * for zero_shard_adam_step. */
+int zero_shard_adam_step_f32(uint16_t* p16, float* p32, float* m32, float* v32,
+                             const float* grad32, uint64_t n,
+                             const zero_step_state_t* dev_state, void* stream);
 
 /* ---- measurement reference ------------------------------------------ */
 

@@ -191,3 +191,122 @@ def step(r: Run, check: bool = True, check_full_cast: bool = True, exact: bool =
         assert torch.equal(r.dev.p16[:w.n].view(torch.int16), r.dev.p32[:w.n].half().view(torch.int16))
     del dsrcs
     return {"gen_s": t1 - t0, "step_s": t2 - t1}
+
+
+# ---- gradient accumulation (fp32 partition) ---------------------------------------
+
+def exact_units32(grad32: np.ndarray) -> Optional[int]:
+    """sum of squares in 2^-48 units of fp32 values that are multiples of
+    2^-24 below 2^24 (the accumulation domain), as a Python integer: with
+    a = x * 2^24 (an integer below 2^48) the square is a^2 units; a is split
+    into 16-bit digits so that every partial product sum fits int64.  None
+    if some value is off that grid."""
+    total = 0
+    m = (1 << 16) - 1
+    for lo in range(0, grad32.size, 1 << 20):
+        x = grad32[lo:lo + (1 << 20)].astype(np.float64)
+        a = x * 2.0 ** 24
+        if not np.all(np.floor(a) == a) or not np.all(np.abs(a) < 2.0 ** 48):
+            return None
+        a = np.abs(a).astype(np.int64)
+        a0, a1, a2 = a & m, (a >> 16) & m, a >> 32
+        sq = lambda u, v: int((u * v).sum())
+        total += (sq(a0, a0) + (2 * sq(a0, a1) << 16) + ((sq(a1, a1) + 2 * sq(a0, a2)) << 32)
+                  + (2 * sq(a1, a2) << 48) + (sq(a2, a2) << 64))
+    return total
+
+
+@dataclass
+class AccumRun:
+    w: shardgen.Workload
+    micro: int
+    sample: Optional[np.ndarray] = None
+    dev: Z.AccumStep = None
+    st: O.OracleState = None
+    hp_o: O.OracleHParams = None
+    hp_d: Z.HParams = None
+    p16: np.ndarray = None
+    p32: np.ndarray = None
+    m32: np.ndarray = None
+    v32: np.ndarray = None
+    k: int = 0
+    stats: dict = field(default_factory=lambda: {"fp32_not_bitwise": 0, "fp32_max_rel": 0.0})
+
+    @property
+    def n(self) -> int:
+        return self.w.n
+
+    def idx(self) -> np.ndarray:
+        return np.arange(self.n) if self.sample is None else self.sample
+
+
+def start_accum(w: shardgen.Workload, micro: int, sample: Optional[int] = None, seed: int = 78,
+                fused: bool = True) -> AccumRun:
+    r = AccumRun(w, micro)
+    n = w.n
+    if sample is not None and sample < n:
+        rng = np.random.default_rng(seed)
+        edges = []
+        for _, _, do, c in w.layout.segments:
+            edges += [do, do + 1, do + c - 1, do + c - 2]
+        edges += list(range(min(n, 64))) + list(range(max(0, n - 64), n))
+        r.sample = np.unique(np.clip(np.concatenate([rng.integers(0, n, sample), np.array(edges)]), 0, n - 1))
+    p32 = shardgen.master_params(w)
+    r.dev = Z.AccumStep(n, fused=fused)
+    if n:
+        r.dev.p32.copy_(torch.from_numpy(p32))
+        r.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
+    r.dev.init_state(w.scale0)
+    i = r.idx()
+    r.p32 = np.ascontiguousarray(p32[i])
+    r.p16 = shardgen.to_f16_bits(r.p32)
+    r.m32 = np.zeros_like(r.p32)
+    r.v32 = np.zeros_like(r.p32)
+    r.st = O.new_state(w.scale0)
+    r.hp_o = oracle_hparams(w.hp)
+    r.hp_d = device_hparams(w.hp)
+    return r
+
+
+def step_accum(r: AccumRun, check: bool = True, exact: bool = True) -> None:
+    """One optimizer step of r.micro micro-batches on both sides."""
+    r.k += 1
+    w = r.w
+    srcs_all, plans, keep = [], [], []
+    for j in range(r.micro):
+        gpart = shardgen.grad_partition(w, (r.k - 1) * r.micro + j + 1, r.st.loss_scale)
+        srcs = shardgen.source_tensors(w.layout, gpart)
+        del gpart
+        srcs_all.append(srcs)
+        dsrcs = [to_dev16(s) for s in srcs]
+        kept, buckets = r.dev.plan(dsrcs, w.layout.segments, w.bucket_elems)
+        keep.append(kept)
+        plans.append(buckets)
+    log(f"{w.name} n={w.n} accum step {r.k}: {r.micro} micro-batches, fused={r.dev.fused}")
+    r.dev.step(plans, r.hp_d)
+    grad = np.zeros(w.n, np.float32)
+    for j, srcs in enumerate(srcs_all):
+        O.flatten(srcs, w.layout.segments, grad, accumulate=(j > 0))
+    sumsq, ovf = O.norm_overflow_f32(grad)
+    O.decide(r.st, r.hp_o, sumsq, ovf)
+    i = r.idx()
+    O.adam_update_f32(r.st, r.p16, r.p32, r.m32, r.v32, np.ascontiguousarray(grad[i]))
+    torch.cuda.synchronize()
+    log(f"{w.name} accum step {r.k}: gpu done, overflow={ovf} norm={r.st.grad_norm:.6g}")
+    if not check:
+        return
+    compare_state(r.dev.read_state(), r.st, exact_units32(grad) if (exact and not ovf) else None)
+    assert np.array_equal(r.dev.grad32[:w.n].cpu().numpy().view(np.uint32), grad.view(np.uint32)), \
+        "accumulated gradient differs"
+    it = torch.from_numpy(i).cuda()
+    d16 = bits16(r.dev.p16[it])
+    assert np.array_equal(d16, r.p16), f"p16 differs at {int(np.sum(d16 != r.p16))} elements"
+    for name, dt, ref in (("p32", r.dev.p32, r.p32), ("m32", r.dev.m32, r.m32), ("v32", r.dev.v32, r.v32)):
+        got = dt[it].cpu().numpy()
+        e = rel_err(got, ref)
+        r.stats["fp32_max_rel"] = max(r.stats["fp32_max_rel"], e)
+        r.stats["fp32_not_bitwise"] += int(np.sum(got.view(np.uint32) != ref.view(np.uint32)))
+        assert e <= FP32_REL_TOL, (name, e)
+    if w.n:
+        assert torch.equal(r.dev.p16[:w.n].view(torch.int16), r.dev.p32[:w.n].half().view(torch.int16))
+    del keep

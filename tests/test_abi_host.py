@@ -119,15 +119,17 @@ def test_workspace_size_is_stable_and_bounded(Z):
 FAKE = 1 << 20          # a 16-byte-aligned address that is never dereferenced
 
 
-def test_adam_validation(Z):
+@pytest.mark.parametrize("fn", ["zero_shard_adam_step", "zero_shard_adam_step_f32"])
+def test_adam_validation(Z, fn):
     L, E = Z.lib(), Z._lib
     ok = dict(p16=FAKE, p32=FAKE, m32=FAKE, v32=FAKE, g=FAKE, st=FAKE)
-    call = lambda **kw: L.zero_shard_adam_step(kw["p16"], kw["p32"], kw["m32"], kw["v32"], kw["g"], kw.get("n", 8),
-                                               kw["st"], None)
+    call = lambda **kw: getattr(L, fn)(kw["p16"], kw["p32"], kw["m32"], kw["v32"], kw["g"], kw.get("n", 8),
+                                       kw["st"], None)
     assert call(**{**ok, "st": 0}) == E.ZERO_EINVAL
     assert call(**{**ok, "p32": 0}) == E.ZERO_EINVAL
     assert call(**{**ok, "m32": FAKE + 4}) == E.ZERO_EALIGN
     assert call(**{**ok, "g": FAKE + 2}) == E.ZERO_EALIGN
+    assert call(**{**ok, "g": FAKE + 8}) == E.ZERO_EALIGN
     assert call(**{**ok, "st": FAKE + 4}) == E.ZERO_EALIGN
     assert call(**{**ok, "p16": 0, "n": 0}) == E.ZERO_OK                 # n == 0: nothing to do
 
@@ -139,14 +141,15 @@ def _hp(Z, **kw):
     return hp
 
 
-def test_norm_validation(Z):
+@pytest.mark.parametrize("fn", ["zero_shard_norm_overflow", "zero_shard_norm_overflow_f32"])
+def test_norm_validation(Z, fn):
     L, E = Z.lib(), Z._lib
     ws = Z.zero_norm_workspace_bytes(1000)
 
     def call(hp=None, g=FAKE, n=1000, st=FAKE, w=FAKE, wsb=ws):
-        return L.zero_shard_norm_overflow(g, n, C.byref(hp or Z.hparams()), st, w, wsb, None)
+        return getattr(L, fn)(g, n, C.byref(hp or Z.hparams()), st, w, wsb, None)
 
-    assert L.zero_shard_norm_overflow(FAKE, 8, None, FAKE, FAKE, ws, None) == E.ZERO_EINVAL
+    assert getattr(L, fn)(FAKE, 8, None, FAKE, FAKE, ws, None) == E.ZERO_EINVAL
     assert call(st=0) == E.ZERO_EINVAL and call(w=0) == E.ZERO_EINVAL and call(g=0) == E.ZERO_EINVAL
     for bad in (dict(lr=-1.0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(weight_decay=-1e-3),
                 dict(backoff=0.0), dict(backoff=1.5), dict(growth=0.5), dict(min_scale=0.0),
@@ -196,16 +199,23 @@ def test_flatten_norm_partial_count(Z):
     assert Z.lib().zero_flatten_norm_partials(None, 3) == 0
 
 
-def test_fused_and_decide_validation(Z):
+@pytest.mark.parametrize("fn", ["zero_flatten_norm_bucket", "zero_flatten_norm_bucket_f32"])
+def test_fused_validation(Z, fn):
     L, E = Z.lib(), Z._lib
+    f = getattr(L, fn)
     arr, k = Z.make_segments([(FAKE, 0, 0, 5000)])
     need = Z.zero_flatten_norm_partials(arr, k)
-    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 5000, 0, 0, need, None) == E.ZERO_EINVAL
-    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 5000, 0, FAKE + 8, need, None) == E.ZERO_EALIGN
-    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 5000, 0, FAKE, need - 1, None) == E.ZERO_ERANGE
-    assert L.zero_flatten_norm_bucket(arr, k, FAKE, 4999, 0, FAKE, need, None) == E.ZERO_ERANGE
-    assert L.zero_flatten_norm_bucket(arr, k, FAKE + 2, 5000, 0, FAKE, need, None) == E.ZERO_EALIGN
-    assert L.zero_flatten_norm_bucket(None, 0, 0, 0, 0, 0, 0, None) == E.ZERO_OK
+    assert f(arr, k, FAKE, 5000, 0, 0, need, None) == E.ZERO_EINVAL
+    assert f(arr, k, FAKE, 5000, 0, FAKE + 8, need, None) == E.ZERO_EALIGN
+    assert f(arr, k, FAKE, 5000, 0, FAKE, need - 1, None) == E.ZERO_ERANGE
+    assert f(arr, k, FAKE, 4999, 0, FAKE, need, None) == E.ZERO_ERANGE
+    assert f(arr, k, FAKE + 2, 5000, 0, FAKE, need, None) == E.ZERO_EALIGN
+    assert f(arr, k, FAKE + 8, 5000, 1, FAKE, need, None) == E.ZERO_EALIGN
+    assert f(None, 0, 0, 0, 0, 0, 0, None) == E.ZERO_OK
+
+
+def test_decide_validation(Z):
+    L, E = Z.lib(), Z._lib
     ws = Z.zero_decide_workspace_bytes(1000)
     hp = Z.hparams()
     assert L.zero_shard_decide(0, 10, C.byref(hp), FAKE, FAKE, ws, None) == E.ZERO_EINVAL

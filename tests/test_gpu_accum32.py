@@ -1,0 +1,199 @@
+"""GPU parity tests of the gradient-accumulation form: K micro-batches of
+per-layer fp16 gradients added into an fp32 partition, the fp32 exact
+reduction (standalone, or fused into the last micro-batch's flatten), the
+decision and the update reading the fp32 gradient -- through the C ABI,
+against the CPU oracle on the same seeded inputs.  Contract as in
+tests/gpu_harness.py: accumulated gradient bitwise, step state bitwise
+(including the exact sum as a 128-bit integer), p16 bitwise, fp32 state
+within 1e-6 relative (0 elements differing expected)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import shardgen
+
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as H  # noqa: E402
+import zero_partitioned_mixed_flatten_amd as Z  # noqa: E402
+
+
+def _small(name, n, seed, max_seg=None, misalign=True):
+    w = shardgen.workload("tiny")
+    w.name = name
+    rng = np.random.default_rng(seed)
+    numels, segs = shardgen.random_segments(rng, n, max_seg or max(1, n // 5), misalign)
+    w.layout = shardgen.ShardLayout(name, n, 1, 0, 0, n, [f"t{i}" for i in range(len(numels))], numels, segs)
+    return w
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("micro", [1, 3])
+def test_accum_tiny_workload_full_parity(fused, micro):
+    w = shardgen.workload("tiny")
+    r = H.start_accum(w, micro, fused=fused)
+    for _ in range(4):
+        H.step_accum(r)
+    assert r.st.step == 4 and r.stats["fp32_not_bitwise"] == 0, r.stats
+    H.log(f"accum tiny micro={micro} fused={fused}: {r.stats}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("n", [1, 7, 9, 4099, 65_536 * 3 + 5, (1 << 20) + 3])
+def test_accum_ragged_sizes_misaligned_segments(n, fused):
+    w = _small(f"accum-ragged{n}", n, seed=100 + n)
+    r = H.start_accum(w, 2, fused=fused)
+    for _ in range(2):
+        H.step_accum(r)
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+def test_accum_empty_shard():
+    w = _small("accum-empty", 0, seed=0)
+    w.layout = shardgen.ShardLayout("empty", 0, 1, 0, 0, 0, [], [], [])
+    for fused in (False, True):
+        r = H.start_accum(w, 2, fused=fused)
+        H.step_accum(r)
+        s = r.dev.read_state()
+        assert s.sumsq == 0.0 and s.step == 1 and s.overflow == 0
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_accum_gpt2_shard_full_size(fused):
+    w = shardgen.workload("gpt2")
+    r = H.start_accum(w, 4, sample=1 << 20, fused=fused)
+    for _ in range(2):
+        H.step_accum(r)
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+@pytest.mark.timeout(900)
+def test_accum_1t_shard_bucketed():
+    w = shardgen.workload("1t")
+    r = H.start_accum(w, 2, sample=1 << 18, fused=True)
+    H.step_accum(r)
+
+
+def test_accum_fused_and_separate_identical():
+    w = _small("accum-fused-vs-separate", 2_000_003, seed=41, max_seg=300_000)
+    w.bucket_elems = 700_000
+    runs = [H.start_accum(w, 3, fused=f) for f in (False, True)]
+    for _ in range(2):
+        for r in runs:
+            H.step_accum(r)
+        a, b = (r.dev.read_state() for r in runs)
+        assert bytes(a) == bytes(b)
+    for x, y in zip((runs[0].dev.grad32, runs[0].dev.p32, runs[0].dev.m32),
+                    (runs[1].dev.grad32, runs[1].dev.p32, runs[1].dev.m32)):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+def _crafted_f32(n, seed, top=16777215.0, expo_hi=1):
+    """binary32 values off the 2^-24 grid at every magnitude the domain allows
+    (|x| < 2^(24 + expo_hi - 1)), plus `top` (by default the largest in-domain
+    value) every 97th element."""
+    rng = np.random.default_rng(seed)
+    mant = rng.integers(1 << 23, 1 << 24, n).astype(np.float64)
+    expo = rng.integers(-80, expo_hi, n).astype(np.float64)
+    x = (mant * np.exp2(expo)).astype(np.float32)
+    x *= np.where(rng.integers(0, 2, n) == 1, -1, 1).astype(np.float32)
+    x[::97] = np.float32(top)
+    x[1::101] = np.float32(3 * 2.0 ** -26)
+    return x
+
+
+def _decide_standalone(g32):
+    n = g32.size
+    ws = torch.empty(max(16, Z.zero_norm_workspace_bytes(n)), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st, 1024.0)
+    Z.zero_shard_norm_overflow_f32(torch.from_numpy(g32).cuda(), n, Z.hparams(), st, ws)
+    return Z.read_state(st)
+
+
+@pytest.mark.parametrize("n,small", [(5, False), (4096 * 3 + 1, False), (1_000_003, False), (1_000_003, True)])
+def test_norm_f32_rounds_each_square_to_grid(n, small):
+    # small: |x| < 2^-9, so the total stays below 2^53 units, sumsq is the
+    # exact integer and every per-square rounding shows in it
+    g = _crafted_f32(n, seed=n, top=2.0 ** -10, expo_hi=-32) if small else _crafted_f32(n, seed=n)
+    H.log(f"norm f32 crafted n={n} small={small}")
+    s = _decide_standalone(g)
+    sumsq, ovf = O.norm_overflow_f32(g)
+    assert s.overflow == ovf == 0
+    assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+
+
+def test_norm_f32_special_values_everywhere():
+    n = 4 * 5000 + 3
+    rng = np.random.default_rng(6)
+    # sums of two binary16 values: on the 2^-24 grid, so the exact sum is checkable
+    base = sum((rng.standard_normal(n) * 1000).astype(np.float16).astype(np.float32) for _ in range(2))
+    cases = [(0, np.inf), (n - 1, -np.inf), (n - 2, np.nan), (777, 2.0 ** 24), (4 * 4999, -(2.0 ** 24)),
+             (31, 3e38), (None, 16777215.0)]
+    for pos, val in cases:
+        g = base.copy()
+        if pos is None:
+            g[::5] = val
+        else:
+            g[pos] = val
+        H.log(f"norm f32 special pos={pos} val={val}")
+        s = _decide_standalone(g)
+        sumsq, ovf = O.norm_overflow_f32(g)
+        assert s.overflow == ovf == (1 if pos is not None else 0)
+        assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+        if not ovf:
+            assert s.as_dict()["sumsq_units"] == H.exact_units32(g)
+
+
+def test_fused_f32_accumulate_into_crafted_partition():
+    """The fused fp32 flatten sums squares of the values it stores: a partition
+    holding off-grid values, values that the added micro-batch pushes to
+    2^24 (overflow) or keeps just below it."""
+    rng = np.random.default_rng(44)
+    n = 300_007
+    numels, segs = shardgen.random_segments(rng, n, 40_000)
+    srcs = [shardgen.to_f16_bits((rng.standard_normal(k) * 20).astype(np.float32)) for k in numels]
+    dsrcs = [H.to_dev16(s) for s in srcs]
+    arr, k = Z.make_segments([(dsrcs[t].data_ptr(), so, do, c) for t, so, do, c in segs])
+    count = Z.zero_flatten_norm_partials(arr, k)
+    partials = torch.empty(count * Z.NORM_PARTIAL_BYTES, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(16, Z.zero_decide_workspace_bytes(count)), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    flat = np.concatenate([srcs[t][so:so + c] for t, so, _, c in segs]).view(np.float16).astype(np.float32)
+    base = _crafted_f32(n, seed=45, top=2.0 ** 23)             # room for the added micro-batch
+    pos = int(np.argmax(flat > 0))
+    cases = [("off-grid", base)]
+    over = base.copy()
+    over[pos] = np.float32(2.0 ** 24) - flat[pos]            # lands on 2^24 after the add
+    cases.append(("reaches 2^24", over))
+    for name, dst0 in cases:
+        ref = dst0.copy()
+        O.flatten(srcs, segs, ref, accumulate=True)
+        dst = torch.from_numpy(dst0.copy()).cuda()
+        H.log(f"fused f32 accumulate: {name}, partials={count}")
+        Z.zero_flatten_norm_bucket_f32(arr, k, dst, partials, n, True)
+        Z.zero_step_state_init(st, 1.0)
+        Z.zero_shard_decide(partials, count, Z.hparams(), st, ws)
+        s = Z.read_state(st)
+        assert np.array_equal(dst.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        sumsq, ovf = O.norm_overflow_f32(ref)
+        assert s.overflow == ovf == (name != "off-grid")
+        assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+
+
+def test_accum_skip_and_resume():
+    """An inf in one micro-batch poisons the accumulated partition: the step is
+    skipped (nothing written, scale halved) and the next one proceeds."""
+    w = _small("accum-skip", 50_000, seed=13)
+    w.inject = {4: 0x7C00}                        # micro-batch 4 = the first of step 2
+    r = H.start_accum(w, 3, fused=True)
+    H.step_accum(r)
+    snap = [t.clone() for t in (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.v32)]
+    H.step_accum(r)
+    s = r.dev.read_state()
+    assert s.skip == 1 and s.overflow == 1 and s.loss_scale == w.scale0 / 2
+    for a, b in zip(snap, (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.v32)):
+        assert a.cpu().numpy().tobytes() == b.cpu().numpy().tobytes()
+    H.step_accum(r)
+    assert r.dev.read_state().step == 2

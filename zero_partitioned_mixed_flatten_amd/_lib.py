@@ -19,7 +19,8 @@ ZERO_F16, ZERO_F32 = 1, 2
 EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "zero_step_state_init",
            "zero_flatten_bucket", "zero_norm_workspace_bytes", "zero_shard_norm_overflow",
            "zero_shard_adam_step", "zero_stream_copy", "zero_flatten_norm_partials", "zero_flatten_norm_bucket",
-           "zero_decide_workspace_bytes", "zero_shard_decide")
+           "zero_decide_workspace_bytes", "zero_shard_decide", "zero_flatten_norm_bucket_f32",
+           "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32")
 NORM_PARTIAL_BYTES = 32
 
 
@@ -81,11 +82,14 @@ def lib():
         L.zero_norm_workspace_bytes.argtypes = [u64]
         L.zero_norm_workspace_bytes.restype = C.c_size_t
         L.zero_shard_norm_overflow.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
+        L.zero_shard_norm_overflow_f32.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
         L.zero_shard_adam_step.argtypes = [vp, vp, vp, vp, vp, u64, vp, vp]
+        L.zero_shard_adam_step_f32.argtypes = [vp, vp, vp, vp, vp, u64, vp, vp]
         L.zero_stream_copy.argtypes = [vp, vp, u64, vp]
         L.zero_flatten_norm_partials.argtypes = [C.POINTER(Segment), u32]
         L.zero_flatten_norm_partials.restype = u64
         L.zero_flatten_norm_bucket.argtypes = [C.POINTER(Segment), u32, vp, u64, i32, vp, u64, vp]
+        L.zero_flatten_norm_bucket_f32.argtypes = [C.POINTER(Segment), u32, vp, u64, i32, vp, u64, vp]
         L.zero_decide_workspace_bytes.argtypes = [u64]
         L.zero_decide_workspace_bytes.restype = C.c_size_t
         L.zero_shard_decide.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
@@ -181,10 +185,23 @@ def zero_shard_norm_overflow(grad16, n: int, hp: HParams, dev_state, workspace, 
                                           ws_bytes, _stream(stream)))
 
 
+def zero_shard_norm_overflow_f32(grad32, n: int, hp: HParams, dev_state, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_shard_norm_overflow_f32",
+           lib().zero_shard_norm_overflow_f32(_ptr(grad32), n, C.byref(hp), _ptr(dev_state), _ptr(workspace),
+                                              ws_bytes, _stream(stream)))
+
+
 def zero_shard_adam_step(p16, p32, m32, v32, grad16, n: int, dev_state, stream=None) -> None:
     _check("zero_shard_adam_step",
            lib().zero_shard_adam_step(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(grad16), n,
                                       _ptr(dev_state), _stream(stream)))
+
+
+def zero_shard_adam_step_f32(p16, p32, m32, v32, grad32, n: int, dev_state, stream=None) -> None:
+    _check("zero_shard_adam_step_f32",
+           lib().zero_shard_adam_step_f32(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(grad32), n,
+                                          _ptr(dev_state), _stream(stream)))
 
 
 def zero_stream_copy(dst, src, nbytes: int, stream=None) -> None:
@@ -206,6 +223,19 @@ def zero_flatten_norm_bucket(segs, nsegs: int, dst, partials, dst_len: Optional[
     _check("zero_flatten_norm_bucket",
            lib().zero_flatten_norm_bucket(segs, nsegs, _ptr(dst), dst_len, int(bool(accumulate)), ptr, cap,
                                           _stream(stream)))
+
+
+def zero_flatten_norm_bucket_f32(segs, nsegs: int, dst, partials, dst_len: Optional[int] = None,
+                                 accumulate: bool = False, partials_offset: int = 0, stream=None) -> None:
+    """Fused fp32 flatten (widen or accumulate) + exact-norm partials of the
+    values stored; partials as for zero_flatten_norm_bucket."""
+    if dst_len is None:
+        dst_len = dst.numel()
+    cap = partials.numel() // NORM_PARTIAL_BYTES - partials_offset
+    ptr = _ptr(partials) + partials_offset * NORM_PARTIAL_BYTES
+    _check("zero_flatten_norm_bucket_f32",
+           lib().zero_flatten_norm_bucket_f32(segs, nsegs, _ptr(dst), dst_len, int(bool(accumulate)), ptr, cap,
+                                              _stream(stream)))
 
 
 def zero_decide_workspace_bytes(count: int) -> int:

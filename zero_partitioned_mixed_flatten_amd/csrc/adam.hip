@@ -12,10 +12,13 @@
 // Memory traffic per parameter: read fp16 g (2) + fp32 p, m, v (12); write
 // fp32 p, m, v (12) + fp16 p (2) = 28 bytes, about 20 flops -- far below the
 // fp32 ridge point, so this is an HBM-streaming kernel: no LDS traffic, no
-// MFMA.  Shape, chosen by measurement on MI355X:
+// MFMA.  The gradient-accumulation form reads an fp32 gradient instead
+// (30 bytes per parameter) and is otherwise the same kernel.
+// Shape, chosen by measurement on MI355X:
 //   * one-shot grid: each thread owns 8 consecutive parameters (one 16-byte
-//     load of g, two each of p, m, v; the matching stores), so the wave front
-//     of resident workgroups sweeps memory once, in order;
+//     load of an fp16 g or two of an fp32 g, two each of p, m, v; the
+//     matching stores), so the wave front of resident workgroups sweeps
+//     memory once, in order;
 //   * plain loads, nontemporal stores (nothing written here is read again
 //     by this kernel);
 //   * at most kBlocksPerCU workgroups resident per CU, enforced by reserving
@@ -51,9 +54,30 @@ __device__ __forceinline__ void update(float gh, float& p, float& m, float& v, c
     v = vn;
 }
 
+// Eight gradient values of one thread, widened to fp32 (exact for fp16).
+__device__ __forceinline__ void load_grad8(const uint16_t* g, uint64_t j, float (&out)[8])
+{
+    const f16x8 h = __builtin_bit_cast(f16x8, reinterpret_cast<const u32x4*>(g)[j]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        out[k] = float(h[k]);
+}
+
+__device__ __forceinline__ void load_grad8(const float* g, uint64_t j, float (&out)[8])
+{
+    const f32x4 a = reinterpret_cast<const f32x4*>(g)[2 * j];
+    const f32x4 b = reinterpret_cast<const f32x4*>(g)[2 * j + 1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+__device__ __forceinline__ float grad_at(const uint16_t* g, uint64_t i) { return float(__builtin_bit_cast(_Float16, g[i])); }
+__device__ __forceinline__ float grad_at(const float* g, uint64_t i) { return g[i]; }
+
+template <typename G>
 __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict__ p16, float* __restrict__ p32,
                                                            float* __restrict__ m32, float* __restrict__ v32,
-                                                           const uint16_t* __restrict__ g16, uint64_t n,
+                                                           const G* __restrict__ grad, uint64_t n,
                                                            const zero_step_state_t* __restrict__ st)
 {
     // The occupancy cap: the launch reserves dynamic LDS that no thread
@@ -80,11 +104,11 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
     const uint64_t nvec = n >> 3;
     const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
     if (j < nvec) {
-        const u32x4* __restrict__ gv = reinterpret_cast<const u32x4*>(g16);
         f32x4* __restrict__ pv = reinterpret_cast<f32x4*>(p32) + 2 * j;
         f32x4* __restrict__ mv = reinterpret_cast<f32x4*>(m32) + 2 * j;
         f32x4* __restrict__ vv = reinterpret_cast<f32x4*>(v32) + 2 * j;
-        const f16x8 g = __builtin_bit_cast(f16x8, gv[j]);
+        float g[8];
+        load_grad8(grad, j, g);
         const f32x4 pa = pv[0], pb = pv[1], ma = mv[0], mb = mv[1], va = vv[0], vb = vv[1];
         float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
         float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
@@ -92,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
         f16x8 h;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            update(float(g[k]), p[k], m[k], v[k], c);
+            update(g[k], p[k], m[k], v[k], c);
             h[k] = _Float16(p[k]);                // round to nearest even
         }
         __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, pv);
@@ -108,12 +132,35 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
     if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
         const uint64_t i = (nvec << 3) + threadIdx.x;
         float p = p32[i], m = m32[i], v = v32[i];
-        update(float(__builtin_bit_cast(_Float16, g16[i])), p, m, v, c);
+        update(grad_at(grad, i), p, m, v, c);
         p32[i] = p;
         m32[i] = m;
         v32[i] = v;
         p16[i] = __builtin_bit_cast(uint16_t, _Float16(p));
     }
+}
+
+template <typename G>
+int adam_step(uint16_t* p16, float* p32, float* m32, float* v32, const G* grad, uint64_t n,
+              const zero_step_state_t* dev_state, void* stream)
+{
+    if (!dev_state || (n && (!p16 || !p32 || !m32 || !v32 || !grad)))
+        return ZERO_EINVAL;
+    if (!is_aligned(dev_state, 8))
+        return ZERO_EALIGN;
+    if (n == 0)
+        return ZERO_OK;
+    if (!is_aligned(p16, 16) || !is_aligned(p32, 16) || !is_aligned(m32, 16) || !is_aligned(v32, 16) ||
+        !is_aligned(grad, 16))
+        return ZERO_EALIGN;
+    const uint64_t nvec = n >> 3;
+    uint64_t grid = (nvec + kBlock - 1) / kBlock;
+    if (grid < 1) grid = 1;
+    if (grid > 0x7fffffffull)
+        return ZERO_ERANGE;
+    hipLaunchKernelGGL(adam_step_kernel<G>, dim3(uint32_t(grid)), dim3(kBlock), lds_reservation(kBlocksPerCU),
+                       (hipStream_t)stream, p16, p32, m32, v32, grad, n, dev_state);
+    return launch_status();
 }
 
 }  // namespace
@@ -124,21 +171,11 @@ using namespace zero;
 extern "C" int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32, const uint16_t* grad16,
                                     uint64_t n, const zero_step_state_t* dev_state, void* stream)
 {
-    if (!dev_state || (n && (!p16 || !p32 || !m32 || !v32 || !grad16)))
-        return ZERO_EINVAL;
-    if (!is_aligned(dev_state, 8))
-        return ZERO_EALIGN;
-    if (n == 0)
-        return ZERO_OK;
-    if (!is_aligned(p16, 16) || !is_aligned(p32, 16) || !is_aligned(m32, 16) || !is_aligned(v32, 16) ||
-        !is_aligned(grad16, 16))
-        return ZERO_EALIGN;
-    const uint64_t nvec = n >> 3;
-    uint64_t grid = (nvec + kBlock - 1) / kBlock;
-    if (grid < 1) grid = 1;
-    if (grid > 0x7fffffffull)
-        return ZERO_ERANGE;
-    hipLaunchKernelGGL(adam_step_kernel, dim3(uint32_t(grid)), dim3(kBlock), lds_reservation(kBlocksPerCU),
-                       (hipStream_t)stream, p16, p32, m32, v32, grad16, n, dev_state);
-    return launch_status();
+    return adam_step(p16, p32, m32, v32, grad16, n, dev_state, stream);
+}
+
+extern "C" int zero_shard_adam_step_f32(uint16_t* p16, float* p32, float* m32, float* v32, const float* grad32,
+                                        uint64_t n, const zero_step_state_t* dev_state, void* stream)
+{
+    return adam_step(p16, p32, m32, v32, grad32, n, dev_state, stream);
 }

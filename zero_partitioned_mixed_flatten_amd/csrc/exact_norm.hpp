@@ -1,20 +1,37 @@
-// exact_norm.hpp -- device helpers for the exact sum of squares of binary16
-// gradients and the step decision, shared by the standalone reduction
-// (norm.hip) and the flatten that computes the sum while it copies
-// (flatten.hip).
+// exact_norm.hpp -- device helpers for the exact sum of squares of the
+// gradient partition and its overflow test, shared by the standalone
+// reductions (norm.hip) and the flattens that compute the sum while they
+// copy (flatten.hip).
 //
-// Every square of a finite binary16 value is an integer multiple of 2^-48
-// below 2^32.  Each thread keeps two binary64 accumulators that stay exact by
-// construction:
-//   hh = x^2 rounded to a multiple of 2^-8   (fma(x, x, C) - C, C = 1.5*2^44)
-//   lo = x^2 - hh, exactly                    (fma(x, x, -hh), |lo| <= 2^-9)
-// With at most kNormMaxPerThread = 2^12 elements per thread, sum(hh) stays a
-// multiple of 2^-8 below 2^44 and sum(lo) a multiple of 2^-48 below 2^3, so
-// neither addition ever rounds.  The two sums become integers of 2^-48 units,
-// split into signed base-2^32 limbs that workgroups and the grid add without
-// carries; one thread propagates the carries at the end and converts the
-// 128-bit total to binary64 with a single round-to-nearest-even.  The result
-// is the exactly rounded sum, independent of grid shape and schedule.
+// The sum is an integer count of 2^-48 units.  Each thread keeps a few
+// binary64 accumulators that cannot round under a per-thread bound of
+// kNormMaxPerThread = 2^12 elements:
+//
+//   binary16 gradients: every square is a multiple of 2^-48 below 2^32.
+//     h = x^2 rounded to a multiple of 2^-8   (fma(x, x, C) - C, C = 1.5*2^44)
+//     l = x^2 - h, exactly                     (fma(x, x, -h), |l| <= 2^-9)
+//     sum(h) stays a multiple of 2^-8 below 2^44, sum(l) a multiple of 2^-48
+//     below 2^3.
+//
+//   binary32 gradients (the accumulation form): |x| < 2^24 on the domain, so
+//   x^2 is exact in binary64 and below 2^48; each square is rounded to the
+//   nearest multiple of 2^-48 (a no-op for sums of binary16 values, which are
+//   multiples of 2^-24).
+//     a = x^2 rounded to a multiple of 2^16   (fma(x, x, C1) - C1, C1 = 1.5*2^68)
+//     r = x^2 - a, exactly, |r| <= 2^15       (fma(x, x, -a))
+//     b = r rounded to a multiple of 2^-16    ((r + C2) - C2, C2 = 1.5*2^36)
+//     c = r - b rounded to a multiple of 2^-48 ((. + C3) - C3, C3 = 24): the
+//         one rounding, to nearest (a square never lies halfway)
+//     sum(a) < 2^60 in steps of 2^16, sum(b) < 2^27 in steps of 2^-16,
+//     sum(c) < 2^-5 in steps of 2^-48: 44 significant bits at most.
+//
+// The sums become signed base-2^32 limbs that threads, workgroups and the
+// grid add without carries.  A workgroup's partial is stored carried (each
+// limb below 2^32), so any number of partials up to 2^30 adds inside int64.
+// At the end one thread carries the total into 128 bits and converts it to
+// binary64 with a single round-to-nearest-even: the exactly rounded sum,
+// independent of grid shape and schedule.  A total of 2^128 units or more
+// (2^80) is reported as an overflow, like an inf/NaN gradient.
 #pragma once
 
 #include <math.h>
@@ -24,7 +41,15 @@
 namespace zero {
 namespace exact {
 
-constexpr double kSplit = 0x1.8p44;           // 1.5 * 2^44: its ulp is 2^-8
+// Flag bits: any of them set means overflow.  Bits 15 and 31 come from the
+// binary16 exponent test; bit 31 from the binary32 domain test; bit 15 also
+// marks a partial whose sum does not fit 128 bits.
+constexpr uint32_t kOverflowBits = 0x80008000u;
+constexpr uint32_t kSumTooLarge = 0x00008000u;
+
+// ---- binary16 gradients ------------------------------------------------------------
+
+constexpr double kSplit16 = 0x1.8p44;          // 1.5 * 2^44: its ulp is 2^-8
 
 // The exponent test adds 0x0400 to each masked exponent field of a word that
 // holds two binary16 values: only an all-ones field carries into bit 15
@@ -36,75 +61,124 @@ __device__ __forceinline__ uint32_t exp_test(u32x4 v)
     return exp_test(v.x) | exp_test(v.y) | exp_test(v.z) | exp_test(v.w);
 }
 
-constexpr uint32_t kOverflowBits = 0x80008000u;
-
-__device__ __forceinline__ void acc_square(_Float16 h, double& ah, double& al)
-{
-    const double x = double(float(h));                       // exact
-    const double hh = __builtin_fma(x, x, kSplit) - kSplit;  // x^2 to a multiple of 2^-8
-    ah += hh;
-    al += __builtin_fma(x, x, -hh);                          // x^2 - hh, exact
-}
-
-__device__ __forceinline__ void acc_vec(u32x4 v, double& ah, double& al, uint32_t& flag)
-{
-    flag |= exp_test(v);
-    const f16x8 h = __builtin_bit_cast(f16x8, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        acc_square(h[k], ah, al);
-}
-
-// One binary16 element given as its bit pattern.
-__device__ __forceinline__ void acc_bits(uint16_t b, double& ah, double& al, uint32_t& flag)
-{
-    flag |= (uint32_t(b) & 0x7C00u) + 0x0400u;
-    acc_square(__builtin_bit_cast(_Float16, b), ah, al);
-}
-
-// Signed base-2^32 limbs of an integer count of 2^-48 units.
+// Signed base-2^32 limbs of an integer count of 2^-48 units:
+// l0 + l1*2^32 + l2*2^64 + l3*2^96.
 struct Limbs {
-    int64_t l0, l1, l2;
+    int64_t l0, l1, l2, l3;
 };
 
-// A thread's exact accumulators as limbs; an inf/NaN seen by the thread
-// (flag) voids its sum, which the overflow flag makes irrelevant anyway.
-__device__ __forceinline__ Limbs to_limbs(double ah, double al, uint32_t flag)
-{
-    if (flag & kOverflowBits) {
-        ah = 0.0;
-        al = 0.0;
-    }
-    const int64_t hu = int64_t(ah * 256.0);       // sum(hh) / 2^-8, < 2^52
-    const int64_t lu = int64_t(al * 0x1p48);      // sum(lo) / 2^-48, |.| < 2^51
-    const int64_t hs = hu << 8;                   // hu * 2^40 = hs * 2^32
-    return Limbs{lu & 0xFFFFFFFFll, (hs & 0xFFFFFFFFll) + (lu >> 32), hs >> 32};
-}
+struct Acc16 {
+    double h = 0.0, l = 0.0;
+    uint32_t flag = 0;
 
-// Carries l0 and l1 into [0, 2^32) (the value is unchanged and >= 0, so l2
-// ends up >= 0).  Stored partials are normalised, so any number of them up
-// to 2^30 can be added in int64.
-__device__ __forceinline__ Limbs normalize(Limbs s)
+    __device__ __forceinline__ void square(_Float16 v)
+    {
+        const double x = double(float(v));                         // exact
+        const double hh = __builtin_fma(x, x, kSplit16) - kSplit16;  // x^2 to a multiple of 2^-8
+        h += hh;
+        l += __builtin_fma(x, x, -hh);                             // x^2 - hh, exact
+    }
+    // Eight binary16 values in one 16-byte vector.
+    __device__ __forceinline__ void vec(u32x4 v)
+    {
+        flag |= exp_test(v);
+        const f16x8 e = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            square(e[k]);
+    }
+    // One element given as its bit pattern.
+    __device__ __forceinline__ void bits(uint16_t b)
+    {
+        flag |= (uint32_t(b) & 0x7C00u) + 0x0400u;
+        square(__builtin_bit_cast(_Float16, b));
+    }
+    // The thread's sum as limbs; an inf/NaN seen by the thread voids it
+    // (the overflow flag makes the sum irrelevant anyway).
+    __device__ __forceinline__ Limbs limbs() const
+    {
+        const bool bad = (flag & kOverflowBits) != 0;
+        const int64_t hu = bad ? 0 : int64_t(h * 256.0);    // sum(h) / 2^-8, < 2^52
+        const int64_t lu = bad ? 0 : int64_t(l * 0x1p48);   // sum(l) / 2^-48, |.| < 2^51
+        const int64_t hs = hu << 8;                         // hu * 2^40 = hs * 2^32
+        return Limbs{lu & 0xFFFFFFFFll, (hs & 0xFFFFFFFFll) + (lu >> 32), hs >> 32, 0};
+    }
+};
+
+// ---- binary32 gradients ------------------------------------------------------------
+
+constexpr double kSplit32Hi = 0x1.8p68;        // ulp 2^16
+constexpr double kSplit32Mid = 0x1.8p36;       // ulp 2^-16
+constexpr double kSplit32Lo = 0x1.8p4;         // ulp 2^-48
+
+// Bit 31 set iff |x| >= 2^24 or x is inf/NaN (0x4B800000 is 2^24).
+__device__ __forceinline__ uint32_t dom_test(uint32_t b) { return ((b & 0x7FFFFFFFu) + 0x34800000u) & 0x80000000u; }
+
+struct Acc32 {
+    double a = 0.0, b = 0.0, c = 0.0;
+    uint32_t flag = 0;
+
+    __device__ __forceinline__ void add(float v)
+    {
+        flag |= dom_test(__builtin_bit_cast(uint32_t, v));
+        const double x = double(v);
+        const double ha = __builtin_fma(x, x, kSplit32Hi) - kSplit32Hi;  // to a multiple of 2^16
+        const double r = __builtin_fma(x, x, -ha);                        // exact, |r| <= 2^15
+        const double hb = (r + kSplit32Mid) - kSplit32Mid;                // to a multiple of 2^-16
+        const double hc = ((r - hb) + kSplit32Lo) - kSplit32Lo;           // nearest multiple of 2^-48
+        a += ha;
+        b += hb;
+        c += hc;
+    }
+    __device__ __forceinline__ void vec(f32x4 v)
+    {
+        add(v.x);
+        add(v.y);
+        add(v.z);
+        add(v.w);
+    }
+    __device__ __forceinline__ Limbs limbs() const
+    {
+        const bool bad = (flag & kOverflowBits) != 0;
+        const int64_t la = bad ? 0 : int64_t(a * 0x1p-16);   // units of 2^16 = 2^64 * 2^-48, < 2^44
+        const int64_t lb = bad ? 0 : int64_t(b * 0x1p16);    // units of 2^-16 = 2^32 * 2^-48, |.| < 2^43
+        const int64_t lc = bad ? 0 : int64_t(c * 0x1p48);    // units of 2^-48, |.| < 2^43
+        return Limbs{lc, lb, la, 0};
+    }
+};
+
+// ---- limbs -------------------------------------------------------------------------
+
+// Carries l0, l1, l2 into [0, 2^32); the value is unchanged and >= 0, so l3
+// ends up >= 0.
+__device__ __forceinline__ Limbs carry(Limbs s)
 {
-    const int64_t c0 = s.l0 >> 32;
+    s.l1 += s.l0 >> 32;
     s.l0 &= 0xFFFFFFFFll;
-    s.l1 += c0;
-    const int64_t c1 = s.l1 >> 32;
+    s.l2 += s.l1 >> 32;
     s.l1 &= 0xFFFFFFFFll;
-    s.l2 += c1;
+    s.l3 += s.l2 >> 32;
+    s.l2 &= 0xFFFFFFFFll;
     return s;
 }
 
-// Carries the limbs into an unsigned 128-bit value (the total is >= 0).
-__device__ __forceinline__ void limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& lo)
+// Adds a stored partial (two carried 64-bit words) as four 32-bit limbs.
+__device__ __forceinline__ void fold_partial(Limbs& s, uint32_t& flag, const NormPartial& p)
 {
-    const int64_t c0 = s.l0 >> 32;
-    const uint64_t w0 = uint64_t(s.l0) & 0xFFFFFFFFull;
-    const int64_t t1 = s.l1 + c0;
-    const uint64_t w1 = uint64_t(t1) & 0xFFFFFFFFull;
-    const int64_t t2 = s.l2 + (t1 >> 32);        // limbs 2 and up, < 2^63
-    lo = w0 | (w1 << 32);
-    hi = uint64_t(t2);
+    s.l0 += int64_t(p.w0 & 0xFFFFFFFFull);
+    s.l1 += int64_t(p.w0 >> 32);
+    s.l2 += int64_t(p.w1 & 0xFFFFFFFFull);
+    s.l3 += int64_t(p.w1 >> 32);
+    flag |= p.flag;
+}
+
+// The total as an unsigned 128-bit value; false if it is 2^128 or more.
+__device__ __forceinline__ bool limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& lo)
+{
+    s = carry(s);
+    lo = uint64_t(s.l0) | (uint64_t(s.l1) << 32);
+    hi = uint64_t(s.l2) | (uint64_t(s.l3) << 32);
+    return (s.l3 >> 32) == 0;
 }
 
 // Sums limbs and ORs flags over a workgroup of BLOCK threads (every thread
@@ -113,13 +187,14 @@ __device__ __forceinline__ void limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& l
 template <int BLOCK>
 __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
 {
-    __shared__ int64_t s0[BLOCK / 64], s1[BLOCK / 64], s2[BLOCK / 64];
+    __shared__ int64_t s0[BLOCK / 64], s1[BLOCK / 64], s2[BLOCK / 64], s3[BLOCK / 64];
     __shared__ uint32_t sf[BLOCK / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         s.l0 += __shfl_xor(s.l0, off, 64);
         s.l1 += __shfl_xor(s.l1, off, 64);
         s.l2 += __shfl_xor(s.l2, off, 64);
+        s.l3 += __shfl_xor(s.l3, off, 64);
         flag |= __shfl_xor(flag, off, 64);
     }
     if (BLOCK > 64) {
@@ -128,6 +203,7 @@ __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
             s0[wave] = s.l0;
             s1[wave] = s.l1;
             s2[wave] = s.l2;
+            s3[wave] = s.l3;
             sf[wave] = flag;
         }
         __syncthreads();
@@ -136,6 +212,7 @@ __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
                 s.l0 += s0[w];
                 s.l1 += s1[w];
                 s.l2 += s2[w];
+                s.l3 += s3[w];
                 flag |= sf[w];
             }
         }
@@ -143,15 +220,16 @@ __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
     }
 }
 
+// A workgroup's partial: the carried sum in two words; a sum of 2^128 units
+// or more is marked as an overflow.
 __device__ __forceinline__ NormPartial make_partial(Limbs s, uint32_t flag)
 {
-    s = normalize(s);
+    s = carry(s);
     NormPartial p;
-    p.l0 = s.l0;
-    p.l1 = s.l1;
-    p.l2 = s.l2;
-    p.flag = flag;
-    p.pad = 0;
+    p.w0 = uint64_t(s.l0) | (uint64_t(s.l1) << 32);
+    p.w1 = uint64_t(s.l2) | (uint64_t(s.l3) << 32);
+    p.flag = flag | ((s.l3 >> 32) != 0 ? kSumTooLarge : 0u);
+    p.pad[0] = p.pad[1] = p.pad[2] = 0;
     return p;
 }
 

@@ -26,6 +26,8 @@
 // It takes four vectors per thread (the workgroup fold is amortised over
 // 8192 elements) and nontemporal stores (nothing reads the partition before
 // the Adam pass, and draining dirty cache lines during it costs more).
+#include <type_traits>
+
 #include "exact_norm.hpp"
 
 namespace zero {
@@ -58,48 +60,56 @@ __host__ __device__ inline uint64_t head_len(uint64_t dst_off, uint64_t count)
     return h < count ? h : count;
 }
 
-// Stores one element; returns the binary16 bits stored (fp16 destinations).
+// The exact accumulator for what a mode stores: binary16 or binary32 values.
 template <int MODE>
-__device__ __forceinline__ uint16_t put_scalar(void* dst, uint64_t i, uint16_t s)
+using AccOf = typename std::conditional<(MODE >= kTo32), exact::Acc32, exact::Acc16>::type;
+
+// Stores one element; in the fused form also accumulates the value stored.
+template <int MODE, bool NORM>
+__device__ __forceinline__ void put_scalar(void* dst, uint64_t i, uint16_t s, AccOf<MODE>& acc)
 {
-    if (MODE == kCopy16) {
+    const _Float16 h = __builtin_bit_cast(_Float16, s);
+    if constexpr (MODE == kCopy16) {
         static_cast<uint16_t*>(dst)[i] = s;
-        return s;
-    } else if (MODE == kAcc16) {
+        if (NORM)
+            acc.bits(s);
+    } else if constexpr (MODE == kAcc16) {
         _Float16* d = static_cast<_Float16*>(dst);
-        const _Float16 r = d[i] + __builtin_bit_cast(_Float16, s);   // correctly rounded binary16 add
+        const _Float16 r = d[i] + h;                     // correctly rounded binary16 add
         d[i] = r;
-        return __builtin_bit_cast(uint16_t, r);
-    } else if (MODE == kTo32) {
-        static_cast<float*>(dst)[i] = float(__builtin_bit_cast(_Float16, s));
-        return 0;
+        if (NORM)
+            acc.bits(__builtin_bit_cast(uint16_t, r));
     } else {
         float* d = static_cast<float*>(dst);
-        d[i] = d[i] + float(__builtin_bit_cast(_Float16, s));
-        return 0;
+        const float r = MODE == kAcc32 ? d[i] + float(h) : float(h);
+        d[i] = r;
+        if (NORM)
+            acc.add(r);
     }
 }
 
-// Stores 8 elements at dst index i (a multiple of 8), nontemporally if NTS;
-// returns the binary16 bits stored (fp16 destinations).
-template <int MODE, bool NTS>
-__device__ __forceinline__ u32x4 put_vector(void* dst, uint64_t i, u32x4 s)
+template <bool NTS, typename V>
+__device__ __forceinline__ void store(V v, V* d)
 {
-    if (MODE == kCopy16) {
+    if (NTS)
+        __builtin_nontemporal_store(v, d);
+    else
+        *d = v;
+}
+
+// Stores 8 elements at dst index i (a multiple of 8), nontemporally in the
+// fused form, which also accumulates the values stored.
+template <int MODE, bool NORM>
+__device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s, AccOf<MODE>& acc)
+{
+    if constexpr (MODE == kCopy16 || MODE == kAcc16) {
         u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i);
-        if (NTS)
-            __builtin_nontemporal_store(s, d);
-        else
-            *d = s;
-        return s;
-    } else if (MODE == kAcc16) {
-        u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i);
-        const u32x4 r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, *d) + __builtin_bit_cast(f16x8, s));
-        if (NTS)
-            __builtin_nontemporal_store(r, d);
-        else
-            *d = r;
-        return r;
+        u32x4 r = s;
+        if (MODE == kAcc16)
+            r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, *d) + __builtin_bit_cast(f16x8, s));
+        store<NORM>(r, d);
+        if (NORM)
+            acc.vec(r);
     } else {
         const f16x8 h = __builtin_bit_cast(f16x8, s);
         f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(dst) + i);
@@ -109,9 +119,12 @@ __device__ __forceinline__ u32x4 put_vector(void* dst, uint64_t i, u32x4 s)
             lo = d[0] + lo;
             hi = d[1] + hi;
         }
-        d[0] = lo;
-        d[1] = hi;
-        return u32x4{0, 0, 0, 0};
+        store<NORM>(lo, d);
+        store<NORM>(hi, d + 1);
+        if (NORM) {
+            acc.vec(lo);
+            acc.vec(hi);
+        }
     }
 }
 
@@ -135,8 +148,7 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     const uint64_t local = b - a.first_block[lo];
     const bool vec_src = is_aligned(src + head, 16);
 
-    double ah = 0.0, al = 0.0;                 // fused form: this thread's exact sum
-    uint32_t flag = 0;
+    AccOf<MODE> acc;                           // fused form: this thread's exact sum
 
     // body: vectors [v0, v1) of this segment
     const uint64_t v0 = local * kVecsPerBlock;
@@ -154,11 +166,8 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
 #pragma unroll
         for (int k = 0; k < kVecsPerThread; ++k) {
             const uint64_t v = v0 + threadIdx.x + uint64_t(k) * kBlock;
-            if (v < v1) {
-                const u32x4 stored = put_vector<MODE, NORM>(dst, dbody + 8 * v, r[k]);
-                if (NORM)
-                    exact::acc_vec(stored, ah, al, flag);
-            }
+            if (v < v1)
+                put_vector<MODE, NORM>(dst, dbody + 8 * v, r[k], acc);
         }
     } else {
         for (uint64_t v = v0 + threadIdx.x; v < v1; v += kBlock) {
@@ -168,9 +177,7 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
             r.y = uint32_t(s[2]) | (uint32_t(s[3]) << 16);
             r.z = uint32_t(s[4]) | (uint32_t(s[5]) << 16);
             r.w = uint32_t(s[6]) | (uint32_t(s[7]) << 16);
-            const u32x4 stored = put_vector<MODE, NORM>(dst, dbody + 8 * v, r);
-            if (NORM)
-                exact::acc_vec(stored, ah, al, flag);
+            put_vector<MODE, NORM>(dst, dbody + 8 * v, r, acc);
         }
     }
 
@@ -178,20 +185,15 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     if (local == 0) {
         const uint64_t t0 = head + 8 * nv;
         const uint64_t t = threadIdx.x;
-        if (t < head) {
-            const uint16_t stored = put_scalar<MODE>(dst, doff + t, src[t]);
-            if (NORM)
-                exact::acc_bits(stored, ah, al, flag);
-        }
-        if (t < cnt - t0) {
-            const uint16_t stored = put_scalar<MODE>(dst, doff + t0 + t, src[t0 + t]);
-            if (NORM)
-                exact::acc_bits(stored, ah, al, flag);
-        }
+        if (t < head)
+            put_scalar<MODE, NORM>(dst, doff + t, src[t], acc);
+        if (t < cnt - t0)
+            put_scalar<MODE, NORM>(dst, doff + t0 + t, src[t0 + t], acc);
     }
 
     if (NORM) {                                 // every thread reaches this point
-        exact::Limbs s = exact::to_limbs(ah, al, flag);
+        uint32_t flag = acc.flag;
+        exact::Limbs s = acc.limbs();
         exact::block_fold<kBlock>(s, flag);
         if (threadIdx.x == 0)
             a.partials[blockIdx.x] = exact::make_partial(s, flag);
@@ -204,8 +206,8 @@ int launch(const FlatArgs& a, uint32_t blocks, int mode, void* dst, hipStream_t 
     switch (mode) {
     case kCopy16: hipLaunchKernelGGL((flatten_kernel<kCopy16, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
     case kAcc16: hipLaunchKernelGGL((flatten_kernel<kAcc16, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    case kTo32: hipLaunchKernelGGL((flatten_kernel<kTo32, false>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    default: hipLaunchKernelGGL((flatten_kernel<kAcc32, false>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    case kTo32: hipLaunchKernelGGL((flatten_kernel<kTo32, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    default: hipLaunchKernelGGL((flatten_kernel<kAcc32, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
     }
     return launch_status();
 }
@@ -305,9 +307,11 @@ extern "C" uint64_t zero_flatten_norm_partials(const zero_segment_t* segs, uint3
     return total;
 }
 
-extern "C" int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nsegs, uint16_t* dst,
-                                        uint64_t dst_len, int accumulate, void* partials,
-                                        uint64_t partials_capacity, void* stream)
+namespace zero {
+namespace {
+
+int flatten_norm(const zero_segment_t* segs, uint32_t nsegs, void* dst, uint64_t dst_len, int mode,
+                 void* partials, uint64_t partials_capacity, void* stream)
 {
     const int rc = validate(segs, nsegs, dst, dst_len);
     if (rc != ZERO_OK)
@@ -319,7 +323,6 @@ extern "C" int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nse
         return ZERO_EALIGN;
     if (need > partials_capacity)
         return ZERO_ERANGE;
-    const int mode = accumulate ? kAcc16 : kCopy16;
     hipStream_t s = (hipStream_t)stream;
     NormPartial* next = static_cast<NormPartial*>(partials);
     return for_each_launch<true>(segs, nsegs, [&](FlatArgs& a, uint32_t blocks) {
@@ -327,4 +330,23 @@ extern "C" int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nse
         next += blocks;
         return launch<true>(a, blocks, mode, dst, s);
     });
+}
+
+}  // namespace
+}  // namespace zero
+
+extern "C" int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nsegs, uint16_t* dst,
+                                        uint64_t dst_len, int accumulate, void* partials,
+                                        uint64_t partials_capacity, void* stream)
+{
+    return flatten_norm(segs, nsegs, dst, dst_len, accumulate ? kAcc16 : kCopy16, partials, partials_capacity,
+                        stream);
+}
+
+extern "C" int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t nsegs, float* dst,
+                                            uint64_t dst_len, int accumulate, void* partials,
+                                            uint64_t partials_capacity, void* stream)
+{
+    return flatten_norm(segs, nsegs, dst, dst_len, accumulate ? kAcc32 : kTo32, partials, partials_capacity,
+                        stream);
 }

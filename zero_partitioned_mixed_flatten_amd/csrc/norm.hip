@@ -1,9 +1,11 @@
-// norm.hip -- exact squared L2 norm + inf/NaN test of a rank's flat fp16
-// gradient partition, and the step decision that follows from them (dynamic
-// loss scaling with skip-step, Micikevicius et al. 2018; global-norm
-// clipping, Pascanu et al. 2013; Adam's bias corrections, Kingma & Ba 2015).
-// The pages fix the gradient as fp16 and the optimizer state as fp32 (ZeRO
-// paper card, "Bottleneck"); the rest of this step is the published methods.
+// norm.hip -- exact squared L2 norm + overflow test of a rank's flat gradient
+// partition, and the step decision that follows from them (dynamic loss
+// scaling with skip-step, Micikevicius et al. 2018; global-norm clipping,
+// Pascanu et al. 2013; Adam's bias corrections, Kingma & Ba 2015).  The pages
+// fix the gradient as fp16 and the optimizer state as fp32 (ZeRO paper card,
+// "Bottleneck"); the fp32 form is the gradient-accumulation partition (the
+// DeepSpeed article leaves gradient accumulation to the library).  The rest
+// of this step is the published methods.
 //
 // The sum is exact (exact_norm.hpp): binary64 accumulators that cannot round
 // under a per-thread element bound, integer limbs across the grid, one
@@ -15,13 +17,14 @@
 //   norm_overflow_kernel  reads the partition itself: 1024-thread workgroups,
 //                         at most one per CU (256), each thread streaming
 //                         16-byte vectors with four nontemporal loads in
-//                         flight, about 8 VALU operations per element;
-//   decide_kernel         folds the per-workgroup partials the fused flatten
+//                         flight; about 8 VALU operations per fp16 element,
+//                         about 12 binary64 operations per fp32 element;
+//   decide_kernel         folds the per-workgroup partials a fused flatten
 //                         (flatten.hip) already computed while copying.
-// In both, every workgroup stores its normalised partial, bumps an
-// agent-scope acq_rel arrival counter once, and the last one to arrive folds
-// all partials, takes the decision in binary64 on one thread, writes it into
-// the step state and re-arms the counter.  No MFMA: 2 bytes per element.
+// In both, every workgroup stores its carried partial, bumps an agent-scope
+// acq_rel arrival counter once, and the last one to arrive folds all
+// partials, takes the decision in binary64 on one thread, writes it into the
+// step state and re-arms the counter.  No MFMA: 2 or 4 bytes per element.
 #include <math.h>
 
 #include "exact_norm.hpp"
@@ -115,31 +118,47 @@ __device__ __forceinline__ void publish_and_decide(Limbs s, uint32_t flag, zero_
 
     // Last workgroup: fold every partial (integer limbs: order is irrelevant).
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    Limbs t{0, 0, 0};
+    Limbs t{0, 0, 0, 0};
     uint32_t tflag = 0;
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock) {
-        const NormPartial p = ws[b];
-        t.l0 += p.l0;
-        t.l1 += p.l1;
-        t.l2 += p.l2;
-        tflag |= p.flag;
-    }
+    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock)
+        exact::fold_partial(t, tflag, ws[b]);
     exact::block_fold<kNormBlock>(t, tflag);
     if (threadIdx.x == 0) {
         uint64_t hi, lo;
-        exact::limbs_to_u128(t, hi, lo);
-        decide(st, d, hi, lo, (tflag & exact::kOverflowBits) != 0);
+        const bool fits = exact::limbs_to_u128(t, hi, lo);
+        decide(st, d, hi, lo, !fits || (tflag & exact::kOverflowBits) != 0);
         st->done_blocks = 0;                                 // re-arm for the next call
     }
 }
 
-__global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const uint16_t* __restrict__ g, uint64_t n,
+// Element type of the partition: 16-byte vectors, the exact accumulator, and
+// a scalar load of one element for the tail.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {
+    static constexpr int kPerVec = 8;
+    using Acc = exact::Acc16;
+    __device__ static void one(Acc& acc, const uint16_t* g, uint64_t i) { acc.bits(g[i]); }
+};
+template <>
+struct Elem<float> {
+    static constexpr int kPerVec = 4;
+    using Acc = exact::Acc32;
+    __device__ static void one(Acc& acc, const float* g, uint64_t i) { acc.add(g[i]); }
+};
+
+__device__ __forceinline__ void acc_vec(exact::Acc16& acc, u32x4 v) { acc.vec(v); }
+__device__ __forceinline__ void acc_vec(exact::Acc32& acc, u32x4 v) { acc.vec(__builtin_bit_cast(f32x4, v)); }
+
+template <typename T>
+__global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const T* __restrict__ g, uint64_t n,
                                                                    zero_step_state_t* __restrict__ st,
                                                                    NormPartial* __restrict__ ws, DecideArgs d)
 {
-    double ah = 0.0, al = 0.0;
-    uint32_t flag = 0;
-    const uint64_t nvec = n >> 3;
+    using E = Elem<T>;
+    typename E::Acc acc;
+    const uint64_t nvec = n / E::kPerVec;
     const u32x4* __restrict__ gv = reinterpret_cast<const u32x4*>(g);
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
     uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
@@ -148,36 +167,32 @@ __global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const uint16_
         const u32x4 b = __builtin_nontemporal_load(gv + j + stride);
         const u32x4 c = __builtin_nontemporal_load(gv + j + 2 * stride);
         const u32x4 e = __builtin_nontemporal_load(gv + j + 3 * stride);
-        exact::acc_vec(a, ah, al, flag);
-        exact::acc_vec(b, ah, al, flag);
-        exact::acc_vec(c, ah, al, flag);
-        exact::acc_vec(e, ah, al, flag);
+        acc_vec(acc, a);
+        acc_vec(acc, b);
+        acc_vec(acc, c);
+        acc_vec(acc, e);
     }
     for (; j < nvec; j += stride)
-        exact::acc_vec(__builtin_nontemporal_load(gv + j), ah, al, flag);
-    if (blockIdx.x == 0 && threadIdx.x < (n & 7))          // the last n % 8 elements
-        exact::acc_bits(g[(nvec << 3) + threadIdx.x], ah, al, flag);
+        acc_vec(acc, __builtin_nontemporal_load(gv + j));
+    if (blockIdx.x == 0 && threadIdx.x < n - nvec * E::kPerVec)   // the last n % kPerVec elements
+        E::one(acc, g, nvec * E::kPerVec + threadIdx.x);
 
-    Limbs s = exact::to_limbs(ah, al, flag);
+    uint32_t flag = acc.flag;
+    Limbs s = acc.limbs();
     exact::block_fold<kNormBlock>(s, flag);
     publish_and_decide(s, flag, st, ws, d);
 }
 
-// Folds `count` normalised partials (from the fused flatten) and decides.
+// Folds `count` carried partials (from a fused flatten) and decides.
 __global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* __restrict__ in, uint64_t count,
                                                             zero_step_state_t* __restrict__ st,
                                                             NormPartial* __restrict__ ws, DecideArgs d)
 {
-    Limbs s{0, 0, 0};
+    Limbs s{0, 0, 0, 0};
     uint32_t flag = 0;
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-    for (uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x; i < count; i += stride) {
-        const NormPartial p = in[i];
-        s.l0 += p.l0;
-        s.l1 += p.l1;
-        s.l2 += p.l2;
-        flag |= p.flag;
-    }
+    for (uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x; i < count; i += stride)
+        exact::fold_partial(s, flag, in[i]);
     exact::block_fold<kNormBlock>(s, flag);
     publish_and_decide(s, flag, st, ws, d);
 }
@@ -210,6 +225,26 @@ DecideArgs decide_args(const zero_hparams_t* hp)
     return d;
 }
 
+template <typename T>
+int norm_overflow(const T* grad, uint64_t n, const zero_hparams_t* hp, zero_step_state_t* dev_state,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!hp || !dev_state || !workspace || (n && !grad))
+        return ZERO_EINVAL;
+    if (!hparams_ok(hp))
+        return ZERO_EINVAL;
+    if ((n && !is_aligned(grad, 16)) || !is_aligned(dev_state, 8) || !is_aligned(workspace, 16))
+        return ZERO_EALIGN;
+    if (n > kNormMaxElems)
+        return ZERO_ERANGE;
+    const uint64_t grid = norm_grid(n);
+    if (workspace_bytes < grid * sizeof(NormPartial))
+        return ZERO_ERANGE;
+    hipLaunchKernelGGL(norm_overflow_kernel<T>, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
+                       grad, n, dev_state, static_cast<NormPartial*>(workspace), decide_args(hp));
+    return launch_status();
+}
+
 }  // namespace
 }  // namespace zero
 
@@ -219,20 +254,14 @@ extern "C" int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, cons
                                         zero_step_state_t* dev_state, void* workspace,
                                         size_t workspace_bytes, void* stream)
 {
-    if (!hp || !dev_state || !workspace || (n && !grad16))
-        return ZERO_EINVAL;
-    if (!hparams_ok(hp))
-        return ZERO_EINVAL;
-    if ((n && !is_aligned(grad16, 16)) || !is_aligned(dev_state, 8) || !is_aligned(workspace, 16))
-        return ZERO_EALIGN;
-    if (n > kNormMaxElems)
-        return ZERO_ERANGE;
-    const uint64_t grid = norm_grid(n);
-    if (workspace_bytes < grid * sizeof(NormPartial))
-        return ZERO_ERANGE;
-    hipLaunchKernelGGL(norm_overflow_kernel, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
-                       grad16, n, dev_state, static_cast<NormPartial*>(workspace), decide_args(hp));
-    return launch_status();
+    return norm_overflow(grad16, n, hp, dev_state, workspace, workspace_bytes, stream);
+}
+
+extern "C" int zero_shard_norm_overflow_f32(const float* grad32, uint64_t n, const zero_hparams_t* hp,
+                                            zero_step_state_t* dev_state, void* workspace,
+                                            size_t workspace_bytes, void* stream)
+{
+    return norm_overflow(grad32, n, hp, dev_state, workspace, workspace_bytes, stream);
 }
 
 extern "C" int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,

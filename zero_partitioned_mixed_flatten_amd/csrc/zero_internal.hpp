@@ -41,21 +41,22 @@ uint32_t lds_reservation(int blocks_per_cu);
 constexpr int kNormBlock = 1024;                            // 16 wavefronts, one workgroup per CU
 constexpr uint64_t kNormMaxBlocks = 256;                    // one per CU of an MI355X
 constexpr uint64_t kNormMaxPerThread = uint64_t(1) << 12;   // keeps the binary64 partial sums exact
-constexpr uint64_t kNormMaxElems = uint64_t(1) << 40;       // keeps the limb sums inside int64
+constexpr uint64_t kNormMaxElems = uint64_t(1) << 40;       // keeps the grid within 2^18 workgroups
 
-// One workgroup's exact partial: the sum of squares in 2^-48 units as signed
-// base-2^32 limbs (l0 + l1*2^32 + l2*2^64), plus the OR-ed exponent test bits.
+// One workgroup's exact partial: the sum of squares in 2^-48 units as a
+// carried 128-bit value (w0 low word, w1 high word), plus the OR-ed overflow
+// test bits.
 struct alignas(16) NormPartial {
-    int64_t l0, l1, l2;
+    uint64_t w0, w1;
     uint32_t flag;
-    uint32_t pad;
+    uint32_t pad[3];
 };
 static_assert(sizeof(NormPartial) == 32, "partial layout");
 
 uint64_t norm_grid(uint64_t n);
 
 // Partials folded by the decide-only pass (the fused flatten writes one per
-// workgroup); stored partials are normalised, so 2^30 of them fit in int64 sums.
+// workgroup); stored partials are carried, so 2^30 of them fit in int64 sums.
 constexpr uint64_t kMaxPartials = uint64_t(1) << 30;
 uint64_t decide_grid(uint64_t count);
 

@@ -1,6 +1,6 @@
-"""ShardStep: the three C-ABI calls of one ZeRO shard step, wired to torch-owned
-device buffers.  Allocation and call order only; the arithmetic is in the HIP
-kernels behind the C ABI.
+"""ShardStep and AccumStep: the C-ABI calls of one ZeRO shard step, wired to
+torch-owned device buffers.  Allocation and call order only; the arithmetic is
+in the HIP kernels behind the C ABI.
 
 One data-parallel rank owns n parameters of the flat model state (ZeRO paper
 card, "Method").  For them it keeps, index-aligned and contiguous: the fp16
@@ -100,6 +100,104 @@ class ShardStep:
             self.decide(hp)
         else:
             self.flatten()
+            self.norm_overflow(hp)
+        self.adam()
+
+    def read_state(self) -> Z.StepState:
+        return Z.read_state(self.state)
+
+
+class AccumStep:
+    """The gradient-accumulation form of the step: K micro-batches of per-layer
+    fp16 gradients are added into an fp32 partition, then the fp32 reduction
+    and the update reading the fp32 gradient run (the DeepSpeed article leaves
+    gradient accumulation to the library).  fused=True computes the
+    exact-norm partials in the last micro-batch's flatten and folds them with
+    the decide-only pass; fused=False runs the standalone fp32 reduction.
+    Both take bit-identical decisions."""
+
+    def __init__(self, n: int, device="cuda", fused: bool = True):
+        import torch
+        self.n = int(n)
+        alloc = max(1, self.n)
+        self.device = torch.device(device)
+        self.p16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
+        self.grad32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.p32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.m32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.v32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
+        ws = Z.zero_norm_workspace_bytes(self.n)
+        self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
+        self.fused = bool(fused)
+        self.partials = None
+        self.decide_ws = None
+        self.partial_count = 0
+        self.partial_offsets: List[int] = []
+
+    def init_state(self, initial_scale: float) -> None:
+        Z.zero_step_state_init(self.state, initial_scale)
+
+    def plan(self, sources: Sequence, segments: Sequence[Tuple[int, int, int, int]], bucket_elems: int = 0):
+        """One micro-batch's segment plan: (kept sources, [(segs, nsegs), ...])."""
+        sources = list(sources)
+        segs, nsegs = Z.make_segments([(sources[t].data_ptr(), so, do, c) for t, so, do, c in segments])
+        if bucket_elems and bucket_elems < self.n:
+            buckets = [Z.zero_bucket_segments(segs, nsegs, b, min(self.n, b + bucket_elems))
+                       for b in range(0, self.n, bucket_elems)]
+        else:
+            buckets = [(segs, nsegs)]
+        if self.fused:
+            self._size_partials(buckets)
+        return sources, buckets
+
+    def _size_partials(self, buckets) -> None:
+        import torch
+        offsets, total = [], 0
+        for segs, nsegs in buckets:
+            offsets.append(total)
+            total += Z.zero_flatten_norm_partials(segs, nsegs)
+        self.partial_offsets, self.partial_count = offsets, total
+        need = max(1, total) * Z.NORM_PARTIAL_BYTES
+        if self.partials is None or self.partials.numel() < need:
+            self.partials = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws = max(16, Z.zero_decide_workspace_bytes(total))
+        if self.decide_ws is None or self.decide_ws.numel() < ws:
+            self.decide_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
+
+    def accumulate(self, buckets, first: bool) -> None:
+        """Widen (first micro-batch) or add one micro-batch into grad32."""
+        for segs, nsegs in buckets:
+            Z.zero_flatten_bucket(segs, nsegs, self.grad32, self.n, Z.ZERO_F32, not first)
+
+    def accumulate_norm(self, buckets, first: bool) -> None:
+        """The last micro-batch's flatten, computing the exact-norm partials of
+        the finished fp32 partition (requires fused=True)."""
+        if self.partial_count != sum(Z.zero_flatten_norm_partials(s, k) for s, k in buckets):
+            self._size_partials(buckets)
+        for (segs, nsegs), off in zip(buckets, self.partial_offsets):
+            Z.zero_flatten_norm_bucket_f32(segs, nsegs, self.grad32, self.partials, self.n, not first, off)
+
+    def norm_overflow(self, hp: Z.HParams) -> None:
+        Z.zero_shard_norm_overflow_f32(self.grad32, self.n, hp, self.state, self.workspace)
+
+    def decide(self, hp: Z.HParams) -> None:
+        Z.zero_shard_decide(self.partials, self.partial_count, hp, self.state, self.decide_ws)
+
+    def adam(self) -> None:
+        Z.zero_shard_adam_step_f32(self.p16, self.p32, self.m32, self.v32, self.grad32, self.n, self.state)
+
+    def step(self, micro_batches, hp: Z.HParams) -> None:
+        """micro_batches: bucket plans from plan(), in accumulation order."""
+        k = len(micro_batches)
+        for i, buckets in enumerate(micro_batches):
+            if self.fused and i == k - 1:
+                self.accumulate_norm(buckets, first=(i == 0))
+            else:
+                self.accumulate(buckets, first=(i == 0))
+        if self.fused:
+            self.decide(hp)
+        else:
             self.norm_overflow(hp)
         self.adam()
 
