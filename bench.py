@@ -47,7 +47,7 @@ NORM_BYTES = 2           # read fp16 g
 FLATTEN_BYTES = 4        # read fp16 source, write fp16 partition
 WIDEN_BYTES = 6          # read fp16 source, write fp32 partition
 ACCUM_BYTES = 10         # read fp16 source and fp32 partition, write fp32 partition
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "adam_step_gpt2_shard_pmc.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "step_kernels_gpt2_shard_pmc.json")
 ADAM_SOURCE = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc", "adam.hip")
 
 
@@ -60,9 +60,10 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(n):
-    """HBM bytes per Adam launch from the committed counter summary, or None
-    when it is missing, for another shard size, or for another kernel source."""
+def measured_traffic(path, n):
+    """HBM bytes per launch of the path's Adam kernel from the committed counter
+    summary, or None when it is missing, for another shard size, for another
+    path, or for another kernel source."""
     try:
         with open(PMC_SUMMARY) as f:
             s = json.load(f)
@@ -70,7 +71,7 @@ def measured_traffic(n):
         return None
     if s.get("adam_source_sha256_16") != source_hash(ADAM_SOURCE) or s.get("n") != n:
         return None
-    return s.get("hbm_bytes_per_launch")
+    return s.get("hbm_bytes_per_launch", {}).get(path)
 
 
 def cpu_baseline(w, p32, grads_host, budget_s, micro=0):
@@ -272,7 +273,7 @@ def main():
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
         cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds, K if accum else 0)
 
-    traffic = measured_traffic(n) if args.path == "fused" else None
+    traffic = measured_traffic(args.path if (not accum or K == 4) else None, n)
     if accum:
         step_bpp = WIDEN_BYTES + ACCUM_BYTES * (K - 1) + ADAM32_BYTES
     else:
