@@ -35,7 +35,12 @@
  *     into an fp32 partition (zero_flatten_bucket with ZERO_F32, or the
  *     fused zero_flatten_norm_bucket_f32 for the last micro-batch), and the
  *     *_f32 reduction and update read that fp32 gradient (30 bytes per
- *     parameter in the update).
+ *     parameter in the update);
+ *   - host step (ZeRO-Offload, in the DeepSpeed article: ZeRO-2 plus CPU
+ *     memory): the fp32 master parameters, momentum and variance live in host
+ *     memory and the CPU steps them (zero_host_*, zero_offload_step), with
+ *     the fp16 gradient partition copied down and the fp16 parameters copied
+ *     back up.
  *
  * Conventions for every entry point:
  *   - pointers named dev_* or documented as device memory are HIP device
@@ -65,7 +70,9 @@ extern "C" {
 #define ZERO_EINVAL  (-1)   /* null pointer, bad dtype/stage/hyperparameter */
 #define ZERO_EALIGN  (-2)   /* a buffer is not aligned as required */
 #define ZERO_ERANGE  (-3)   /* a size or segment is out of the allowed range */
-#define ZERO_EHIP    (-4)   /* the HIP runtime refused a launch */
+#define ZERO_EHIP    (-4)   /* the HIP runtime refused a launch or a copy */
+#define ZERO_ENOTSUP (-5)   /* the host CPU lacks an instruction set the host step needs */
+#define ZERO_ENOMEM  (-6)   /* out of host memory */
 
 /* Human-readable text for a status code (static storage; never NULL).
  * For ZERO_EHIP the text of the last HIP error seen by this thread. */
@@ -312,6 +319,75 @@ int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32,
 int zero_shard_adam_step_f32(uint16_t* p16, float* p32, float* m32, float* v32,
                              const float* grad32, uint64_t n,
                              const zero_step_state_t* dev_state, void* stream);
+
+/* ---- host step (ZeRO-Offload form) ----------------------------------- */
+
+/* A host context: a pool of worker threads (and, once zero_offload_step has
+ * run, the HIP events it pipelines with).  Calls that share a context must
+ * not overlap; different contexts are independent.  Every zero_host_* call
+ * runs on the calling thread plus the pool and returns when it is done. */
+typedef struct zero_host_ctx zero_host_ctx_t;
+
+/* Create a context with `threads` workers in all (the calling thread counts
+ * as one; <= 0: every CPU this process may run on).
+ * Errors: ZERO_EINVAL (out NULL), ZERO_ENOTSUP (the CPU lacks AVX-512 F, BW,
+ *         VL, DQ, F16C or FMA), ZERO_ERANGE (threads > 1024), ZERO_ENOMEM. */
+int zero_host_create(int threads, zero_host_ctx_t** out);
+
+/* Stop the workers and free the context (NULL is allowed). */
+void zero_host_destroy(zero_host_ctx_t* ctx);
+
+/* Number of workers of a context (0 for NULL). */
+int zero_host_threads(const zero_host_ctx_t* ctx);
+
+/* zero_step_state_init for a step state in HOST memory (no device work).
+ * Errors: ZERO_EINVAL (NULL, initial_scale not finite and > 0). */
+int zero_host_state_init(zero_step_state_t* state, double initial_scale);
+
+/* zero_shard_norm_overflow on the CPU: over the n binary16 values at grad16
+ * (host memory, any alignment), the same overflow test and the same exact
+ * sum of squares, then the same decision into the HOST step state, bit for
+ * bit (one source for the decision; the sum is exact on both).
+ * Errors: ZERO_EINVAL (NULL, hyperparameters out of range as for
+ *         zero_shard_norm_overflow). */
+int zero_host_norm_overflow(zero_host_ctx_t* ctx, const uint16_t* grad16, uint64_t n, const zero_hparams_t* hp,
+                            zero_step_state_t* state);
+
+/* zero_shard_adam_step on the CPU: the same element update, each operation
+ * one binary32 round-to-nearest-even operation in the same order, the fp16
+ * copy rounded to nearest even -- bit-identical to the device kernel.  All
+ * arrays are host memory of n elements; any alignment works, and when p32,
+ * m32, v32 are 64-byte aligned and p16 32-byte aligned at the same index the
+ * stores bypass the caches.  Nothing is written when state->skip is set.
+ * Errors: ZERO_EINVAL (NULL). */
+int zero_host_adam_step(zero_host_ctx_t* ctx, uint16_t* p16, float* p32, float* m32, float* v32,
+                        const uint16_t* grad16, uint64_t n, const zero_step_state_t* state);
+
+/* The whole offloaded step for a partition whose fp16 gradient and fp16
+ * parameters live on the device and whose fp32 master parameters, momentum
+ * and variance live in host memory:
+ *   1. copy dev_grad16 -> host_grad16 in chunks of chunk_elems on `stream`,
+ *      reducing each chunk on the CPU as soon as it has landed;
+ *   2. decide into the host state (as zero_host_norm_overflow);
+ *   3. unless the step is skipped, update each chunk on the CPU (as
+ *      zero_host_adam_step, fp16 parameters into host_p16) and enqueue its
+ *      copy host_p16 -> dev_p16 on `stream` right away.
+ * The call returns once every update is done; the last parameter copies may
+ * still be in flight on `stream` (later work on `stream` sees them; the host
+ * must not write host_p16 before they complete).  host_grad16 and host_p16
+ * should be pinned host memory (hipHostMalloc) for the copies to overlap.
+ * dev_grad16, dev_p16: device, n elements; everything else host memory.
+ * Errors: ZERO_EINVAL (NULL, hyperparameters out of range), ZERO_EALIGN
+ *         (chunk_elems 0 or not a multiple of 64), ZERO_ERANGE (more than
+ *         4096 chunks), ZERO_EHIP (a copy, event or synchronisation failed). */
+int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad16, uint16_t* dev_p16, uint16_t* host_grad16,
+                      uint16_t* host_p16, float* p32, float* m32, float* v32, uint64_t n,
+                      const zero_hparams_t* hp, zero_step_state_t* state, uint64_t chunk_elems, void* stream);
+
+/* A streaming copy of `bytes` host bytes (dst, src 64-byte aligned, bytes a
+ * multiple of 64) on the context's workers: the host memory bandwidth
+ * reference next to the host step.  Errors: ZERO_EINVAL, ZERO_EALIGN. */
+int zero_host_stream_copy(zero_host_ctx_t* ctx, void* dst, const void* src, uint64_t bytes);
 
 /* ---- measurement reference ------------------------------------------ */
 

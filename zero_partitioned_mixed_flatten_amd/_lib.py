@@ -12,7 +12,7 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzero_mi355x.so")
 
-ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP = 0, -1, -2, -3, -4
+ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP, ZERO_ENOTSUP, ZERO_ENOMEM = 0, -1, -2, -3, -4, -5, -6
 ZERO_F16, ZERO_F32 = 1, 2
 
 # Every function the public header declares (checked against the header by a test).
@@ -20,7 +20,9 @@ EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "ze
            "zero_flatten_bucket", "zero_norm_workspace_bytes", "zero_shard_norm_overflow",
            "zero_shard_adam_step", "zero_stream_copy", "zero_flatten_norm_partials", "zero_flatten_norm_bucket",
            "zero_decide_workspace_bytes", "zero_shard_decide", "zero_flatten_norm_bucket_f32",
-           "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32")
+           "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32", "zero_host_create", "zero_host_destroy",
+           "zero_host_threads", "zero_host_state_init", "zero_host_norm_overflow", "zero_host_adam_step",
+           "zero_offload_step", "zero_host_stream_copy")
 NORM_PARTIAL_BYTES = 32
 
 
@@ -93,9 +95,19 @@ def lib():
         L.zero_decide_workspace_bytes.argtypes = [u64]
         L.zero_decide_workspace_bytes.restype = C.c_size_t
         L.zero_shard_decide.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
+        L.zero_host_create.argtypes = [i32, C.POINTER(vp)]
+        L.zero_host_destroy.argtypes = [vp]
+        L.zero_host_destroy.restype = None
+        L.zero_host_threads.argtypes = [vp]
+        L.zero_host_state_init.argtypes = [C.POINTER(StepState), C.c_double]
+        L.zero_host_norm_overflow.argtypes = [vp, vp, u64, C.POINTER(HParams), C.POINTER(StepState)]
+        L.zero_host_adam_step.argtypes = [vp, vp, vp, vp, vp, vp, u64, C.POINTER(StepState)]
+        L.zero_offload_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u64, C.POINTER(HParams),
+                                        C.POINTER(StepState), u64, vp]
+        L.zero_host_stream_copy.argtypes = [vp, vp, vp, u64]
         for name in EXPORTS:
             if name not in ("zero_status_string", "zero_norm_workspace_bytes", "zero_flatten_norm_partials",
-                            "zero_decide_workspace_bytes"):
+                            "zero_decide_workspace_bytes", "zero_host_destroy"):
                 getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -253,3 +265,63 @@ def read_state(dev_state) -> StepState:
     """Copy a device step state to the host (synchronises the current stream)."""
     raw = dev_state.detach().to("cpu").numpy().tobytes()
     return StepState.from_buffer_copy(raw)
+
+
+# ---- host step (ZeRO-Offload form) -------------------------------------------------
+
+def _hptr(a) -> int:
+    """Host address of a contiguous numpy array or CPU torch tensor (or an int)."""
+    if a is None:
+        return 0
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "ctypes"):                         # numpy
+        if not a.flags.c_contiguous:
+            raise ValueError("expected a contiguous array")
+        return a.ctypes.data
+    if a.is_cuda:
+        raise ValueError("expected host memory")
+    if not a.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return a.data_ptr()
+
+
+def zero_host_create(threads: int = 0) -> int:
+    out = C.c_void_p()
+    _check("zero_host_create", lib().zero_host_create(threads, C.byref(out)))
+    return out.value
+
+
+def zero_host_destroy(ctx: int) -> None:
+    lib().zero_host_destroy(ctx)
+
+
+def zero_host_threads(ctx: int) -> int:
+    return int(lib().zero_host_threads(ctx))
+
+
+def zero_host_state_init(state: StepState, initial_scale: float) -> None:
+    _check("zero_host_state_init", lib().zero_host_state_init(C.byref(state), initial_scale))
+
+
+def zero_host_norm_overflow(ctx: int, grad16, n: int, hp: HParams, state: StepState) -> None:
+    _check("zero_host_norm_overflow",
+           lib().zero_host_norm_overflow(ctx, _hptr(grad16), n, C.byref(hp), C.byref(state)))
+
+
+def zero_host_adam_step(ctx: int, p16, p32, m32, v32, grad16, n: int, state: StepState) -> None:
+    _check("zero_host_adam_step",
+           lib().zero_host_adam_step(ctx, _hptr(p16), _hptr(p32), _hptr(m32), _hptr(v32), _hptr(grad16), n,
+                                     C.byref(state)))
+
+
+def zero_offload_step(ctx: int, dev_grad16, dev_p16, host_grad16, host_p16, p32, m32, v32, n: int,
+                      hp: HParams, state: StepState, chunk_elems: int, stream=None) -> None:
+    _check("zero_offload_step",
+           lib().zero_offload_step(ctx, _ptr(dev_grad16), _ptr(dev_p16), _hptr(host_grad16), _hptr(host_p16),
+                                   _hptr(p32), _hptr(m32), _hptr(v32), n, C.byref(hp), C.byref(state),
+                                   chunk_elems, _stream(stream)))
+
+
+def zero_host_stream_copy(ctx: int, dst, src, nbytes: int) -> None:
+    _check("zero_host_stream_copy", lib().zero_host_stream_copy(ctx, _hptr(dst), _hptr(src), nbytes))

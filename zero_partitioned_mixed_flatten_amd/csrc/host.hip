@@ -107,6 +107,8 @@ extern "C" const char* zero_status_string(int code)
     case ZERO_EALIGN: return "buffer not aligned as required";
     case ZERO_ERANGE: return "size or segment out of range";
     case ZERO_EHIP: return hipGetErrorString(g_last_hip_error);
+    case ZERO_ENOTSUP: return "the host CPU lacks AVX-512 (F, BW, VL, DQ), F16C or FMA";
+    case ZERO_ENOMEM: return "out of host memory";
     default: return "unknown status code";
     }
 }

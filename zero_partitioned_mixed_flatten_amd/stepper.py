@@ -205,6 +205,80 @@ class AccumStep:
         return Z.read_state(self.state)
 
 
+class HostContext:
+    """Owns a zero_host_ctx_t (the host step's worker pool)."""
+
+    def __init__(self, threads: int = 0):
+        self.ptr = Z.zero_host_create(threads)
+
+    @property
+    def threads(self) -> int:
+        return Z.zero_host_threads(self.ptr)
+
+    def close(self) -> None:
+        if self.ptr:
+            Z.zero_host_destroy(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        self.close()
+
+
+class OffloadStep:
+    """The ZeRO-Offload form of the step (the DeepSpeed article: ZeRO-2 plus CPU
+    memory).  On the device: the per-layer fp16 gradients, the flat fp16
+    gradient partition the flatten packs them into, and the fp16 parameters.
+    In host memory: the fp32 master parameters, momentum and variance, the
+    pinned staging copies of the fp16 gradient and parameters, and the step
+    state.  A step is the device flatten, then zero_offload_step."""
+
+    def __init__(self, n: int, threads: int = 0, chunk_elems: int = 1 << 22, device="cuda"):
+        import torch
+        self.n = int(n)
+        alloc = max(1, self.n)
+        self.device = torch.device(device)
+        self.ctx = HostContext(threads)
+        self.chunk = int(chunk_elems)
+        self.grad16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
+        self.p16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
+        self.host_grad16 = torch.zeros(alloc, dtype=torch.float16, pin_memory=True)
+        self.host_p16 = torch.zeros(alloc, dtype=torch.float16, pin_memory=True)
+        self.p32 = torch.zeros(alloc, dtype=torch.float32)
+        self.m32 = torch.zeros(alloc, dtype=torch.float32)
+        self.v32 = torch.zeros(alloc, dtype=torch.float32)
+        self.state = Z.StepState()
+        self.buckets: List[Tuple[object, int]] = []
+        self._sources: Sequence = ()
+
+    def init_state(self, initial_scale: float) -> None:
+        Z.zero_host_state_init(self.state, initial_scale)
+
+    def set_segments(self, sources: Sequence, segments: Sequence[Tuple[int, int, int, int]],
+                     bucket_elems: int = 0) -> None:
+        self._sources = list(sources)
+        segs, nsegs = Z.make_segments([(self._sources[t].data_ptr(), so, do, c) for t, so, do, c in segments])
+        if bucket_elems and bucket_elems < self.n:
+            self.buckets = [Z.zero_bucket_segments(segs, nsegs, b, min(self.n, b + bucket_elems))
+                            for b in range(0, self.n, bucket_elems)]
+        else:
+            self.buckets = [(segs, nsegs)]
+
+    def flatten(self) -> None:
+        for segs, nsegs in self.buckets:
+            Z.zero_flatten_bucket(segs, nsegs, self.grad16, self.n, Z.ZERO_F16, False)
+
+    def offload(self, hp: Z.HParams) -> None:
+        Z.zero_offload_step(self.ctx.ptr, self.grad16, self.p16, self.host_grad16, self.host_p16, self.p32,
+                            self.m32, self.v32, self.n, hp, self.state, self.chunk)
+
+    def step(self, hp: Z.HParams) -> None:
+        self.flatten()
+        self.offload(hp)
+
+    def read_state(self) -> Z.StepState:
+        return Z.StepState.from_buffer_copy(bytes(self.state))
+
+
 def hparams(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=1.0,
             backoff=0.5, growth=2.0, min_scale=1.0, growth_interval=20) -> Z.HParams:
     return Z.HParams(lr, beta1, beta2, eps, weight_decay, max_grad_norm, backoff, growth, min_scale,
