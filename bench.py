@@ -119,19 +119,20 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
     import torch
     import zero_partitioned_mixed_flatten_amd as Z
     n = w.n
-    dev = Z.OffloadStep(n, threads=args.threads, chunk_elems=args.chunk)
+    dev = Z.OffloadStep(n, threads=args.threads, chunk_elems=args.chunk,
+                        device_decides=(args.offload_decide == "device"))
     dev.p32.copy_(torch.from_numpy(p32))
     dev.p16.copy_(dev.p32.half().cuda())
     dev.init_state(w.scale0)
     plans = []
     for d in dev_sets:
-        dev.set_segments(d, w.layout.segments, w.bucket_elems)
+        dev.set_segments(d, w.layout.segments, w.bucket_elems)     # same partial plan for every set
         plans.append(dev.buckets)
     threads = dev.ctx.threads
 
     def one_step(k):
         dev.buckets = plans[k % len(plans)]
-        dev.flatten()
+        dev.flatten(hp)
         dev.offload(hp)
 
     log(f"offload: {threads} host threads, chunk {args.chunk}; warmup {args.warmup} steps")
@@ -156,7 +157,7 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
         return (time.perf_counter() - t) / reps
 
     # the host phases alone, on the same host arrays (the state is not advanced: a copy decides)
-    probe = Z.StepState.from_buffer_copy(bytes(dev.state))
+    probe = dev.read_state()
     norm_s = timed(lambda: Z.zero_host_norm_overflow(dev.ctx.ptr, dev.host_grad16, n, hp, probe))
     adam_s = timed(lambda: Z.zero_host_adam_step(dev.ctx.ptr, dev.host_p16, dev.p32, dev.m32, dev.v32,
                                                  dev.host_grad16, n, probe))
@@ -193,7 +194,7 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
         "data": "synthetic",
         "config": {"workload": f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard, offloaded step",
                    "params": n, "segments": len(w.layout.segments), "path": "offload", "host_threads": threads,
-                   "chunk_elems": args.chunk,
+                   "chunk_elems": args.chunk, "decides": args.offload_decide,
                    "state": "device: fp16 p, g; host: fp32 p, m, v (+ pinned fp16 g, p staging)"},
         "roofline": {"bound": "host-dram", "kernel": "host_adam_step", "achieved": achieved,
                      "peak": host_copy_gbps, "unit": "GB/s", "frac": achieved / host_copy_gbps, "traffic": None,
@@ -215,8 +216,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2", choices=["tiny", "gpt2", "100b", "1t"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate", "accum32", "offload"])
-    ap.add_argument("--threads", type=int, default=0, help="host workers for --path offload (0: all CPUs)")
-    ap.add_argument("--chunk", type=int, default=1 << 23, help="elements per transfer chunk for --path offload")
+    ap.add_argument("--threads", type=int, default=None,
+                    help="host workers for --path offload (default: all CPUs but one)")
+    ap.add_argument("--chunk", type=int, default=1 << 24, help="elements per transfer chunk for --path offload")
+    ap.add_argument("--offload-decide", default="device", choices=["device", "host"],
+                    help="--path offload: who reduces and decides (bit-identical either way)")
     ap.add_argument("--micro-batches", type=int, default=4,
                     help="micro-batches per optimizer step for --path accum32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -365,24 +365,33 @@ int zero_host_adam_step(zero_host_ctx_t* ctx, uint16_t* p16, float* p32, float* 
 
 /* The whole offloaded step for a partition whose fp16 gradient and fp16
  * parameters live on the device and whose fp32 master parameters, momentum
- * and variance live in host memory:
- *   1. copy dev_grad16 -> host_grad16 in chunks of chunk_elems on `stream`,
- *      reducing each chunk on the CPU as soon as it has landed;
- *   2. decide into the host state (as zero_host_norm_overflow);
- *   3. unless the step is skipped, update each chunk on the CPU (as
- *      zero_host_adam_step, fp16 parameters into host_p16) and enqueue its
- *      copy host_p16 -> dev_p16 on `stream` right away.
- * The call returns once every update is done; the last parameter copies may
- * still be in flight on `stream` (later work on `stream` sees them; the host
- * must not write host_p16 before they complete).  host_grad16 and host_p16
+ * and variance live in host memory.  Two ways to decide:
+ *   dev_state NULL: the CPU decides.  dev_grad16 is copied to host_grad16
+ *     in chunks of chunk_elems on `stream`, each chunk reduced on the CPU as
+ *     soon as it has landed; then the decision into the host `state` (as
+ *     zero_host_norm_overflow; `hp` is required);
+ *   dev_state given: the device has already decided on `stream`
+ *     (zero_shard_decide over zero_flatten_norm_bucket partials, or
+ *     zero_shard_norm_overflow), bit-identically to the CPU's decision.  The
+ *     128-byte device state is copied into `state` first, then the gradient
+ *     chunks, and the CPU updates each chunk as soon as it has landed
+ *     (`hp` is not used and may be NULL).
+ * Unless the step is skipped, each chunk is updated on the CPU (as
+ * zero_host_adam_step, fp16 parameters into host_p16) and its copy
+ * host_p16 -> dev_p16 is enqueued on `stream` right away.  The call returns
+ * once every update is done; copies may still be in flight on `stream`
+ * (later work on `stream` sees them; the host must not touch host_grad16
+ * or host_p16 before they complete).  host_grad16, host_p16 and `state`
  * should be pinned host memory (hipHostMalloc) for the copies to overlap.
- * dev_grad16, dev_p16: device, n elements; everything else host memory.
+ * dev_grad16, dev_p16, dev_state: device; the other arrays host memory.
  * Errors: ZERO_EINVAL (NULL, hyperparameters out of range), ZERO_EALIGN
- *         (chunk_elems 0 or not a multiple of 64), ZERO_ERANGE (more than
- *         4096 chunks), ZERO_EHIP (a copy, event or synchronisation failed). */
+ *         (chunk_elems 0 or not a multiple of 64, dev_state not 8-byte
+ *         aligned), ZERO_ERANGE (more than 4096 chunks), ZERO_EHIP (a copy,
+ *         event or synchronisation failed). */
 int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad16, uint16_t* dev_p16, uint16_t* host_grad16,
                       uint16_t* host_p16, float* p32, float* m32, float* v32, uint64_t n,
-                      const zero_hparams_t* hp, zero_step_state_t* state, uint64_t chunk_elems, void* stream);
+                      const zero_hparams_t* hp, zero_step_state_t* state, const zero_step_state_t* dev_state,
+                      uint64_t chunk_elems, void* stream);
 
 /* A streaming copy of `bytes` host bytes (dst, src 64-byte aligned, bytes a
  * multiple of 64) on the context's workers: the host memory bandwidth

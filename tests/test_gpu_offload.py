@@ -30,11 +30,11 @@ def _small(name, n, seed, max_seg=None):
 
 
 class Offload:
-    def __init__(self, w, threads=0, chunk=1 << 20):
+    def __init__(self, w, threads=0, chunk=1 << 20, device_decides=True):
         self.w = w
         n = w.n
         p32 = shardgen.master_params(w)
-        self.dev = Z.OffloadStep(n, threads=threads, chunk_elems=chunk)
+        self.dev = Z.OffloadStep(n, threads=threads, chunk_elems=chunk, device_decides=device_decides)
         if n:
             self.dev.p32.copy_(torch.from_numpy(p32))
             self.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
@@ -53,7 +53,8 @@ class Offload:
         srcs = shardgen.source_tensors(w.layout, gpart)
         del gpart
         dsrcs = [H.to_dev16(s) for s in srcs]
-        H.log(f"offload {w.name} n={w.n} step {self.k} chunk={self.dev.chunk} threads={self.dev.ctx.threads}")
+        H.log(f"offload {w.name} n={w.n} step {self.k} chunk={self.dev.chunk} threads={self.dev.ctx.threads} "
+              f"device_decides={self.dev.device_decides}")
         self.dev.set_segments(dsrcs, w.layout.segments, w.bucket_elems)
         self.dev.step(self.hp_d)
         grad = np.empty(w.n, np.uint16)
@@ -71,38 +72,43 @@ class Offload:
         del dsrcs
 
 
+@pytest.mark.parametrize("device_decides", [True, False])
 @pytest.mark.parametrize("chunk", [256, 4096, 1 << 20])       # 256: 4096 chunks, the most allowed
-def test_offload_tiny_full_parity(chunk):
-    r = Offload(shardgen.workload("tiny"), chunk=chunk)
+def test_offload_tiny_full_parity(chunk, device_decides):
+    r = Offload(shardgen.workload("tiny"), chunk=chunk, device_decides=device_decides)
     for _ in range(3):
         r.step()
 
 
+@pytest.mark.parametrize("device_decides", [True, False])
 @pytest.mark.parametrize("n", [1, 7, 65_536 * 3 + 5])
-def test_offload_ragged(n):
-    r = Offload(_small(f"offload{n}", n, seed=300 + n), threads=3, chunk=64)
+def test_offload_ragged(n, device_decides):
+    r = Offload(_small(f"offload{n}", n, seed=300 + n), threads=3, chunk=64, device_decides=device_decides)
     for _ in range(2):
         r.step()
 
 
-def test_offload_empty():
+@pytest.mark.parametrize("device_decides", [True, False])
+def test_offload_empty(device_decides):
     w = _small("offload-empty", 0, seed=0)
     w.layout = shardgen.ShardLayout("empty", 0, 1, 0, 0, 0, [], [], [])
-    r = Offload(w)
+    r = Offload(w, device_decides=device_decides)
     r.step()
     assert r.dev.read_state().step == 1
 
 
-def test_offload_gpt2_shard_full_size():
-    r = Offload(shardgen.workload("gpt2"), chunk=1 << 23)
+@pytest.mark.parametrize("device_decides", [True, False])
+def test_offload_gpt2_shard_full_size(device_decides):
+    r = Offload(shardgen.workload("gpt2"), chunk=1 << 23, device_decides=device_decides)
     for _ in range(2):
         r.step()
 
 
-def test_offload_skip_leaves_everything():
+@pytest.mark.parametrize("device_decides", [True, False])
+def test_offload_skip_leaves_everything(device_decides):
     w = _small("offload-skip", 100_000, seed=17)
     w.inject = {2: 0x7E00}
-    r = Offload(w, chunk=8192)
+    r = Offload(w, chunk=8192, device_decides=device_decides)
     r.step()
     snap = [t.clone() for t in (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.v32)]
     r.step()
@@ -118,7 +124,7 @@ def test_offload_matches_device_step():
     """The offloaded step and the all-device step take the same decision and
     produce the same parameters, bit for bit."""
     w = _small("offload-vs-device", 500_003, seed=23, max_seg=90_000)
-    off = Offload(w, chunk=1 << 16)
+    off = Offload(w, chunk=1 << 16, device_decides=False)       # the CPU decides here
     dev = H.start(w, fused=True)
     for _ in range(2):
         off.step()

@@ -229,8 +229,13 @@ def test_host_validation(Z, ctxs):
     assert L.zero_host_stream_copy(ctxs[1].ptr, 65, 128, 64) == E.ZERO_EALIGN
     # the offload step rejects a bad chunk before touching the device
     f = 1 << 20
-    assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 100, C.byref(hp), C.byref(st), 100,
+    sp = C.addressof(st)
+    assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 100, C.byref(hp), sp, None, 100,
                                None) == E.ZERO_EALIGN
-    assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 1 << 30, C.byref(hp), C.byref(st), 64,
+    assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 1 << 30, C.byref(hp), sp, None, 64,
                                None) == E.ZERO_ERANGE
+    assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 100, None, sp, None, 64,
+                               None) == E.ZERO_EINVAL             # no hp and no device decision
+    assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 100, None, sp, f + 4, 64,
+                               None) == E.ZERO_EALIGN             # misaligned device state
     assert Z.zero_status_string(E.ZERO_ENOTSUP) and Z.zero_status_string(E.ZERO_ENOMEM)

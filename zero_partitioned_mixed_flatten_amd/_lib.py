@@ -102,8 +102,7 @@ def lib():
         L.zero_host_state_init.argtypes = [C.POINTER(StepState), C.c_double]
         L.zero_host_norm_overflow.argtypes = [vp, vp, u64, C.POINTER(HParams), C.POINTER(StepState)]
         L.zero_host_adam_step.argtypes = [vp, vp, vp, vp, vp, vp, u64, C.POINTER(StepState)]
-        L.zero_offload_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u64, C.POINTER(HParams),
-                                        C.POINTER(StepState), u64, vp]
+        L.zero_offload_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u64, C.POINTER(HParams), vp, vp, u64, vp]
         L.zero_host_stream_copy.argtypes = [vp, vp, vp, u64]
         for name in EXPORTS:
             if name not in ("zero_status_string", "zero_norm_workspace_bytes", "zero_flatten_norm_partials",
@@ -316,11 +315,16 @@ def zero_host_adam_step(ctx: int, p16, p32, m32, v32, grad16, n: int, state: Ste
 
 
 def zero_offload_step(ctx: int, dev_grad16, dev_p16, host_grad16, host_p16, p32, m32, v32, n: int,
-                      hp: HParams, state: StepState, chunk_elems: int, stream=None) -> None:
+                      hp: Optional[HParams], state, dev_state=None, chunk_elems: int = 1 << 22, stream=None) -> None:
+    """state: a host StepState or the host address of one (e.g. a pinned
+    128-byte tensor); dev_state: a device state the device has already
+    decided on this stream, or None to decide on the CPU."""
+    st = C.addressof(state) if isinstance(state, StepState) else _hptr(state)
     _check("zero_offload_step",
            lib().zero_offload_step(ctx, _ptr(dev_grad16), _ptr(dev_p16), _hptr(host_grad16), _hptr(host_p16),
-                                   _hptr(p32), _hptr(m32), _hptr(v32), n, C.byref(hp), C.byref(state),
-                                   chunk_elems, _stream(stream)))
+                                   _hptr(p32), _hptr(m32), _hptr(v32), n, C.byref(hp) if hp is not None else None,
+                                   st, _ptr(dev_state) if dev_state is not None else None, chunk_elems,
+                                   _stream(stream)))
 
 
 def zero_host_stream_copy(ctx: int, dst, src, nbytes: int) -> None:

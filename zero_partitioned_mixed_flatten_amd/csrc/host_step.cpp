@@ -22,8 +22,11 @@
 //     squares before it is flushed into a 128-bit integer per worker, so the
 //     sum is exact and the decision bit-identical to the GPU's;
 //   * the offload step pipelines: the D2H copy of the gradient is split into
-//     chunks, each followed by an event, and the workers reduce chunk i while
-//     chunk i+1 is in flight; after the decision, the H2D copy of each chunk
+//     chunks, each followed by an event.  When the device has already taken
+//     the decision (its exact reduction is bit-identical to this one), the
+//     128-byte state comes down first and the workers update chunk i while
+//     chunk i+1 is in flight; otherwise they reduce chunk i while chunk i+1 is
+//     in flight, decide, then update.  Either way the H2D copy of each chunk
 //     of fp16 parameters is enqueued as soon as the workers have updated it.
 #include <hip/hip_runtime.h>
 #include <immintrin.h>
@@ -440,13 +443,15 @@ extern "C" int zero_host_stream_copy(zero_host_ctx_t* ctx, void* dst, const void
 extern "C" int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad16, uint16_t* dev_p16,
                                  uint16_t* host_grad16, uint16_t* host_p16, float* p32, float* m32, float* v32,
                                  uint64_t n, const zero_hparams_t* hp, zero_step_state_t* state,
-                                 uint64_t chunk_elems, void* stream)
+                                 const zero_step_state_t* dev_state, uint64_t chunk_elems, void* stream)
 {
-    if (!ctx || !hp || !state ||
+    if (!ctx || !state || (!dev_state && !hp) ||
         (n && (!dev_grad16 || !dev_p16 || !host_grad16 || !host_p16 || !p32 || !m32 || !v32)))
         return ZERO_EINVAL;
-    if (!hparams_ok(hp))
+    if (!dev_state && !hparams_ok(hp))
         return ZERO_EINVAL;
+    if (dev_state && !is_aligned(dev_state, 8))
+        return ZERO_EALIGN;
     if (chunk_elems == 0 || (chunk_elems & 63))
         return ZERO_EALIGN;
     hipStream_t s = (hipStream_t)stream;
@@ -462,39 +467,57 @@ extern "C" int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad1
         ctx->events.clear();
         ctx->event_device = dev;
     }
-    while (ctx->events.size() < chunks) {
+    while (ctx->events.size() < chunks + 1) {
         hipEvent_t e;
         const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
         if (err != hipSuccess)
             return hip_fail(err);
         ctx->events.push_back(e);
     }
-    // gradient down, chunk by chunk; reduce each chunk as it lands
-    for (uint64_t c = 0; c < chunks; ++c) {
-        const uint64_t lo = c * chunk_elems, cnt = (n - lo < chunk_elems ? n - lo : chunk_elems);
-        hipError_t err = hipMemcpyAsync(host_grad16 + lo, dev_grad16 + lo, cnt * 2, hipMemcpyDeviceToHost, s);
+    hipEvent_t* ev = ctx->events.data();         // ev[0]: the state, ev[1 + c]: gradient chunk c
+    auto lo_of = [&](uint64_t c) { return c * chunk_elems; };
+    auto hi_of = [&](uint64_t c) { return n - c * chunk_elems < chunk_elems ? n : (c + 1) * chunk_elems; };
+    // the decision first (when the device has made it), then the gradient, chunk by chunk
+    if (dev_state) {
+        hipError_t err = hipMemcpyAsync(state, dev_state, sizeof *state, hipMemcpyDeviceToHost, s);
         if (err == hipSuccess)
-            err = hipEventRecord(ctx->events[c], s);
+            err = hipEventRecord(ev[0], s);
         if (err != hipSuccess)
             return hip_fail(err);
     }
-    norm_reset(ctx);
     for (uint64_t c = 0; c < chunks; ++c) {
-        const hipError_t err = hipEventSynchronize(ctx->events[c]);
+        hipError_t err = hipMemcpyAsync(host_grad16 + lo_of(c), dev_grad16 + lo_of(c), (hi_of(c) - lo_of(c)) * 2,
+                                        hipMemcpyDeviceToHost, s);
+        if (err == hipSuccess)
+            err = hipEventRecord(ev[1 + c], s);
         if (err != hipSuccess)
             return hip_fail(err);
-        const uint64_t lo = c * chunk_elems, hi = (n - lo < chunk_elems ? n : lo + chunk_elems);
-        norm_chunk(ctx, host_grad16, lo, hi);
     }
-    norm_decide(ctx, hp, state);
+    if (dev_state) {
+        const hipError_t err = hipEventSynchronize(ev[0]);
+        if (err != hipSuccess)
+            return hip_fail(err);
+    } else {                                     // reduce each chunk as it lands, then decide here
+        norm_reset(ctx);
+        for (uint64_t c = 0; c < chunks; ++c) {
+            const hipError_t err = hipEventSynchronize(ev[1 + c]);
+            if (err != hipSuccess)
+                return hip_fail(err);
+            norm_chunk(ctx, host_grad16, lo_of(c), hi_of(c));
+        }
+        norm_decide(ctx, hp, state);
+    }
     if (state->skip)
         return ZERO_OK;                          // nothing changes, nothing goes back up
-    // update chunk by chunk; send each chunk of fp16 parameters up as soon as it is ready
+    // update chunk by chunk as the gradient lands; send each chunk of fp16 parameters up when ready
     const Coef co = coef_of(state);
     for (uint64_t c = 0; c < chunks; ++c) {
-        const uint64_t lo = c * chunk_elems, hi = (n - lo < chunk_elems ? n : lo + chunk_elems);
-        adam_chunk(ctx, host_p16, p32, m32, v32, host_grad16, lo, hi, co);
-        const hipError_t err = hipMemcpyAsync(dev_p16 + lo, host_p16 + lo, (hi - lo) * 2, hipMemcpyHostToDevice, s);
+        hipError_t err = dev_state ? hipEventSynchronize(ev[1 + c]) : hipSuccess;
+        if (err != hipSuccess)
+            return hip_fail(err);
+        adam_chunk(ctx, host_p16, p32, m32, v32, host_grad16, lo_of(c), hi_of(c), co);
+        err = hipMemcpyAsync(dev_p16 + lo_of(c), host_p16 + lo_of(c), (hi_of(c) - lo_of(c)) * 2,
+                             hipMemcpyHostToDevice, s);
         if (err != hipSuccess)
             return hip_fail(err);
     }
