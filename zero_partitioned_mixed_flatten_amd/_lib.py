@@ -123,6 +123,17 @@ def _stream(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _need(fn: str, t, nbytes: int) -> None:
+    """Raise on the host, before any device work, if tensor `t` holds fewer than
+    nbytes bytes (the C ABI takes raw pointers and cannot check this itself).
+    Raw integer addresses are passed through unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    have = t.numel() * t.element_size()
+    if nbytes > have:
+        raise ValueError(f"{fn}: buffer holds {have} bytes, the call would touch {nbytes}")
+
+
 def _ptr(t, dtype=None) -> int:
     import torch
     if t is None:
@@ -178,6 +189,7 @@ def zero_norm_workspace_bytes(n: int) -> int:
 # ---- device entry points (asynchronous on the current torch stream) ---------------
 
 def zero_step_state_init(dev_state, initial_scale: float, stream=None) -> None:
+    _need("zero_step_state_init", dev_state, STATE_BYTES)
     _check("zero_step_state_init", lib().zero_step_state_init(_ptr(dev_state), initial_scale, _stream(stream)))
 
 
@@ -185,11 +197,14 @@ def zero_flatten_bucket(segs, nsegs: int, dst, dst_len: Optional[int] = None, ds
                         accumulate: bool = False, stream=None) -> None:
     if dst_len is None:
         dst_len = dst.numel()
+    _need("zero_flatten_bucket", dst, dst_len * (4 if dst_dtype == ZERO_F32 else 2))
     _check("zero_flatten_bucket", lib().zero_flatten_bucket(segs, nsegs, _ptr(dst), dst_len, dst_dtype,
                                                             int(bool(accumulate)), _stream(stream)))
 
 
 def zero_shard_norm_overflow(grad16, n: int, hp: HParams, dev_state, workspace, stream=None) -> None:
+    _need("zero_shard_norm_overflow", grad16, 2 * n)
+    _need("zero_shard_norm_overflow", dev_state, STATE_BYTES)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_shard_norm_overflow",
            lib().zero_shard_norm_overflow(_ptr(grad16), n, C.byref(hp), _ptr(dev_state), _ptr(workspace),
@@ -197,6 +212,8 @@ def zero_shard_norm_overflow(grad16, n: int, hp: HParams, dev_state, workspace, 
 
 
 def zero_shard_norm_overflow_f32(grad32, n: int, hp: HParams, dev_state, workspace, stream=None) -> None:
+    _need("zero_shard_norm_overflow_f32", grad32, 4 * n)
+    _need("zero_shard_norm_overflow_f32", dev_state, STATE_BYTES)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_shard_norm_overflow_f32",
            lib().zero_shard_norm_overflow_f32(_ptr(grad32), n, C.byref(hp), _ptr(dev_state), _ptr(workspace),
@@ -204,18 +221,26 @@ def zero_shard_norm_overflow_f32(grad32, n: int, hp: HParams, dev_state, workspa
 
 
 def zero_shard_adam_step(p16, p32, m32, v32, grad16, n: int, dev_state, stream=None) -> None:
+    for t, b in ((p16, 2), (p32, 4), (m32, 4), (v32, 4), (grad16, 2)):
+        _need("zero_shard_adam_step", t, b * n)
+    _need("zero_shard_adam_step", dev_state, STATE_BYTES)
     _check("zero_shard_adam_step",
            lib().zero_shard_adam_step(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(grad16), n,
                                       _ptr(dev_state), _stream(stream)))
 
 
 def zero_shard_adam_step_f32(p16, p32, m32, v32, grad32, n: int, dev_state, stream=None) -> None:
+    for t, b in ((p16, 2), (p32, 4), (m32, 4), (v32, 4), (grad32, 4)):
+        _need("zero_shard_adam_step_f32", t, b * n)
+    _need("zero_shard_adam_step_f32", dev_state, STATE_BYTES)
     _check("zero_shard_adam_step_f32",
            lib().zero_shard_adam_step_f32(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(grad32), n,
                                           _ptr(dev_state), _stream(stream)))
 
 
 def zero_stream_copy(dst, src, nbytes: int, stream=None) -> None:
+    _need("zero_stream_copy", dst, nbytes)
+    _need("zero_stream_copy", src, nbytes)
     _check("zero_stream_copy", lib().zero_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
 
 
@@ -229,6 +254,7 @@ def zero_flatten_norm_bucket(segs, nsegs: int, dst, partials, dst_len: Optional[
     `partials_offset` of the uint8 device buffer `partials`."""
     if dst_len is None:
         dst_len = dst.numel()
+    _need("zero_flatten_norm_bucket", dst, 2 * dst_len)
     cap = partials.numel() // NORM_PARTIAL_BYTES - partials_offset
     ptr = _ptr(partials) + partials_offset * NORM_PARTIAL_BYTES
     _check("zero_flatten_norm_bucket",
@@ -242,6 +268,7 @@ def zero_flatten_norm_bucket_f32(segs, nsegs: int, dst, partials, dst_len: Optio
     values stored; partials as for zero_flatten_norm_bucket."""
     if dst_len is None:
         dst_len = dst.numel()
+    _need("zero_flatten_norm_bucket_f32", dst, 4 * dst_len)
     cap = partials.numel() // NORM_PARTIAL_BYTES - partials_offset
     ptr = _ptr(partials) + partials_offset * NORM_PARTIAL_BYTES
     _check("zero_flatten_norm_bucket_f32",
@@ -254,6 +281,8 @@ def zero_decide_workspace_bytes(count: int) -> int:
 
 
 def zero_shard_decide(partials, count: int, hp: HParams, dev_state, workspace, stream=None) -> None:
+    _need("zero_shard_decide", partials, NORM_PARTIAL_BYTES * count)
+    _need("zero_shard_decide", dev_state, STATE_BYTES)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_shard_decide",
            lib().zero_shard_decide(_ptr(partials), count, C.byref(hp), _ptr(dev_state), _ptr(workspace), ws_bytes,
@@ -303,12 +332,23 @@ def zero_host_state_init(state: StepState, initial_scale: float) -> None:
     _check("zero_host_state_init", lib().zero_host_state_init(C.byref(state), initial_scale))
 
 
+def _hneed(fn: str, a, nbytes: int) -> None:
+    if a is None or isinstance(a, int):
+        return
+    have = a.nbytes if hasattr(a, "nbytes") and not hasattr(a, "element_size") else a.numel() * a.element_size()
+    if nbytes > have:
+        raise ValueError(f"{fn}: buffer holds {have} bytes, the call would touch {nbytes}")
+
+
 def zero_host_norm_overflow(ctx: int, grad16, n: int, hp: HParams, state: StepState) -> None:
+    _hneed("zero_host_norm_overflow", grad16, 2 * n)
     _check("zero_host_norm_overflow",
            lib().zero_host_norm_overflow(ctx, _hptr(grad16), n, C.byref(hp), C.byref(state)))
 
 
 def zero_host_adam_step(ctx: int, p16, p32, m32, v32, grad16, n: int, state: StepState) -> None:
+    for a, b in ((p16, 2), (p32, 4), (m32, 4), (v32, 4), (grad16, 2)):
+        _hneed("zero_host_adam_step", a, b * n)
     _check("zero_host_adam_step",
            lib().zero_host_adam_step(ctx, _hptr(p16), _hptr(p32), _hptr(m32), _hptr(v32), _hptr(grad16), n,
                                      C.byref(state)))
@@ -319,6 +359,11 @@ def zero_offload_step(ctx: int, dev_grad16, dev_p16, host_grad16, host_p16, p32,
     """state: a host StepState or the host address of one (e.g. a pinned
     128-byte tensor); dev_state: a device state the device has already
     decided on this stream, or None to decide on the CPU."""
+    for t, b in ((dev_grad16, 2), (dev_p16, 2), (host_grad16, 2), (host_p16, 2), (p32, 4), (m32, 4), (v32, 4)):
+        _need("zero_offload_step", t, b * n)
+    _need("zero_offload_step", dev_state, STATE_BYTES)
+    if not isinstance(state, StepState):
+        _need("zero_offload_step", state, STATE_BYTES)
     st = C.addressof(state) if isinstance(state, StepState) else _hptr(state)
     _check("zero_offload_step",
            lib().zero_offload_step(ctx, _ptr(dev_grad16), _ptr(dev_p16), _hptr(host_grad16), _hptr(host_p16),
@@ -328,4 +373,6 @@ def zero_offload_step(ctx: int, dev_grad16, dev_p16, host_grad16, host_p16, p32,
 
 
 def zero_host_stream_copy(ctx: int, dst, src, nbytes: int) -> None:
+    _hneed("zero_host_stream_copy", dst, nbytes)
+    _hneed("zero_host_stream_copy", src, nbytes)
     _check("zero_host_stream_copy", lib().zero_host_stream_copy(ctx, _hptr(dst), _hptr(src), nbytes))

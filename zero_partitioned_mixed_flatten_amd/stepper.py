@@ -15,6 +15,16 @@ from typing import List, Optional, Sequence, Tuple
 from . import _lib as Z
 
 
+def _segments(sources, segments, fn):
+    """(tensor index, src_off, dst_off, count) -> ctypes segments, with every
+    source range checked against its tensor on the host."""
+    for t, so, do, c in segments:
+        if so < 0 or c < 0 or so + c > sources[t].numel():
+            raise ValueError(f"{fn}: segment ({t}, {so}, {do}, {c}) reads past its source tensor "
+                             f"of {sources[t].numel()} elements")
+    return Z.make_segments([(sources[t].data_ptr(), so, do, c) for t, so, do, c in segments])
+
+
 class ShardStep:
     """fused=False: flatten, then the standalone exact-norm pass over the
     partition.  fused=True: the flatten computes the exact-norm partials while
@@ -52,8 +62,7 @@ class ShardStep:
         dst_off, count).  With bucket_elems > 0 the partition is flattened in
         windows of that many destination elements, one call each."""
         self._sources = list(sources)                  # keep the tensors alive
-        segs, nsegs = Z.make_segments([(self._sources[t].data_ptr(), so, do, c)
-                                       for t, so, do, c in segments])
+        segs, nsegs = _segments(self._sources, segments, "ShardStep.set_segments")
         if bucket_elems and bucket_elems < self.n:
             self.buckets = [Z.zero_bucket_segments(segs, nsegs, b, min(self.n, b + bucket_elems))
                             for b in range(0, self.n, bucket_elems)]
@@ -141,7 +150,7 @@ class AccumStep:
     def plan(self, sources: Sequence, segments: Sequence[Tuple[int, int, int, int]], bucket_elems: int = 0):
         """One micro-batch's segment plan: (kept sources, [(segs, nsegs), ...])."""
         sources = list(sources)
-        segs, nsegs = Z.make_segments([(sources[t].data_ptr(), so, do, c) for t, so, do, c in segments])
+        segs, nsegs = _segments(sources, segments, "AccumStep.plan")
         if bucket_elems and bucket_elems < self.n:
             buckets = [Z.zero_bucket_segments(segs, nsegs, b, min(self.n, b + bucket_elems))
                        for b in range(0, self.n, bucket_elems)]
@@ -279,7 +288,7 @@ class OffloadStep:
                      bucket_elems: int = 0) -> None:
         import torch
         self._sources = list(sources)
-        segs, nsegs = Z.make_segments([(self._sources[t].data_ptr(), so, do, c) for t, so, do, c in segments])
+        segs, nsegs = _segments(self._sources, segments, "OffloadStep.set_segments")
         if bucket_elems and bucket_elems < self.n:
             self.buckets = [Z.zero_bucket_segments(segs, nsegs, b, min(self.n, b + bucket_elems))
                             for b in range(0, self.n, bucket_elems)]
