@@ -35,6 +35,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #if defined(__FAST_MATH__)
@@ -427,4 +428,128 @@ void oracle_step(const oracle_hparams_t* hp, oracle_state_t* st,
     oracle_norm_overflow(grad16, n, &sumsq, &overflow);
     oracle_decide(st, hp, sumsq, overflow);
     oracle_adam_update(st, p16, p32, m32, v32, grad16, n);
+}
+
+/* ------------------------------------------------------------------ */
+/* 1-bit Adam, compression stage (DeepSpeed article: 1-bit Adam cuts    */
+/* communication up to 5x with Adam-like convergence; the algorithm is  */
+/* Tang et al. 2021, "1-bit Adam", Algorithm 1).  After a warm-up of    */
+/* ordinary Adam steps the variance v is frozen; each step then         */
+/*   m  = beta1*m + (1-beta1)*g                (local momentum)          */
+/*   x  = m + ew;  cw = C[x];  ew = x - cw     (worker error feedback)   */
+/*   u  = avg_workers(cw) + es; m = C[u]; es = u - m   (server side)     */
+/*   p  = p - lr*(m/(sqrt(v)+eps) + wd*p)      (frozen v; decoupled wd)  */
+/* With one data-parallel rank the rank is its own server and the       */
+/* average is its own cw.                                               */
+/*                                                                      */
+/* The compressor C[x] = s * sgn(x), one bit per element plus one       */
+/* scale per vector: sgn(x) = +1 for x >= 0 (zeros included) and -1     */
+/* otherwise; s = ||x||_2 / sqrt(d) in fp32, so that C[x] keeps the L2  */
+/* norm of x.  The sum of squares is exact: with E the binary exponent  */
+/* of max|x|, each square is rounded to the nearest multiple of         */
+/* q = 2^(2E-80) (no square is ever halfway: x^2/q is an integer times  */
+/* an even power of two), the integers are summed exactly (each is      */
+/* below 2^82), and S = sum*q is rounded once to binary64; then         */
+/* s = fp32(sqrt(S / d)).  A square below q/2 (below 2^-81 of the       */
+/* largest) contributes nothing.                                        */
+/* ------------------------------------------------------------------ */
+/* units_out (optional): the exact integer sum (low, high 64 bits) and the
+ * window exponent 2E-80, so that S = units * 2^(2E-80) before rounding. */
+float oracle_onebit_scale_units(const float* x, uint64_t n, double* sumsq_out, uint64_t* units_out, int* qexp_out)
+{
+    double big = 0.0;
+    for (uint64_t i = 0; i < n; ++i)
+        if (fabs((double)x[i]) > big)
+            big = fabs((double)x[i]);
+    if (big == 0.0) {
+        if (sumsq_out)
+            *sumsq_out = 0.0;
+        if (units_out)
+            units_out[0] = units_out[1] = 0;
+        if (qexp_out)
+            *qexp_out = 0;
+        return 0.0f;
+    }
+    int ex;
+    frexp(big, &ex);                                    /* big = f * 2^ex, f in [0.5, 1) */
+    const int E = ex - 1;                               /* 2^E <= max|x| < 2^(E+1) */
+    unsigned __int128 units = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        double sq = (double)x[i] * (double)x[i];        /* exact: 48 bits */
+        double y = ldexp(sq, 80 - 2 * E);               /* exact power-of-two scaling, < 2^82 */
+        units += (unsigned __int128)nearbyint(y);
+    }
+    double S = ldexp((double)units, 2 * E - 80);        /* one rounding */
+    if (sumsq_out)
+        *sumsq_out = S;
+    if (units_out) {
+        units_out[0] = (uint64_t)units;
+        units_out[1] = (uint64_t)(units >> 64);
+    }
+    if (qexp_out)
+        *qexp_out = 2 * E - 80;
+    return (float)sqrt(S / (double)n);
+}
+
+float oracle_onebit_scale(const float* x, uint64_t n, double* sumsq_out)
+{
+    return oracle_onebit_scale_units(x, n, sumsq_out, 0, 0);
+}
+
+/* Sign bits, little-endian within each byte: bit k of byte j is element 8j+k,
+ * 1 for x >= 0 (sgn = +1), 0 for x < 0. */
+void oracle_onebit_pack(const float* x, uint64_t n, uint8_t* bits)
+{
+    for (uint64_t j = 0; j < (n + 7) / 8; ++j)
+        bits[j] = 0;
+    for (uint64_t i = 0; i < n; ++i)
+        if (!(x[i] < 0.0f))
+            bits[i / 8] |= (uint8_t)(1u << (i % 8));
+}
+
+/* x -> the compressed vector s*sgn(x) and the new error x - s*sgn(x). */
+static void compress(const float* x, uint64_t n, float s, float* c, float* err)
+{
+    for (uint64_t i = 0; i < n; ++i) {
+        c[i] = x[i] < 0.0f ? -s : s;
+        err[i] = x[i] - c[i];
+    }
+}
+
+/* One compression-stage step; scales[0] = worker scale, scales[1] = server
+ * scale.  Nothing changes when the decision skipped the step. */
+int oracle_onebit_step(const oracle_state_t* st, uint16_t* p16, float* p32, float* m32, const float* v32,
+                       float* err_w, float* err_s, const uint16_t* g16, uint64_t n,
+                       uint8_t* bits_w, uint8_t* bits_s, float* scales)
+{
+    if (st->skip)
+        return 0;
+    float* x = (float*)calloc(n ? n : 1, sizeof(float));
+    float* c = (float*)calloc(n ? n : 1, sizeof(float));
+    if (!x || !c) {
+        free(x);
+        free(c);
+        return -1;
+    }
+    for (uint64_t i = 0; i < n; ++i) {                  /* local momentum, then the worker's error */
+        float g = oracle_f32_from_f16(g16[i]) * st->gmul;
+        m32[i] = st->beta1 * m32[i] + st->omb1 * g;
+        x[i] = m32[i] + err_w[i];
+    }
+    scales[0] = oracle_onebit_scale(x, n, 0);
+    oracle_onebit_pack(x, n, bits_w);
+    compress(x, n, scales[0], c, err_w);
+    for (uint64_t i = 0; i < n; ++i)                    /* server: one worker's average is its own */
+        x[i] = c[i] + err_s[i];
+    scales[1] = oracle_onebit_scale(x, n, 0);
+    oracle_onebit_pack(x, n, bits_s);
+    compress(x, n, scales[1], m32, err_s);              /* the momentum becomes the server's output */
+    for (uint64_t i = 0; i < n; ++i) {
+        float u = m32[i] / (sqrtf(v32[i]) + st->eps) + st->wd * p32[i];
+        p32[i] = p32[i] - st->lr * u;
+        p16[i] = oracle_f16_from_f32(p32[i]);
+    }
+    free(x);
+    free(c);
+    return 0;
 }

@@ -61,6 +61,13 @@ def lib():
         L.oracle_norm_overflow.argtypes = [vp, u64, C.POINTER(C.c_double), C.POINTER(i32)]
         L.oracle_norm_overflow_f32.argtypes = [vp, u64, C.POINTER(C.c_double), C.POINTER(i32)]
         L.oracle_adam_update_f32.argtypes = [C.POINTER(OracleState), vp, vp, vp, vp, vp, u64]
+        L.oracle_onebit_scale.argtypes = [vp, u64, C.POINTER(C.c_double)]
+        L.oracle_onebit_scale.restype = C.c_float
+        L.oracle_onebit_scale_units.argtypes = [vp, u64, C.POINTER(C.c_double), vp, C.POINTER(C.c_int)]
+        L.oracle_onebit_scale_units.restype = C.c_float
+        L.oracle_onebit_pack.argtypes = [vp, u64, vp]
+        L.oracle_onebit_step.argtypes = [C.POINTER(OracleState), vp, vp, vp, vp, vp, vp, vp, u64, vp, vp, vp]
+        L.oracle_onebit_step.restype = C.c_int
         L.oracle_state_init.argtypes = [C.POINTER(OracleState), C.c_double]
         L.oracle_decide.argtypes = [C.POINTER(OracleState), C.POINTER(OracleHParams),
                                     C.c_double, i32]
@@ -184,3 +191,45 @@ def step(hp: OracleHParams, st: OracleState, srcs, segments, grad16, p16, p32, m
     lib().oracle_step(C.byref(hp), C.byref(st), arr, len(segments), _ptr(grad16, np.uint16),
                       _ptr(p16, np.uint16), _ptr(p32, np.float32), _ptr(m32, np.float32),
                       _ptr(v32, np.float32), p32.size)
+
+
+# ---- 1-bit Adam, compression stage -----------------------------------------------
+
+def onebit_scale(x: np.ndarray):
+    """-> (s, S): the fp32 scale ||x||_2/sqrt(d) from the exact windowed sum S."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    S = C.c_double()
+    s = lib().oracle_onebit_scale(_ptr(x, np.float32), x.size, C.byref(S))
+    return float(np.float32(s)), S.value
+
+
+def onebit_scale_units(x: np.ndarray):
+    """-> (s, S, units, qexp): also the exact integer sum and the window exponent."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    S = C.c_double()
+    u = np.zeros(2, np.uint64)
+    e = C.c_int()
+    s = lib().oracle_onebit_scale_units(_ptr(x, np.float32), x.size, C.byref(S), u.ctypes.data, C.byref(e))
+    return float(np.float32(s)), S.value, (int(u[1]) << 64) | int(u[0]), e.value
+
+
+def onebit_pack(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros((x.size + 7) // 8, np.uint8)
+    lib().oracle_onebit_pack(_ptr(x, np.float32), x.size, out.ctypes.data)
+    return out
+
+
+def onebit_step(st: OracleState, p16, p32, m32, v32, err_w, err_s, g16):
+    """One compression-stage step; -> (bits_w, bits_s, (s_w, s_s))."""
+    n = p32.size
+    assert p16.size == m32.size == v32.size == err_w.size == err_s.size == g16.size == n
+    bw = np.zeros((n + 7) // 8, np.uint8)
+    bs = np.zeros((n + 7) // 8, np.uint8)
+    sc = np.zeros(2, np.float32)
+    rc = lib().oracle_onebit_step(C.byref(st), _ptr(p16, np.uint16), _ptr(p32, np.float32), _ptr(m32, np.float32),
+                                  _ptr(v32, np.float32), _ptr(err_w, np.float32), _ptr(err_s, np.float32),
+                                  _ptr(g16, np.uint16), n, bw.ctypes.data, bs.ctypes.data, sc.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle_onebit_step")
+    return bw, bs, (float(sc[0]), float(sc[1]))
