@@ -36,6 +36,9 @@
  *     fused zero_flatten_norm_bucket_f32 for the last micro-batch), and the
  *     *_f32 reduction and update read that fp32 gradient (30 bytes per
  *     parameter in the update);
+ *   - 1-bit Adam (DeepSpeed article): after a warm-up of ordinary steps,
+ *     zero_onebit_step compresses the momentum to one bit per element with
+ *     error feedback and updates with the frozen variance;
  *   - host step (ZeRO-Offload, in the DeepSpeed article: ZeRO-2 plus CPU
  *     memory): the fp32 master parameters, momentum and variance live in host
  *     memory and the CPU steps them (zero_host_*, zero_offload_step), with
@@ -319,6 +322,56 @@ int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32,
 int zero_shard_adam_step_f32(uint16_t* p16, float* p32, float* m32, float* v32,
                              const float* grad32, uint64_t n,
                              const zero_step_state_t* dev_state, void* stream);
+
+/* ---- 1-bit Adam, compression stage ------------------------------------ */
+
+/* State of the compression stage in DEVICE memory (72 bytes, 8-byte
+ * aligned; initialise with zero_onebit_state_init).  After each step it
+ * holds the two scales and their exact sums. */
+typedef struct {
+    float    scale_w, scale_s;  /* worker and server scales of the last step */
+    double   sumsq_w, sumsq_s;  /* the exact windowed sums, rounded to binary64 */
+    int32_t  qexp_w, qexp_s;    /* window exponents: sum = units * 2^qexp */
+    uint32_t done_blocks;       /* internal arrival counter; 0 between calls */
+    uint32_t reserved;
+    uint64_t units_w[2];        /* exact integer sums (low, high) */
+    uint64_t units_s[2];
+} zero_onebit_state_t;
+
+/* Enqueue the zeroing of a compression-stage state.
+ * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_EHIP. */
+int zero_onebit_state_init(zero_onebit_state_t* dev_onebit, void* stream);
+
+/* Bytes of device workspace zero_onebit_step needs for n elements. */
+size_t zero_onebit_workspace_bytes(uint64_t n);
+
+/* One compression-stage step of 1-bit Adam (the DeepSpeed article: 1-bit
+ * Adam cuts communication up to 5x with Adam-like convergence; the
+ * algorithm is Tang et al. 2021, Algorithm 1), run after a warm-up of
+ * ordinary steps (zero_shard_adam_step) with the variance v32 frozen.  With
+ * the decision in dev_state (gmul, beta1, lr, eps, wd; nothing happens when
+ * it says skip), on this rank, which is its own server:
+ *   g = fp32(grad16)*gmul;  m = beta1*m + (1-beta1)*g
+ *   x = m + err_w;  s_w = S(x);  bits_w = sgn(x);  err_w = x - s_w*sgn(x)
+ *   u = s_w*sgn(x) + err_s;  s_s = S(u);  bits_s = sgn(u)
+ *   m = s_s*sgn(u);  err_s = u - m
+ *   p = p - lr*(m/(sqrt(v)+eps) + wd*p);  p16 = fp16(p)
+ * sgn(x) = +1 for x >= 0 (zeros too), -1 otherwise; bit k of byte j of a
+ * bits array is element 8j+k, 1 for +1.  S(x) = fp32(sqrt(sum/n)) with the
+ * sum of squares EXACT in a window set by max|x|: with 2^E <= max|x| <
+ * 2^(E+1), each square is rounded to the nearest multiple of 2^(2E-80),
+ * the integers are summed exactly and the total is rounded once to
+ * binary64.  Every elementwise operation is one binary32 operation in the
+ * order above.  Results do not depend on the launch configuration.
+ * p16, p32, m32, v32, err_w, err_s, grad16: device, n elements, 16-byte
+ * aligned; bits_w, bits_s: device, (n+7)/8 bytes; workspace: device,
+ * 256-byte aligned, >= zero_onebit_workspace_bytes(n).
+ * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_ERANGE (n > 2^40,
+ *         workspace too small), ZERO_EHIP. */
+int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const float* v32, float* err_w, float* err_s,
+                     const uint16_t* grad16, uint64_t n, uint8_t* bits_w, uint8_t* bits_s,
+                     const zero_step_state_t* dev_state, zero_onebit_state_t* dev_onebit,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- host step (ZeRO-Offload form) ----------------------------------- */
 

@@ -224,3 +224,24 @@ def test_decide_validation(Z):
     assert L.zero_shard_decide(FAKE, (1 << 30) + 1, C.byref(hp), FAKE, FAKE, 1 << 20, None) == E.ZERO_ERANGE
     bad = Z.hparams(beta2=1.0)
     assert L.zero_shard_decide(FAKE, 10, C.byref(bad), FAKE, FAKE, ws, None) == E.ZERO_EINVAL
+
+
+def test_onebit_validation(Z):
+    L, E = Z.lib(), Z._lib
+    n = 1000
+    ws = Z.zero_onebit_workspace_bytes(n)
+    assert ws > 0 and Z.zero_onebit_workspace_bytes(n) == ws
+    ok = [FAKE] * 7
+    call = lambda ptrs=ok, nn=n, bw=FAKE, bs=FAKE, st=FAKE, ob=FAKE, w=FAKE, wb=ws: L.zero_onebit_step(
+        *ptrs, nn, bw, bs, st, ob, w, wb, None)
+    assert call(st=0) == E.ZERO_EINVAL and call(ob=0) == E.ZERO_EINVAL and call(w=0) == E.ZERO_EINVAL
+    assert call(bw=0) == E.ZERO_EINVAL
+    assert call(ptrs=[FAKE] * 6 + [0]) == E.ZERO_EINVAL
+    assert call(ptrs=[FAKE + 8] + [FAKE] * 6) == E.ZERO_EALIGN
+    assert call(w=FAKE + 16) == E.ZERO_EALIGN
+    assert call(ob=FAKE + 4) == E.ZERO_EALIGN
+    assert call(wb=ws - 1) == E.ZERO_ERANGE
+    assert call(nn=(1 << 40) + 8, wb=1 << 62) == E.ZERO_ERANGE
+    assert L.zero_onebit_state_init(0, None) == E.ZERO_EINVAL
+    assert L.zero_onebit_state_init(FAKE + 4, None) == E.ZERO_EALIGN
+    assert C.sizeof(Z.OneBitState) == 72

@@ -1,0 +1,191 @@
+"""GPU parity tests of 1-bit Adam on the shard (warm-up with the ordinary fused
+step, then the compression stage with frozen variance): the HIP path through
+the C ABI against the oracle on the same seeded inputs.
+
+Contract, every step: the step state bitwise; in the compression stage both
+scales, their exact integer sums and window exponents bitwise, both sign-bit
+payloads bitwise, the momentum, both error buffers, p32 and p16 bitwise over
+the whole shard (every operation is one binary32 operation in the same order
+on both sides, and the scales come from exact sums), and v32 unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import shardgen
+
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as H  # noqa: E402
+import zero_partitioned_mixed_flatten_amd as Z  # noqa: E402
+
+
+def _small(name, n, seed, max_seg=None):
+    w = shardgen.workload("tiny")
+    w.name = name
+    rng = np.random.default_rng(seed)
+    numels, segs = shardgen.random_segments(rng, n, max_seg or max(1, n // 5))
+    w.layout = shardgen.ShardLayout(name, n, 1, 0, 0, n, [f"t{i}" for i in range(len(numels))], numels, segs)
+    return w
+
+
+def _f32(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+class OneBitRun:
+    def __init__(self, w, warmup):
+        self.w = w
+        n = w.n
+        p32 = shardgen.master_params(w)
+        self.dev = Z.OneBitStep(n, warmup)
+        if n:
+            self.dev.p32.copy_(torch.from_numpy(p32))
+            self.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
+        self.dev.init_state(w.scale0)
+        self.st = O.new_state(w.scale0)
+        self.hp_o = H.oracle_hparams(w.hp)
+        self.hp_d = H.device_hparams(w.hp)
+        z = lambda: np.zeros(n, np.float32)
+        self.p32, self.m32, self.v32, self.ew, self.es = p32.copy(), z(), z(), z(), z()
+        self.p16 = shardgen.to_f16_bits(p32)
+        self.warmup = warmup
+        self.k = 0
+        self.compressed = 0
+
+    def step(self):
+        self.k += 1
+        w = self.w
+        gpart = shardgen.grad_partition(w, self.k, self.st.loss_scale)
+        srcs = shardgen.source_tensors(w.layout, gpart)
+        del gpart
+        dsrcs = [H.to_dev16(s) for s in srcs]
+        compress = self.st.step >= self.warmup
+        assert compress == self.dev.compressing()
+        H.log(f"onebit {w.name} n={w.n} step {self.k} compress={compress}")
+        self.dev.set_segments(dsrcs, w.layout.segments, w.bucket_elems)
+        v_before = self.dev.v32.clone()
+        self.dev.step(self.hp_d)
+        grad = np.empty(w.n, np.uint16)
+        O.flatten(srcs, w.layout.segments, grad)
+        s, o = O.norm_overflow(grad)
+        O.decide(self.st, self.hp_o, s, o)
+        if compress:
+            bw, bs, (sw, ss) = O.onebit_step(self.st, self.p16, self.p32, self.m32, self.v32, self.ew, self.es, grad)
+        else:
+            O.adam_update(self.st, self.p16, self.p32, self.m32, self.v32, grad)
+        torch.cuda.synchronize()
+        H.compare_state(self.dev.read_state(), self.st, None)
+        n = w.n
+        if compress and not self.st.skip:
+            self.compressed += 1
+            ob = self.dev.read_onebit()
+            assert (ob.scale_w, ob.scale_s) == (np.float32(sw), np.float32(ss)), (ob.scale_w, sw, ob.scale_s, ss)
+            assert np.array_equal(self.dev.bits_w.cpu().numpy()[:(n + 7) // 8], bw)
+            assert np.array_equal(self.dev.bits_s.cpu().numpy()[:(n + 7) // 8], bs)
+            assert torch.equal(self.dev.v32, v_before)                    # frozen
+        for name, t, ref in (("p32", self.dev.p32, self.p32), ("m32", self.dev.m32, self.m32),
+                             ("v32", self.dev.v32, self.v32), ("err_w", self.dev.err_w, self.ew),
+                             ("err_s", self.dev.err_s, self.es)):
+            got = _f32(t)[:n]
+            assert np.array_equal(got, ref.view(np.uint32)), (name, int(np.sum(got != ref.view(np.uint32))))
+        assert np.array_equal(H.bits16(self.dev.p16)[:n], self.p16)
+        del dsrcs
+
+
+def test_onebit_tiny_warmup_then_compression():
+    r = OneBitRun(shardgen.workload("tiny"), warmup=3)
+    for _ in range(8):
+        r.step()
+    assert r.compressed == 5
+
+
+@pytest.mark.parametrize("n", [1, 7, 9, 4099, 65_536 * 3 + 5, (1 << 20) + 3])
+def test_onebit_ragged(n):
+    r = OneBitRun(_small(f"onebit{n}", n, seed=500 + n), warmup=1)
+    for _ in range(3):
+        r.step()
+
+
+def test_onebit_empty():
+    w = _small("onebit-empty", 0, seed=0)
+    w.layout = shardgen.ShardLayout("empty", 0, 1, 0, 0, 0, [], [], [])
+    r = OneBitRun(w, warmup=0)
+    r.step()
+    ob = r.dev.read_onebit()
+    assert (ob.scale_w, ob.scale_s) == (0.0, 0.0)
+
+
+def test_onebit_gpt2_shard_full_size():
+    r = OneBitRun(shardgen.workload("gpt2"), warmup=2)
+    for _ in range(4):
+        r.step()
+    assert r.compressed == 2
+
+
+def test_onebit_skip_in_compression_stage():
+    w = _small("onebit-skip", 100_003, seed=31)
+    w.inject = {4: 0x7C00}
+    r = OneBitRun(w, warmup=2)
+    for _ in range(3):
+        r.step()
+    snap = [t.clone() for t in (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.err_w, r.dev.err_s)]
+    r.step()                                           # step 4: inf -> skipped
+    assert r.dev.read_state().skip == 1
+    for a, b in zip(snap, (r.dev.p16, r.dev.p32, r.dev.m32, r.dev.err_w, r.dev.err_s)):
+        assert a.cpu().numpy().tobytes() == b.cpu().numpy().tobytes()
+    r.step()
+    assert r.dev.read_state().step == 4
+
+
+def _crafted(n, seed, lo, hi):
+    rng = np.random.default_rng(seed)
+    mant = rng.integers(1 << 23, 1 << 24, n).astype(np.float64)
+    x = (mant * np.exp2(rng.integers(lo, hi, n).astype(np.float64))).astype(np.float32)
+    return x * np.where(rng.integers(0, 2, n) == 1, -1, 1).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", ["wide", "subnormal", "zeros", "huge"])
+def test_onebit_window_extremes(case):
+    """One compression step from crafted momentum and error buffers: values
+    spanning 40 binades, binary32 subnormals, all-zero vectors (scale 0, with
+    -0.0 entries) and magnitudes near 2^100."""
+    n = 40_009
+    rng = np.random.default_rng({"wide": 11, "subnormal": 12, "zeros": 13, "huge": 14}[case])
+    if case == "wide":
+        m, ew, es = (_crafted(n, s, -60, -20) for s in (1, 2, 3))
+    elif case == "subnormal":
+        m, ew, es = (_crafted(n, s, -170, -140) for s in (4, 5, 6))
+    elif case == "zeros":
+        m = np.zeros(n, np.float32)
+        m[::3] = -0.0
+        ew, es = m.copy(), m.copy()
+    else:
+        m, ew, es = (_crafted(n, s, 80, 100) for s in (7, 8, 9))
+    p32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    v32 = (np.abs(rng.standard_normal(n)) * 1e-6).astype(np.float32)
+    g16 = np.zeros(n, np.uint16)                       # zero gradient: m = beta1 * m
+    dev = Z.OneBitStep(n, warmup=0)
+    for t, a in ((dev.p32, p32), (dev.m32, m), (dev.v32, v32), (dev.err_w, ew), (dev.err_s, es)):
+        t.copy_(torch.from_numpy(a))
+    dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
+    dev.grad16.copy_(torch.from_numpy(g16.view(np.float16)))
+    dev.init_state(1.0)
+    hp = Z.hparams(max_grad_norm=0.0)
+    Z.zero_shard_norm_overflow(dev.grad16, n, hp, dev.state, dev.workspace)
+    H.log(f"onebit window case {case}")
+    dev.compress()
+    st = O.new_state(1.0)
+    O.decide(st, O.hparams(max_grad_norm=0.0), *O.norm_overflow(g16))
+    refs = [shardgen.to_f16_bits(p32), p32.copy(), m.copy(), v32.copy(), ew.copy(), es.copy()]
+    x_w = (np.float32(st.beta1) * m + np.float32(st.omb1) * np.float32(0.0)) + ew   # the worker's input, for units
+    bw, bs, (sw, ss) = O.onebit_step(st, *refs, g16)
+    torch.cuda.synchronize()
+    ob = dev.read_onebit()
+    _, S, units, qexp = O.onebit_scale_units(x_w)
+    assert (ob.scale_w, ob.scale_s) == (np.float32(sw), np.float32(ss))
+    assert ob.units("w") == units and ob.qexp_w == qexp and ob.sumsq_w == S
+    assert np.array_equal(dev.bits_w.cpu().numpy(), bw) and np.array_equal(dev.bits_s.cpu().numpy(), bs)
+    for t, ref in ((dev.p32, refs[1]), (dev.m32, refs[2]), (dev.err_w, refs[4]), (dev.err_s, refs[5])):
+        assert np.array_equal(_f32(t), ref.view(np.uint32))
+    assert np.array_equal(H.bits16(dev.p16), refs[0])

@@ -22,7 +22,8 @@ EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "ze
            "zero_decide_workspace_bytes", "zero_shard_decide", "zero_flatten_norm_bucket_f32",
            "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32", "zero_host_create", "zero_host_destroy",
            "zero_host_threads", "zero_host_state_init", "zero_host_norm_overflow", "zero_host_adam_step",
-           "zero_offload_step", "zero_host_stream_copy")
+           "zero_offload_step", "zero_host_stream_copy", "zero_onebit_state_init", "zero_onebit_workspace_bytes",
+           "zero_onebit_step")
 NORM_PARTIAL_BYTES = 32
 
 
@@ -59,8 +60,19 @@ class StepState(C.Structure):
         return d
 
 
+class OneBitState(C.Structure):
+    _fields_ = [("scale_w", C.c_float), ("scale_s", C.c_float), ("sumsq_w", C.c_double), ("sumsq_s", C.c_double),
+                ("qexp_w", C.c_int32), ("qexp_s", C.c_int32), ("done_blocks", C.c_uint32), ("reserved", C.c_uint32),
+                ("units_w", C.c_uint64 * 2), ("units_s", C.c_uint64 * 2)]
+
+    def units(self, which: str) -> int:
+        u = getattr(self, f"units_{which}")
+        return (int(u[1]) << 64) | int(u[0])
+
+
 STATE_BYTES = C.sizeof(StepState)
-assert STATE_BYTES == 128 and C.sizeof(Segment) == 32 and C.sizeof(HParams) == 80
+ONEBIT_STATE_BYTES = C.sizeof(OneBitState)
+assert STATE_BYTES == 128 and C.sizeof(Segment) == 32 and C.sizeof(HParams) == 80 and ONEBIT_STATE_BYTES == 72
 
 _lib = None
 
@@ -104,9 +116,13 @@ def lib():
         L.zero_host_adam_step.argtypes = [vp, vp, vp, vp, vp, vp, u64, C.POINTER(StepState)]
         L.zero_offload_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u64, C.POINTER(HParams), vp, vp, u64, vp]
         L.zero_host_stream_copy.argtypes = [vp, vp, vp, u64]
+        L.zero_onebit_state_init.argtypes = [vp, vp]
+        L.zero_onebit_workspace_bytes.argtypes = [u64]
+        L.zero_onebit_workspace_bytes.restype = C.c_size_t
+        L.zero_onebit_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp, C.c_size_t, vp]
         for name in EXPORTS:
             if name not in ("zero_status_string", "zero_norm_workspace_bytes", "zero_flatten_norm_partials",
-                            "zero_decide_workspace_bytes", "zero_host_destroy"):
+                            "zero_decide_workspace_bytes", "zero_host_destroy", "zero_onebit_workspace_bytes"):
                 getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -376,3 +392,34 @@ def zero_host_stream_copy(ctx: int, dst, src, nbytes: int) -> None:
     _hneed("zero_host_stream_copy", dst, nbytes)
     _hneed("zero_host_stream_copy", src, nbytes)
     _check("zero_host_stream_copy", lib().zero_host_stream_copy(ctx, _hptr(dst), _hptr(src), nbytes))
+
+
+# ---- 1-bit Adam, compression stage -------------------------------------------------
+
+def zero_onebit_state_init(dev_onebit, stream=None) -> None:
+    _need("zero_onebit_state_init", dev_onebit, ONEBIT_STATE_BYTES)
+    _check("zero_onebit_state_init", lib().zero_onebit_state_init(_ptr(dev_onebit), _stream(stream)))
+
+
+def zero_onebit_workspace_bytes(n: int) -> int:
+    return int(lib().zero_onebit_workspace_bytes(n))
+
+
+def zero_onebit_step(p16, p32, m32, v32, err_w, err_s, grad16, n: int, bits_w, bits_s, dev_state, dev_onebit,
+                     workspace, stream=None) -> None:
+    for t, b in ((p16, 2), (p32, 4), (m32, 4), (v32, 4), (err_w, 4), (err_s, 4), (grad16, 2)):
+        _need("zero_onebit_step", t, b * n)
+    for t in (bits_w, bits_s):
+        _need("zero_onebit_step", t, (n + 7) // 8)
+    _need("zero_onebit_step", dev_state, STATE_BYTES)
+    _need("zero_onebit_step", dev_onebit, ONEBIT_STATE_BYTES)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_onebit_step",
+           lib().zero_onebit_step(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(err_w), _ptr(err_s),
+                                  _ptr(grad16), n, _ptr(bits_w), _ptr(bits_s), _ptr(dev_state), _ptr(dev_onebit),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def read_onebit_state(dev_onebit) -> OneBitState:
+    raw = dev_onebit.detach().to("cpu").numpy().tobytes()
+    return OneBitState.from_buffer_copy(raw)

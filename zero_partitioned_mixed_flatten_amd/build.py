@@ -22,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libzero_mi355x.so")
-SOURCES = ["host.hip", "flatten.hip", "norm.hip", "adam.hip"]
+SOURCES = ["host.hip", "flatten.hip", "norm.hip", "adam.hip", "onebit.hip"]
 HOST_SOURCES = ["host_step.cpp"]          # plain C++ (the CPU side of the offloaded step)
 ARCH = "gfx950"
 

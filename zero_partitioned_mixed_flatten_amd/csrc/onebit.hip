@@ -1,0 +1,527 @@
+// onebit.hip -- the compression stage of 1-bit Adam on one rank's flat shard
+// (the DeepSpeed article: 1-bit Adam cuts communication up to 5x with
+// Adam-like convergence; the algorithm is Tang et al. 2021, Algorithm 1).
+// After a warm-up of ordinary Adam steps the variance is frozen; each step
+//   m = beta1*m + (1-beta1)*g;  x = m + ew;  cw = s_w*sgn(x);  ew = x - cw
+//   u = cw + es;  m = s_s*sgn(u);  es = u - m      (one rank is its own server)
+//   p = p - lr*(m/(sqrt(v)+eps) + wd*p),  p16 = fp16(p)
+// with sgn(x) = +1 for x >= 0, -1 otherwise, and s = ||x||_2/sqrt(d) in fp32
+// from an EXACT sum of squares: with E the binary exponent of max|x|, each
+// square is rounded to the nearest multiple of 2^(2E-80) (never a tie), the
+// integers are summed exactly and the total is rounded once to binary64.
+// The sign bits (one byte per 8 elements, element 8j+k in bit k of byte j)
+// are what a multi-rank run would exchange.
+//
+// Five kernels, because two global scales sit on the data path:
+//   A  momentum + per-block max|x|           one-shot, 8 elements per thread
+//   B  exact sum of x^2 in the window, s_w   <= 256 workgroups x 1024, grid-stride;
+//      every workgroup first folds A's block maxima (L2-resident), the last
+//      one to arrive folds the limbs and writes s_w
+//   C  worker compression: sign byte, ew, u = cw + es, per-block max|u|
+//   D  exact sum of u^2, s_s                  as B (u is recomputed from the bits)
+//   E  server compression + update: m, es, bits, p, p16
+// Per-block maxima go to memory (no same-address atomics, which serialise).
+// The exact windowed square: z = x * 2^(40-E) (exact, |z| < 2^41),
+//   a = fma(z, z, C1) - C1       z^2 to a multiple of 2^41 (C1 = 1.5*2^93)
+//   b = (fma(z, z, -a) + C2) - C2   the rest, to the nearest integer (C2 = 1.5*2^52)
+// so z^2 rounded to an integer is a + b; with at most 2^11 elements per
+// thread, sum(a) <= 2^93 in steps of 2^41 and |sum(b)| <= 2^51 stay exact.
+#include <math.h>
+
+#include "decide.hpp"
+#include "exact_norm.hpp"
+
+namespace zero {
+namespace {
+
+constexpr int kBlock = 256;                  // one-shot kernels A, C, E
+constexpr double kWinHi = 0x1.8p93;          // ulp 2^41
+constexpr double kWinLo = 0x1.8p52;          // ulp 1
+
+struct Coef {
+    float gmul, b1, omb1, eps, wd, lr;
+};
+
+__device__ __forceinline__ Coef coef_of(const zero_step_state_t* st)
+{
+    return Coef{st->gmul, st->beta1, st->omb1, st->eps, st->wd, st->lr};
+}
+
+__device__ __forceinline__ float sgn_scale(float x, float s) { return x < 0.0f ? -s : s; }
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
+
+// Max over a workgroup of BLOCK threads; valid in thread 0.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_max(uint32_t v)
+{
+    __shared__ uint32_t sm[BLOCK / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    if (BLOCK > 64) {
+        if ((threadIdx.x & 63) == 0)
+            sm[threadIdx.x >> 6] = v;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int w = 1; w < BLOCK / 64; ++w)
+                v = sm[w] > v ? sm[w] : v;
+        __syncthreads();
+    }
+    return v;
+}
+
+// Binary exponent E of a positive binary32 given as bits: 2^E <= x < 2^(E+1).
+__device__ __forceinline__ int exponent_of(uint32_t bits)
+{
+    const int e = int(bits >> 23);
+    if (e)
+        return e - 127;
+    return (31 - __builtin_clz(bits)) - 149;                 // subnormal: highest mantissa bit
+}
+
+struct AccWin {
+    double a = 0.0, b = 0.0;
+    __device__ __forceinline__ void add(float x, double w)
+    {
+        const double z = double(x) * w;                       // exact
+        const double hi = __builtin_fma(z, z, kWinHi) - kWinHi;
+        a += hi;
+        b += (__builtin_fma(z, z, -hi) + kWinLo) - kWinLo;
+    }
+    __device__ __forceinline__ exact::Limbs limbs() const
+    {
+        const int64_t au = int64_t(a * 0x1p-41);              // < 2^53
+        const int64_t bu = int64_t(b);                         // |.| <= 2^52
+        const int64_t hs = au << 9;                            // au * 2^41 = hs * 2^32
+        return exact::Limbs{bu & 0xFFFFFFFFll, (hs & 0xFFFFFFFFll) + (bu >> 32), hs >> 32, 0};
+    }
+};
+
+// ---- A: momentum + block max of |m + ew| ----------------------------------------
+
+__global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restrict__ m32, const float* __restrict__ ew,
+                                                                 const uint16_t* __restrict__ g16, uint64_t n,
+                                                                 const zero_step_state_t* __restrict__ st,
+                                                                 uint32_t* __restrict__ blockmax)
+{
+    if (st->skip)
+        return;
+    const Coef c = coef_of(st);
+    const uint64_t nvec = n >> 3;
+    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
+    uint32_t mx = 0;
+    if (j < nvec) {
+        const f16x8 g = __builtin_bit_cast(f16x8, reinterpret_cast<const u32x4*>(g16)[j]);
+        f32x4* mv = reinterpret_cast<f32x4*>(m32) + 2 * j;
+        const f32x4* ev = reinterpret_cast<const f32x4*>(ew) + 2 * j;
+        f32x4 m[2] = {mv[0], mv[1]};
+        const f32x4 e[2] = {ev[0], ev[1]};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+#pragma clang fp contract(off)
+                const float gk = float(g[4 * h + k]) * c.gmul;
+                m[h][k] = c.b1 * m[h][k] + c.omb1 * gk;
+                const uint32_t a = abs_bits(m[h][k] + e[h][k]);
+                mx = a > mx ? a : mx;
+            }
+        mv[0] = m[0];
+        mv[1] = m[1];
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+#pragma clang fp contract(off)
+        const uint64_t i = (nvec << 3) + threadIdx.x;
+        const float gk = float(__builtin_bit_cast(_Float16, g16[i])) * c.gmul;
+        const float mi = c.b1 * m32[i] + c.omb1 * gk;
+        m32[i] = mi;
+        const uint32_t a = abs_bits(mi + ew[i]);
+        mx = a > mx ? a : mx;
+    }
+    mx = block_max<kBlock>(mx);
+    if (threadIdx.x == 0)
+        blockmax[blockIdx.x] = mx;
+}
+
+// ---- B / D: the exact windowed sum and the scale ------------------------------------
+
+// The vector whose scale is taken: x = m + ew (worker), or u = s_w*sgn + es (server).
+struct WorkerX {
+    const float* m;
+    const float* ew;
+    __device__ __forceinline__ float at(uint64_t i) const { return m[i] + ew[i]; }
+    __device__ __forceinline__ void vec(uint64_t j, float (&x)[8]) const
+    {
+        const f32x4* mv = reinterpret_cast<const f32x4*>(m) + 2 * j;
+        const f32x4* ev = reinterpret_cast<const f32x4*>(ew) + 2 * j;
+        const f32x4 a = __builtin_nontemporal_load(mv), b = __builtin_nontemporal_load(mv + 1);
+        const f32x4 c = __builtin_nontemporal_load(ev), d = __builtin_nontemporal_load(ev + 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[k] = a[k] + c[k];
+            x[4 + k] = b[k] + d[k];
+        }
+    }
+};
+
+struct ServerU {
+    const uint8_t* bits;
+    const float* es;
+    float sw;
+    __device__ __forceinline__ float at(uint64_t i) const
+    {
+        const float c = ((bits[i >> 3] >> (i & 7)) & 1) ? sw : -sw;
+        return c + es[i];
+    }
+    __device__ __forceinline__ void vec(uint64_t j, float (&x)[8]) const
+    {
+        const uint32_t byte = bits[j];
+        const f32x4* ev = reinterpret_cast<const f32x4*>(es) + 2 * j;
+        const f32x4 a = __builtin_nontemporal_load(ev), b = __builtin_nontemporal_load(ev + 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[k] = (((byte >> k) & 1) ? sw : -sw) + a[k];
+            x[4 + k] = (((byte >> (4 + k)) & 1) ? sw : -sw) + b[k];
+        }
+    }
+};
+
+// Which scale a sum kernel writes.
+enum Which { kWorker = 0, kServer = 1 };
+
+template <int WHICH, typename V>
+__device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restrict__ blockmax, uint64_t nmax,
+                              const zero_step_state_t* __restrict__ st, zero_onebit_state_t* __restrict__ ob,
+                              NormPartial* __restrict__ ws)
+{
+    // the window: max over the previous kernel's block maxima
+    uint32_t mx = 0;
+    for (uint64_t b = threadIdx.x; b < nmax; b += kNormBlock)
+        mx = blockmax[b] > mx ? blockmax[b] : mx;
+    __shared__ uint32_t s_mx;
+    mx = block_max<kNormBlock>(mx);
+    if (threadIdx.x == 0)
+        s_mx = mx;
+    __syncthreads();
+    mx = s_mx;
+    const int E = mx ? exponent_of(mx) : 0;
+    const double w = ldexp(1.0, 40 - E);
+
+    AccWin acc;
+    if (mx) {
+        const uint64_t nvec = n >> 3;
+        const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
+        for (uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x; j < nvec; j += stride) {
+            float x[8];
+            vsrc.vec(j, x);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                acc.add(x[k], w);
+        }
+        if (blockIdx.x == 0 && threadIdx.x < (n & 7))
+            acc.add(vsrc.at((nvec << 3) + threadIdx.x), w);
+    }
+    exact::Limbs s = acc.limbs();
+    uint32_t flag = 0;
+    exact::block_fold<kNormBlock>(s, flag);
+
+    __shared__ uint32_t s_last;
+    if (threadIdx.x == 0) {
+        ws[blockIdx.x] = exact::make_partial(s, 0);
+        const uint32_t prev = __hip_atomic_fetch_add(&ob->done_blocks, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    exact::Limbs t{0, 0, 0, 0};
+    uint32_t tflag = 0;
+    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock)
+        exact::fold_partial(t, tflag, ws[b]);
+    exact::block_fold<kNormBlock>(t, tflag);
+    if (threadIdx.x == 0) {
+        uint64_t hi = 0, lo = 0;
+        exact::limbs_to_u128(t, hi, lo);                        // < n * 2^82: always fits
+        const int qexp = 2 * E - 80;
+        const double S = mx ? ldexp(u128_to_f64(hi, lo), qexp) : 0.0;
+        const float scale = n ? float(sqrt(S / double(n))) : 0.0f;
+        if (WHICH == kWorker) {
+            ob->scale_w = scale;
+            ob->sumsq_w = S;
+            ob->qexp_w = mx ? qexp : 0;
+            ob->units_w[0] = lo;
+            ob->units_w[1] = hi;
+        } else {
+            ob->scale_s = scale;
+            ob->sumsq_s = S;
+            ob->qexp_s = mx ? qexp : 0;
+            ob->units_s[0] = lo;
+            ob->units_s[1] = hi;
+        }
+        ob->done_blocks = 0;                                    // re-arm for the next sum
+    }
+}
+
+__global__ __launch_bounds__(kNormBlock) void onebit_sum_worker_kernel(const float* __restrict__ m32,
+                                                                       const float* __restrict__ ew, uint64_t n,
+                                                                       const uint32_t* __restrict__ blockmax,
+                                                                       uint64_t nmax,
+                                                                       const zero_step_state_t* __restrict__ st,
+                                                                       zero_onebit_state_t* __restrict__ ob,
+                                                                       NormPartial* __restrict__ ws)
+{
+    if (st->skip)
+        return;
+    sum_and_scale<kWorker>(WorkerX{m32, ew}, n, blockmax, nmax, st, ob, ws);
+}
+
+__global__ __launch_bounds__(kNormBlock) void onebit_sum_server_kernel(const uint8_t* __restrict__ bits_w,
+                                                                       const float* __restrict__ es, uint64_t n,
+                                                                       const uint32_t* __restrict__ blockmax,
+                                                                       uint64_t nmax,
+                                                                       const zero_step_state_t* __restrict__ st,
+                                                                       zero_onebit_state_t* __restrict__ ob,
+                                                                       NormPartial* __restrict__ ws)
+{
+    if (st->skip)
+        return;
+    sum_and_scale<kServer>(ServerU{bits_w, es, ob->scale_w}, n, blockmax, nmax, st, ob, ws);
+}
+
+// ---- C: worker compression ----------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const float* __restrict__ m32,
+                                                                        float* __restrict__ ew,
+                                                                        const float* __restrict__ es,
+                                                                        uint8_t* __restrict__ bits_w, uint64_t n,
+                                                                        const zero_step_state_t* __restrict__ st,
+                                                                        const zero_onebit_state_t* __restrict__ ob,
+                                                                        uint32_t* __restrict__ blockmax)
+{
+    if (st->skip)
+        return;
+    const float sw = ob->scale_w;
+    const uint64_t nvec = n >> 3;
+    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
+    uint32_t mx = 0;
+    if (j < nvec) {
+        const f32x4* mv = reinterpret_cast<const f32x4*>(m32) + 2 * j;
+        f32x4* ev = reinterpret_cast<f32x4*>(ew) + 2 * j;
+        const f32x4* sv = reinterpret_cast<const f32x4*>(es) + 2 * j;
+        const f32x4 m[2] = {mv[0], mv[1]};
+        f32x4 e[2] = {ev[0], ev[1]};
+        const f32x4 s[2] = {__builtin_nontemporal_load(sv), __builtin_nontemporal_load(sv + 1)};
+        uint32_t byte = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float x = m[h][k] + e[h][k];
+                const float cw = sgn_scale(x, sw);
+                byte |= (x < 0.0f ? 0u : 1u) << (4 * h + k);
+                e[h][k] = x - cw;
+                const uint32_t a = abs_bits(cw + s[h][k]);
+                mx = a > mx ? a : mx;
+            }
+        __builtin_nontemporal_store(e[0], ev);
+        __builtin_nontemporal_store(e[1], ev + 1);
+        bits_w[j] = uint8_t(byte);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {     // the ragged last byte
+        uint32_t byte = 0;
+        for (uint64_t i = nvec << 3; i < n; ++i) {
+            const float x = m32[i] + ew[i];
+            const float cw = sgn_scale(x, sw);
+            byte |= (x < 0.0f ? 0u : 1u) << (i & 7);
+            ew[i] = x - cw;
+            const uint32_t a = abs_bits(cw + es[i]);
+            mx = a > mx ? a : mx;
+        }
+        bits_w[nvec] = uint8_t(byte);
+    }
+    mx = block_max<kBlock>(mx);
+    if (threadIdx.x == 0)
+        blockmax[blockIdx.x] = mx;
+}
+
+// ---- E: server compression + update ----------------------------------------------------
+
+__device__ __forceinline__ void update(float m, float& p, float v, const Coef& c)
+{
+#pragma clang fp contract(off)
+    const float u = m / (__builtin_sqrtf(v) + c.eps) + c.wd * p;
+    p = p - c.lr * u;
+}
+
+__global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restrict__ p16, float* __restrict__ p32,
+                                                               float* __restrict__ m32, const float* __restrict__ v32,
+                                                               float* __restrict__ es,
+                                                               const uint8_t* __restrict__ bits_w,
+                                                               uint8_t* __restrict__ bits_s, uint64_t n,
+                                                               const zero_step_state_t* __restrict__ st,
+                                                               const zero_onebit_state_t* __restrict__ ob)
+{
+    extern __shared__ char occupancy_reserve[];
+    if (st->skip) {
+        if (n == UINT64_MAX)
+            occupancy_reserve[threadIdx.x] = 0;
+        return;
+    }
+    const Coef c = coef_of(st);
+    const float sw = ob->scale_w, ss = ob->scale_s;
+    const uint64_t nvec = n >> 3;
+    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (j < nvec) {
+        const uint32_t bw = bits_w[j];
+        f32x4* sv = reinterpret_cast<f32x4*>(es) + 2 * j;
+        f32x4* pv = reinterpret_cast<f32x4*>(p32) + 2 * j;
+        f32x4* mv = reinterpret_cast<f32x4*>(m32) + 2 * j;
+        const f32x4* vv = reinterpret_cast<const f32x4*>(v32) + 2 * j;
+        f32x4 s[2] = {sv[0], sv[1]};
+        f32x4 p[2] = {pv[0], pv[1]};
+        const f32x4 v[2] = {vv[0], vv[1]};
+        f32x4 m[2];
+        f16x8 h16;
+        uint32_t bs = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = 4 * h + k;
+                const float u = (((bw >> i) & 1) ? sw : -sw) + s[h][k];
+                const float mi = sgn_scale(u, ss);
+                bs |= (u < 0.0f ? 0u : 1u) << i;
+                s[h][k] = u - mi;
+                m[h][k] = mi;
+                float pk = p[h][k];
+                update(mi, pk, v[h][k], c);
+                p[h][k] = pk;
+                h16[i] = _Float16(pk);
+            }
+        __builtin_nontemporal_store(s[0], sv);
+        __builtin_nontemporal_store(s[1], sv + 1);
+        __builtin_nontemporal_store(m[0], mv);
+        __builtin_nontemporal_store(m[1], mv + 1);
+        __builtin_nontemporal_store(p[0], pv);
+        __builtin_nontemporal_store(p[1], pv + 1);
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h16), reinterpret_cast<u32x4*>(p16) + j);
+        bits_s[j] = uint8_t(bs);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {
+        const uint32_t bw = bits_w[nvec];
+        uint32_t bs = 0;
+        for (uint64_t i = nvec << 3; i < n; ++i) {
+            const float u = (((bw >> (i & 7)) & 1) ? sw : -sw) + es[i];
+            const float mi = sgn_scale(u, ss);
+            bs |= (u < 0.0f ? 0u : 1u) << (i & 7);
+            es[i] = u - mi;
+            m32[i] = mi;
+            float p = p32[i];
+            update(mi, p, v32[i], c);
+            p32[i] = p;
+            p16[i] = __builtin_bit_cast(uint16_t, _Float16(p));
+        }
+        bits_s[nvec] = uint8_t(bs);
+    }
+}
+
+__global__ void onebit_state_init_kernel(zero_onebit_state_t* ob)
+{
+    zero_onebit_state_t s;
+    memset(&s, 0, sizeof s);
+    *ob = s;
+}
+
+// Workspace: block maxima of A and C, then the partials of B and D.
+struct Plan {
+    uint64_t grid1;                 // one-shot kernels (A, C, E)
+    uint64_t grid2;                 // sums (B, D)
+    uint64_t off_max_a, off_max_c, off_part_b, off_part_d, bytes;
+};
+
+Plan plan(uint64_t n)
+{
+    Plan p;
+    const uint64_t nvec = n >> 3;
+    p.grid1 = (nvec + kBlock - 1) / kBlock;
+    if (p.grid1 < 1) p.grid1 = 1;
+    // at most 2^11 elements per thread, so the binary64 window sums stay exact
+    p.grid2 = norm_grid(n);
+    const uint64_t per = uint64_t(kNormBlock) * 2048;
+    if ((n + p.grid2 * kNormBlock - 1) / (p.grid2 * kNormBlock) > 2048)
+        p.grid2 = (n + per - 1) / per;
+    auto up = [](uint64_t b) { return (b + 255) / 256 * 256; };
+    p.off_max_a = 0;
+    p.off_max_c = up(p.grid1 * 4);
+    p.off_part_b = p.off_max_c + up(p.grid1 * 4);
+    p.off_part_d = p.off_part_b + up(p.grid2 * sizeof(NormPartial));
+    p.bytes = p.off_part_d + up(p.grid2 * sizeof(NormPartial));
+    return p;
+}
+
+}  // namespace
+}  // namespace zero
+
+using namespace zero;
+
+extern "C" size_t zero_onebit_workspace_bytes(uint64_t n) { return size_t(plan(n).bytes); }
+
+extern "C" int zero_onebit_state_init(zero_onebit_state_t* dev_onebit, void* stream)
+{
+    if (!dev_onebit)
+        return ZERO_EINVAL;
+    if (!is_aligned(dev_onebit, 8))
+        return ZERO_EALIGN;
+    hipLaunchKernelGGL(onebit_state_init_kernel, dim3(1), dim3(1), 0, (hipStream_t)stream, dev_onebit);
+    return launch_status();
+}
+
+extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const float* v32, float* err_w,
+                                float* err_s, const uint16_t* grad16, uint64_t n, uint8_t* bits_w, uint8_t* bits_s,
+                                const zero_step_state_t* dev_state, zero_onebit_state_t* dev_onebit,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!dev_state || !dev_onebit || !workspace ||
+        (n && (!p16 || !p32 || !m32 || !v32 || !err_w || !err_s || !grad16 || !bits_w || !bits_s)))
+        return ZERO_EINVAL;
+    if (!is_aligned(dev_state, 8) || !is_aligned(dev_onebit, 8) || !is_aligned(workspace, 256))
+        return ZERO_EALIGN;
+    if (n && (!is_aligned(p16, 16) || !is_aligned(p32, 16) || !is_aligned(m32, 16) || !is_aligned(v32, 16) ||
+              !is_aligned(err_w, 16) || !is_aligned(err_s, 16) || !is_aligned(grad16, 16)))
+        return ZERO_EALIGN;
+    if (n > kNormMaxElems)
+        return ZERO_ERANGE;
+    const Plan pl = plan(n);
+    if (workspace_bytes < pl.bytes || pl.grid1 > 0x7fffffffull)
+        return ZERO_ERANGE;
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* max_a = reinterpret_cast<uint32_t*>(ws + pl.off_max_a);
+    uint32_t* max_c = reinterpret_cast<uint32_t*>(ws + pl.off_max_c);
+    NormPartial* part_b = reinterpret_cast<NormPartial*>(ws + pl.off_part_b);
+    NormPartial* part_d = reinterpret_cast<NormPartial*>(ws + pl.off_part_d);
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 g1(uint32_t(pl.grid1)), g2(uint32_t(pl.grid2));
+    hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), 0, s, m32, err_w, grad16, n, dev_state, max_a);
+    int rc = launch_status();
+    if (rc != ZERO_OK)
+        return rc;
+    hipLaunchKernelGGL(onebit_sum_worker_kernel, g2, dim3(kNormBlock), 0, s, m32, err_w, n, max_a, pl.grid1,
+                       dev_state, dev_onebit, part_b);
+    if ((rc = launch_status()) != ZERO_OK)
+        return rc;
+    hipLaunchKernelGGL(onebit_compress_worker_kernel, g1, dim3(kBlock), 0, s, m32, err_w, err_s, bits_w, n,
+                       dev_state, dev_onebit, max_c);
+    if ((rc = launch_status()) != ZERO_OK)
+        return rc;
+    hipLaunchKernelGGL(onebit_sum_server_kernel, g2, dim3(kNormBlock), 0, s, bits_w, err_s, n, max_c, pl.grid1,
+                       dev_state, dev_onebit, part_d);
+    if ((rc = launch_status()) != ZERO_OK)
+        return rc;
+    hipLaunchKernelGGL(onebit_update_kernel, g1, dim3(kBlock), lds_reservation(2), s, p16, p32, m32, v32, err_s,
+                       bits_w, bits_s, n, dev_state, dev_onebit);
+    return launch_status();
+}

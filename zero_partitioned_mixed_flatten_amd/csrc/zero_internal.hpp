@@ -16,6 +16,7 @@ static_assert(offsetof(zero_step_state_t, done_blocks) == 104, "state layout");
 static_assert(offsetof(zero_step_state_t, sumsq_units) == 112, "state layout");
 static_assert(sizeof(zero_segment_t) == 32, "segment layout");
 static_assert(sizeof(zero_hparams_t) == 80, "hparams layout");
+static_assert(sizeof(zero_onebit_state_t) == 72, "1-bit state layout");
 
 namespace zero {
 

@@ -214,6 +214,54 @@ class AccumStep:
         return Z.read_state(self.state)
 
 
+class OneBitStep(ShardStep):
+    """1-bit Adam on the shard (the DeepSpeed article; Tang et al. 2021,
+    Algorithm 1): the first `warmup` applied steps are the ordinary fused step,
+    which also builds the variance; after them the variance is frozen and each
+    step runs the compression stage (zero_onebit_step) instead of the Adam
+    update.  The flatten with exact-norm partials and the decision are the same
+    in both stages."""
+
+    def __init__(self, n: int, warmup: int, device="cuda"):
+        import torch
+        super().__init__(n, device=device, fused=True)
+        alloc = max(1, self.n)
+        self.warmup = int(warmup)
+        self.err_w = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.err_s = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        self.bits_w = torch.zeros((alloc + 7) // 8, dtype=torch.uint8, device=self.device)
+        self.bits_s = torch.zeros((alloc + 7) // 8, dtype=torch.uint8, device=self.device)
+        self.onebit = torch.zeros(Z.ONEBIT_STATE_BYTES, dtype=torch.uint8, device=self.device)
+        self.onebit_ws = torch.empty(max(256, Z.zero_onebit_workspace_bytes(self.n)), dtype=torch.uint8,
+                                     device=self.device)
+        self.applied = 0                 # applied steps, counted on the host from the device state
+
+    def init_state(self, initial_scale: float) -> None:
+        super().init_state(initial_scale)
+        Z.zero_onebit_state_init(self.onebit)
+
+    def compressing(self) -> bool:
+        return self.applied >= self.warmup
+
+    def compress(self) -> None:
+        Z.zero_onebit_step(self.p16, self.p32, self.m32, self.v32, self.err_w, self.err_s, self.grad16, self.n,
+                           self.bits_w, self.bits_s, self.state, self.onebit, self.onebit_ws)
+
+    def step(self, hp: Z.HParams) -> None:
+        """One step; reads the applied-step count back (a 128-byte copy) to know
+        when the warm-up ends."""
+        self.flatten_norm()
+        self.decide(hp)
+        if self.compressing():
+            self.compress()
+        else:
+            self.adam()
+        self.applied = int(self.read_state().step)
+
+    def read_onebit(self) -> Z.OneBitState:
+        return Z.read_onebit_state(self.onebit)
+
+
 class HostContext:
     """Owns a zero_host_ctx_t (the host step's worker pool)."""
 
