@@ -47,8 +47,11 @@ NORM_BYTES = 2           # read fp16 g
 FLATTEN_BYTES = 4        # read fp16 source, write fp16 partition
 WIDEN_BYTES = 6          # read fp16 source, write fp32 partition
 ACCUM_BYTES = 10         # read fp16 source and fp32 partition, write fp32 partition
+# 1-bit Adam compression stage, per parameter: momentum 14, worker sum 8, worker
+# compression 16 + 1/8, server sum 4 + 1/8, server compression + update 26 + 1/4
+ONEBIT_BYTES = 14 + 8 + 16.125 + 4.125 + 26.25
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "step_kernels_gpt2_shard_pmc.json")
-ADAM_SOURCE = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc", "adam.hip")
+CSRC = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc")
 
 
 def log(msg):
@@ -61,16 +64,19 @@ def source_hash(path):
 
 
 def measured_traffic(path, n):
-    """HBM bytes per launch of the path's Adam kernel from the committed counter
-    summary, or None when it is missing, for another shard size, for another
-    path, or for another kernel source."""
+    """HBM bytes per step of the path's roofline kernel(s) from the committed
+    counter summary, or None when it is missing, for another shard size, for
+    another path, or taken on other kernel sources."""
     try:
         with open(PMC_SUMMARY) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
-    if s.get("adam_source_sha256_16") != source_hash(ADAM_SOURCE) or s.get("n") != n:
+    if path is None or s.get("n") != n:
         return None
+    for src in s.get("sources_for", {}).get(path, []):
+        if s.get("source_sha256_16", {}).get(src) != source_hash(os.path.join(CSRC, src)):
+            return None
     return s.get("hbm_bytes_per_launch", {}).get(path)
 
 
@@ -209,13 +215,125 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
     print(json.dumps(out), flush=True)
 
 
+def run_onebit(args, w, p32, grads_host, dev_sets, hp):
+    """1-bit Adam: two untimed warm-up steps of the ordinary fused step, then
+    the timed steps of the compression stage (flatten with exact-norm
+    partials, decide, zero_onebit_step).  The roofline object is the whole
+    compression stage (five kernels, 68.5 algorithmic bytes per parameter);
+    rocprofv3 gives the split."""
+    import torch
+    import zero_partitioned_mixed_flatten_amd as Z
+    n = w.n
+    stream = torch.cuda.current_stream()
+    dev = Z.OneBitStep(n, warmup=2)
+    dev.p32.copy_(torch.from_numpy(p32))
+    dev.p16.copy_(dev.p32.half())
+    dev.init_state(w.scale0)
+    plans = []
+    for d in dev_sets:
+        dev.set_segments(d, w.layout.segments, w.bucket_elems)
+        plans.append(dev.buckets)
+    k = 0
+    while not dev.compressing():                      # the warm-up, with its host read-back
+        dev.buckets = plans[k % len(plans)]
+        dev.step(hp)
+        k += 1
+    log(f"onebit: warm-up done after {k} steps; warmup {args.warmup} compression steps")
+
+    def one_step(i, ev=None):
+        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        dev.buckets = plans[i % len(plans)]
+        rec(0)
+        dev.flatten_norm()
+        dev.decide(hp)
+        rec(1)
+        dev.compress()
+        rec(2)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    st = dev.read_state()
+    mean = lambda xs: sum(xs) / len(xs)
+    front_ms = mean([e[0].elapsed_time(e[1]) for e in events])
+    comp_ms = mean([e[1].elapsed_time(e[2]) for e in events])
+    achieved = ONEBIT_BYTES * n / (comp_ms / 1e3) / 1e9
+    ob = dev.read_onebit()
+    log(f"step {1e3 * el / args.steps:.3f} ms; flatten+decide {1e3 * front_ms:.1f} us, compression stage "
+        f"{1e3 * comp_ms:.1f} us ({achieved:.0f} GB/s); scales {ob.scale_w:.4g}/{ob.scale_s:.4g}; "
+        f"skipped={st.skipped_total}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline_onebit(w, p32, grads_host, args.cpu_seconds)
+    out = {
+        "metric": METRIC,
+        "value": n * args.steps / el,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * el / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard, 1-bit Adam "
+                               f"compression stage", "params": n, "path": "onebit", "warmup_steps": 2,
+                   "state": "fp16 p, g + fp32 p, m, v (frozen) + fp32 worker/server errors + 2 x 1 bit",
+                   "step_bytes_per_param": FLATTEN_BYTES + ONEBIT_BYTES},
+        "roofline": {"bound": "hbm", "kernel": "onebit_step (5 kernels)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("onebit", n), "algorithmic_bytes": ONEBIT_BYTES * n},
+        "kernels_us": {"flatten_norm+decide": 1e3 * front_ms, "onebit_step": 1e3 * comp_ms},
+        "scales": {"worker": ob.scale_w, "server": ob.scale_s},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_onebit(w, p32, grads_host, budget_s):
+    """The oracle's compression-stage steps (after two warm-up steps, untimed)."""
+    import numpy as np
+    import oracle as O
+    import shardgen
+    hp = O.hparams()
+    st = O.new_state(w.scale0)
+    p = p32.copy()
+    m, v, ew, es = (np.zeros_like(p) for _ in range(4))
+    p16 = shardgen.to_f16_bits(p)
+    grad = np.empty(w.n, np.uint16)
+    for k in range(2):
+        O.step(hp, st, grads_host[k % len(grads_host)], w.layout.segments, grad, p16, p, m, v)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        O.flatten(grads_host[steps % len(grads_host)], w.layout.segments, grad)
+        O.decide(st, hp, *O.norm_overflow(grad))
+        O.onebit_step(st, p16, p, m, v, ew, es, grad)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 20:
+            break
+    return {"value": w.n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} compression-stage step(s) of the same {w.n:,}-parameter shard (flatten + exact "
+                      f"norm + decision + 1-bit Adam), single-threaded C, {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2", choices=["tiny", "gpt2", "100b", "1t"])
-    ap.add_argument("--path", default="fused", choices=["fused", "separate", "accum32", "offload"])
+    ap.add_argument("--path", default="fused", choices=["fused", "separate", "accum32", "offload", "onebit"])
     ap.add_argument("--threads", type=int, default=None,
                     help="host workers for --path offload (default: all CPUs but one)")
     ap.add_argument("--chunk", type=int, default=1 << 24, help="elements per transfer chunk for --path offload")
@@ -271,6 +389,9 @@ def main():
     dev_sets = [[torch.from_numpy(s.view(np.float16)).cuda() for s in srcs] for srcs in grads_host]
     if args.path == "offload":
         run_offload(args, w, p32, grads_host, dev_sets, hp)
+        return
+    if args.path == "onebit":
+        run_onebit(args, w, p32, grads_host, dev_sets, hp)
         return
     accum = args.path == "accum32"
     fused = args.path in ("fused", "accum32")
