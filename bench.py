@@ -341,6 +341,8 @@ def main():
                     help="--path offload: who reduces and decides (bit-identical either way)")
     ap.add_argument("--micro-batches", type=int, default=4,
                     help="micro-batches per optimizer step for --path accum32")
+    ap.add_argument("--graph", action="store_true",
+                    help="fused/separate paths: replay each step as a captured HIP graph (one per gradient set)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
@@ -441,9 +443,31 @@ def main():
         dev.adam()
         rec(nev - 1)
 
+    graphs = None
+    if args.graph and not accum:
+        # one graph per gradient set, each capturing flatten(+partials), decide/norm and Adam;
+        # the per-kernel split is timed afterwards on eager steps
+        one_step(0)
+        torch.cuda.synchronize()
+        graphs = []
+        side = torch.cuda.Stream()
+        for k in range(nsets):
+            g = torch.cuda.CUDAGraph()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    one_step(k)
+            torch.cuda.current_stream().wait_stream(side)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        log(f"captured {len(graphs)} step graphs")
+
     log(f"warmup {args.warmup} steps")
     for k in range(args.warmup):
-        one_step(k)
+        if graphs:
+            graphs[k % nsets].replay()
+        else:
+            one_step(k)
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
@@ -451,12 +475,19 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        one_step(args.warmup + k, events[k])
+        if graphs:
+            graphs[(args.warmup + k) % nsets].replay()
+        else:
+            one_step(args.warmup + k, events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     el = t1 - t0
     st = dev.read_state()
     mean = lambda xs: sum(xs) / len(xs)
+    if graphs:                     # the split, from eager steps after the timed replays
+        for k in range(args.steps):
+            one_step(k, events[k])
+        torch.cuda.synchronize()
     seg_ms = [mean([e[i].elapsed_time(e[i + 1]) for e in events]) for i in range(nev - 1)]
     adam_s = seg_ms[-1] / 1e3
     adam_bpp = ADAM32_BYTES if accum else ADAM_BYTES
@@ -528,7 +559,8 @@ def main():
                    "params": n, "segments": len(w.layout.segments), "bucket_elems": w.bucket_elems,
                    "state": "fp16 p,g + fp32 p,m,v (16 B/param)" if not accum else
                             "fp16 p + fp32 g,p,m,v (18 B/param)", "loss_scale0": w.scale0,
-                   "path": args.path, "micro_batches": K, "step_bytes_per_param": step_bpp},
+                   "path": args.path, "micro_batches": K, "step_bytes_per_param": step_bpp,
+                   "hip_graph": bool(graphs)},
         "roofline": {"bound": "hbm", "kernel": names[-1], "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": adam_bpp * n},

@@ -53,10 +53,15 @@ __global__ void state_init_kernel(zero_step_state_t* st, double scale)
 
 uint64_t decide_grid(uint64_t count)
 {
-    // Four partials per thread at least, at most one workgroup per CU.
-    const uint64_t per_block = uint64_t(kNormBlock) * 4;
+    // Up to 2^15 partials (1 MiB, L2-resident after the flatten) one workgroup
+    // folds faster than several that must meet at an agent-scope arrival
+    // counter; beyond that, at least 32 partials per thread and at most one
+    // workgroup per CU.
+    if (count <= (uint64_t(1) << 15))
+        return 1;
+    const uint64_t per_block = uint64_t(kNormBlock) * 32;
     uint64_t g = (count + per_block - 1) / per_block;
-    if (g < 1) g = 1;
+    if (g < 2) g = 2;
     if (g > kNormMaxBlocks) g = kNormMaxBlocks;
     return g;
 }

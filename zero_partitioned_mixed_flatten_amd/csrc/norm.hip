@@ -20,7 +20,9 @@
 //                         flight; about 8 VALU operations per fp16 element,
 //                         about 12 binary64 operations per fp32 element;
 //   decide_kernel         folds the per-workgroup partials a fused flatten
-//                         (flatten.hip) already computed while copying.
+//                         (flatten.hip) already computed while copying; up
+//                         to 2^15 partials in a single workgroup, which then
+//                         decides without an arrival counter or fence.
 // In both, every workgroup stores its carried partial, bumps an agent-scope
 // acq_rel arrival counter once, and the last one to arrive folds all
 // partials, takes the decision in binary64 on one thread, writes it into the
@@ -40,6 +42,14 @@ using exact::Limbs;
 __device__ __forceinline__ void publish_and_decide(Limbs s, uint32_t flag, zero_step_state_t* st,
                                                    NormPartial* ws, const DecideArgs& d)
 {
+    if (gridDim.x == 1) {          // one workgroup holds the whole sum: no arrival counter, no fence
+        if (threadIdx.x == 0) {
+            uint64_t hi, lo;
+            const bool fits = exact::limbs_to_u128(s, hi, lo);
+            decide_state(st, d, hi, lo, !fits || (flag & exact::kOverflowBits) != 0);
+        }
+        return;
+    }
     __shared__ uint32_t s_last;
     if (threadIdx.x == 0) {
         ws[blockIdx.x] = exact::make_partial(s, flag);
@@ -127,7 +137,15 @@ __global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* _
     Limbs s{0, 0, 0, 0};
     uint32_t flag = 0;
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-    for (uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x; i < count; i += stride)
+    uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
+    for (; i + 3 * stride < count; i += 4 * stride) {          // four partials' loads in flight
+        const NormPartial a = in[i], b = in[i + stride], c = in[i + 2 * stride], e = in[i + 3 * stride];
+        exact::fold_partial(s, flag, a);
+        exact::fold_partial(s, flag, b);
+        exact::fold_partial(s, flag, c);
+        exact::fold_partial(s, flag, e);
+    }
+    for (; i < count; i += stride)
         exact::fold_partial(s, flag, in[i]);
     exact::block_fold<kNormBlock>(s, flag);
     publish_and_decide(s, flag, st, ws, d);

@@ -14,9 +14,10 @@
 //
 // Five kernels, because two global scales sit on the data path:
 //   A  momentum + per-block max|x|           one-shot, 8 elements per thread
-//   B  exact sum of x^2 in the window, s_w   <= 256 workgroups x 1024, grid-stride;
-//      every workgroup first folds A's block maxima (L2-resident), the last
-//      one to arrive folds the limbs and writes s_w
+//   B  exact sum of x^2 in the window, s_w   <= 256 workgroups x 1024, grid-stride
+//      with four vectors' loads in flight; every workgroup first folds A's
+//      block maxima (L2-resident), the last one to arrive folds the limbs and
+//      writes s_w
 //   C  worker compression: sign byte, ew, u = cw + es, per-block max|u|
 //   D  exact sum of u^2, s_s                  as B (u is recomputed from the bits)
 //   E  server compression + update: m, es, bits, p, p16
@@ -196,9 +197,20 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
                               const zero_step_state_t* __restrict__ st, zero_onebit_state_t* __restrict__ ob,
                               NormPartial* __restrict__ ws)
 {
-    // the window: max over the previous kernel's block maxima
+    // the window: max over the previous kernel's block maxima (L2-resident;
+    // eight loads in flight per thread, or the fold is a chain of latencies)
     uint32_t mx = 0;
-    for (uint64_t b = threadIdx.x; b < nmax; b += kNormBlock)
+    uint64_t b = threadIdx.x;
+    for (; b + 7 * kNormBlock < nmax; b += 8 * kNormBlock) {
+        uint32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = blockmax[b + q * kNormBlock];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            mx = v[q] > mx ? v[q] : mx;
+    }
+    for (; b < nmax; b += kNormBlock)
         mx = blockmax[b] > mx ? blockmax[b] : mx;
     __shared__ uint32_t s_mx;
     mx = block_max<kNormBlock>(mx);
@@ -213,7 +225,19 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
     if (mx) {
         const uint64_t nvec = n >> 3;
         const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-        for (uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x; j < nvec; j += stride) {
+        uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
+        for (; j + 3 * stride < nvec; j += 4 * stride) {      // four vectors' loads in flight
+            float x[4][8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                vsrc.vec(j + q * stride, x[q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    acc.add(x[q][k], w);
+        }
+        for (; j < nvec; j += stride) {
             float x[8];
             vsrc.vec(j, x);
 #pragma unroll
