@@ -239,3 +239,41 @@ def test_host_validation(Z, ctxs):
     assert L.zero_offload_step(ctxs[1].ptr, f, f, f, f, f, f, f, 100, None, sp, f + 4, 64,
                                None) == E.ZERO_EALIGN             # misaligned device state
     assert Z.zero_status_string(E.ZERO_ENOTSUP) and Z.zero_status_string(E.ZERO_ENOMEM)
+
+
+# ---- randomized: any size, alignment, worker count, gradient pattern and hyperparameters ----
+
+from hypothesis import HealthCheck, given, settings, strategies as hs  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(n=hs.integers(0, 3000), off=hs.integers(0, 31), threads=hs.sampled_from([1, 3, 8]),
+       seed=hs.integers(0, 2 ** 32 - 1), special=hs.sampled_from([None, 0x7C00, 0xFE00, 0x7BFF, 0x0001]),
+       lr=hs.floats(0.0, 1e-2), b1=hs.floats(0.0, 0.999), b2=hs.floats(0.0, 0.9999),
+       wd=hs.floats(0.0, 0.1), clip=hs.sampled_from([0.0, 1e-3, 1.0]), scale_exp=hs.integers(0, 24))
+def test_host_step_random_against_oracle(Z, ctxs, n, off, threads, seed, special, lr, b1, b2, wd, clip, scale_exp):
+    import oracle as O
+    rng = np.random.default_rng(seed)
+    S = 2.0 ** scale_exp
+    g = shardgen.to_f16_bits((rng.standard_normal(n) * rng.choice([1e-3, 1.0, 100.0])).astype(np.float32))
+    if special is not None and n:
+        g[int(rng.integers(n))] = special
+    p32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v32 = (np.abs(rng.standard_normal(n)) * 1e-6).astype(np.float32)
+    host = [_offset_view(a, off) for a in (shardgen.to_f16_bits(p32), p32, m32, v32)]
+    orc = [shardgen.to_f16_bits(p32), p32.copy(), m32.copy(), v32.copy()]
+    gv = _offset_view(g, off)
+    hp = Z.hparams(lr=lr, beta1=b1, beta2=b2, weight_decay=wd, max_grad_norm=clip)
+    hpo = O.hparams(lr=lr, beta1=b1, beta2=b2, weight_decay=wd, max_grad_norm=clip)
+    st = Z.StepState()
+    Z.zero_host_state_init(st, S)
+    ref = O.new_state(S)
+    Z.zero_host_norm_overflow(ctxs[threads].ptr, gv, n, hp, st)
+    Z.zero_host_adam_step(ctxs[threads].ptr, *host, gv, n, st)
+    s, o = O.norm_overflow(g)
+    O.decide(ref, hpo, s, o)
+    O.adam_update(ref, *orc, g)
+    _state_equal(st, ref)
+    for a, b in zip(host, orc):
+        assert a.tobytes() == b.tobytes()
