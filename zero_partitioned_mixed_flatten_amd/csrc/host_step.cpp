@@ -243,9 +243,8 @@ ZERO_HOST_ISA void adam_range(uint16_t* p16, float* p32, float* m32, float* v32,
     uint64_t i = a;
     // masked elements up to the first index where every stream is 64-byte aligned
     // (the fp16 copy then is 32-byte aligned), if the arrays share that phase
-    uint64_t body = a;
-    while (body < b && (reinterpret_cast<uintptr_t>(p32 + body) & 63))
-        ++body;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(p32 + a);
+    const uint64_t body = (pa & 3) ? b : a + ((64 - (pa & 63)) & 63) / 4;
     const bool nt = body < b && !(reinterpret_cast<uintptr_t>(m32 + body) & 63) &&
                     !(reinterpret_cast<uintptr_t>(v32 + body) & 63) &&
                     !(reinterpret_cast<uintptr_t>(p16 + body) & 31);
