@@ -80,6 +80,33 @@ def measured_traffic(path, n):
     return s.get("hbm_bytes_per_launch", {}).get(path)
 
 
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+class one_core:
+    """Run the oracle pinned to one core (the process's first allowed CPU),
+    then restore the affinity."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(self.saved)})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+        return False
+
+
 def cpu_baseline(w, p32, grads_host, budget_s, micro=0):
     """The oracle on whole steps of the same shard until budget_s has passed
     (at most 20 steps).  micro > 0: the gradient-accumulation step over that
@@ -110,9 +137,14 @@ def cpu_baseline(w, p32, grads_host, budget_s, micro=0):
             break
     what = (f"{micro} fp16 micro-batches accumulated in fp32 + exact fp32 norm + decision + fp32 AdamW + "
             f"fp16 copy" if micro else "flatten + exact norm + decision + fp32 AdamW + fp16 copy")
+    bpp = (WIDEN_BYTES + ACCUM_BYTES * (micro - 1) + ADAM32_BYTES) if micro else (FLATTEN_BYTES + NORM_BYTES +
+                                                                                   ADAM_BYTES)
+    model, ncpu = cpu_info()
     return {"value": w.n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "gbps": bpp * w.n * steps / el / 1e9, "bytes_per_param": bpp, "cpu_model": model,
+            "cpus_available": ncpu,
             "sample": f"{steps} full step(s) of the same {w.n:,}-parameter shard ({what}), "
-                      f"single-threaded C, {el:.1f} s"}
+                      f"single-threaded C pinned to one core, {el:.1f} s"}
 
 
 def run_offload(args, w, p32, grads_host, dev_sets, hp):
@@ -184,7 +216,8 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds)
+        with one_core():
+            cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds)
     out = {
         "metric": METRIC,
         "value": n * args.steps / el,
@@ -272,7 +305,8 @@ def run_onebit(args, w, p32, grads_host, dev_sets, hp):
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline_onebit(w, p32, grads_host, args.cpu_seconds)
+        with one_core():
+            cpu = cpu_baseline_onebit(w, p32, grads_host, args.cpu_seconds)
     out = {
         "metric": METRIC,
         "value": n * args.steps / el,
@@ -322,9 +356,11 @@ def cpu_baseline_onebit(w, p32, grads_host, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 20:
             break
+    model, ncpu = cpu_info()
     return {"value": w.n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "cpu_model": model, "cpus_available": ncpu,
             "sample": f"{steps} compression-stage step(s) of the same {w.n:,}-parameter shard (flatten + exact "
-                      f"norm + decision + 1-bit Adam), single-threaded C, {el:.1f} s"}
+                      f"norm + decision + 1-bit Adam), single-threaded C pinned to one core, {el:.1f} s"}
 
 
 def main():
@@ -488,7 +524,11 @@ def main():
         for k in range(args.steps):
             one_step(k, events[k])
         torch.cuda.synchronize()
-    seg_ms = [mean([e[i].elapsed_time(e[i + 1]) for e in events]) for i in range(nev - 1)]
+    seg_all = [[e[i].elapsed_time(e[i + 1]) for e in events] for i in range(nev - 1)]
+    seg_ms = [mean(x) for x in seg_all]
+    median = lambda xs: sorted(xs)[len(xs) // 2]
+    seg_med = [median(x) for x in seg_all]
+    step_med_ms = median([e[0].elapsed_time(e[nev - 1]) for e in events])
     adam_s = seg_ms[-1] / 1e3
     adam_bpp = ADAM32_BYTES if accum else ADAM_BYTES
     achieved = adam_bpp * n / adam_s / 1e9
@@ -500,10 +540,12 @@ def main():
         names = ["flatten_norm" if fused else "flatten", "decide" if fused else "norm_overflow", "adam_step"]
         flat_bpp = [FLATTEN_BYTES]
     kernels_us = {}
+    kernels_us_median = {}
     kernels_gbps = {}
     for i, name in enumerate(names):
         key = name if name not in kernels_us else f"{name}_{i}"
         kernels_us[key] = 1e3 * seg_ms[i]
+        kernels_us_median[key] = 1e3 * seg_med[i]
         if i < len(flat_bpp):
             kernels_gbps[key] = flat_bpp[i] * n / (seg_ms[i] / 1e3) / 1e9
     if not fused:
@@ -531,7 +573,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds, K if accum else 0)
+        with one_core():
+            cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds, K if accum else 0)
 
     traffic = measured_traffic(args.path if (not accum or K == 4) else None, n)
     if accum:
@@ -565,8 +608,12 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": adam_bpp * n},
         "step_gbps": step_bytes / (el / args.steps) / 1e9,
+        "step_frac": step_bytes / (el / args.steps) / 1e9 / HBM_PEAK_GBPS,
+        "step_ms_median_events": step_med_ms,
         "kernels_us": kernels_us,
+        "kernels_us_median": kernels_us_median,
         "kernels_gbps": kernels_gbps,
+        "kernels_frac": {k: v / HBM_PEAK_GBPS for k, v in kernels_gbps.items()},
         "copy_reference_gbps": copy_gbps,
         "cpu_baseline": cpu,
     }

@@ -57,3 +57,17 @@ def test_injection_and_sentinel():
     t = shardgen.source_tensors(small, np.arange(4, dtype=np.uint16))
     assert list(t[0]) == [0x7E00] * 3 + [0, 1, 2, 3] + [0x7E00] * 3
     assert L.n > 0
+
+
+def test_stress_injections_are_the_only_non_finite_values_full_shard():
+    """On the full 97M-element stress shard at S = 2^24 (sigma 1e-4: 65520 is 39
+    sigma away), the injected +inf (step 3) and NaN (step 7) are the only
+    non-finite fp16 values, and a clean step has none."""
+    w = shardgen.workload("stress")
+    for step, bits in ((3, 0x7C00), (7, 0x7E00), (4, None)):
+        g = shardgen.grad_partition(w, step, w.scale0)
+        bad = np.flatnonzero((g & 0x7C00) == 0x7C00)
+        if bits is None:
+            assert bad.size == 0
+        else:
+            assert bad.tolist() == [shardgen.injection_position(w, step)] and g[bad[0]] == bits
