@@ -80,6 +80,9 @@ def measured_traffic(path, n):
     return s.get("hbm_bytes_per_launch", {}).get(path)
 
 
+CPUS_AVAILABLE = None          # set before the oracle is pinned to one core
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -90,7 +93,7 @@ def cpu_info():
                     break
     except OSError:
         pass
-    return model, len(os.sched_getaffinity(0))
+    return model, CPUS_AVAILABLE or len(os.sched_getaffinity(0))
 
 
 class one_core:
@@ -99,6 +102,8 @@ class one_core:
 
     def __enter__(self):
         self.saved = os.sched_getaffinity(0)
+        global CPUS_AVAILABLE
+        CPUS_AVAILABLE = len(self.saved)
         os.sched_setaffinity(0, {min(self.saved)})
         return self
 
