@@ -15,10 +15,14 @@
 // MFMA.  The gradient-accumulation form reads an fp32 gradient instead
 // (30 bytes per parameter) and is otherwise the same kernel.
 // Shape, chosen by measurement on MI355X:
-//   * one-shot grid: each thread owns 8 consecutive parameters (one 16-byte
-//     load of an fp16 g or two of an fp32 g, two each of p, m, v; the
-//     matching stores), so the wave front of resident workgroups sweeps
-//     memory once, in order;
+//   * one-shot grid: each workgroup owns 2048 consecutive parameters and each
+//     thread two groups of 4 of them, 1024 apart (an 8-byte load of fp16 g or
+//     a 16-byte load of fp32 g, and a 16-byte load of each of p, m, v, per
+//     group; the matching stores), so every load and store instruction of a
+//     wave covers one contiguous span and the wave front of resident
+//     workgroups sweeps memory once, in order (giving each thread 8 adjacent
+//     parameters instead, with two 16-byte accesses 32 bytes apart across the
+//     lanes, was about 1% slower);
 //   * plain loads of p, m, v, nontemporal loads of the gradient (read once)
 //     and nontemporal stores (nothing written here is read again by this
 //     kernel);
@@ -55,23 +59,30 @@ __device__ __forceinline__ void update(float gh, float& p, float& m, float& v, c
     v = vn;
 }
 
-// Eight gradient values of one thread, widened to fp32 (exact for fp16).  The
-// gradient is read once and never again this step: nontemporal loads (worth
-// about 2% of the kernel; the same hint on p, m, v costs 3%).
-__device__ __forceinline__ void load_grad8(const uint16_t* g, uint64_t j, float (&out)[8])
+// Gradient group j (parameters 4j..4j+3), widened to fp32 (exact for fp16).
+// The gradient is read once and never again this step: nontemporal loads
+// (worth about 2% of the kernel; the same hint on p, m, v costs 3%).
+__device__ __forceinline__ void load_grad4(const uint16_t* g, uint64_t j, float* out)
 {
-    const f16x8 h = __builtin_bit_cast(f16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g) + j));
+    const f16x4 h = __builtin_bit_cast(f16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g) + j));
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < 4; ++k)
         out[k] = float(h[k]);
 }
 
-__device__ __forceinline__ void load_grad8(const float* g, uint64_t j, float (&out)[8])
+__device__ __forceinline__ void load_grad4(const float* g, uint64_t j, float* out)
 {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + 2 * j);
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + 2 * j + 1);
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + j);
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+__device__ __forceinline__ u32x2 to_f16x4(const float* p)
+{
+    f16x4 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        h[k] = _Float16(p[k]);                    // round to nearest even
+    return __builtin_bit_cast(u32x2, h);
 }
 
 __device__ __forceinline__ float grad_at(const uint16_t* g, uint64_t i) { return float(__builtin_bit_cast(_Float16, g[i])); }
@@ -104,36 +115,56 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
     c.wd = st->wd;
     c.lr = st->lr;
 
-    const uint64_t nvec = n >> 3;
-    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
-    if (j < nvec) {
-        f32x4* __restrict__ pv = reinterpret_cast<f32x4*>(p32) + 2 * j;
-        f32x4* __restrict__ mv = reinterpret_cast<f32x4*>(m32) + 2 * j;
-        f32x4* __restrict__ vv = reinterpret_cast<f32x4*>(v32) + 2 * j;
+    // groups of 4 parameters: this thread's are ja and jb = ja + kBlock
+    const uint64_t ng = n >> 2;
+    const uint64_t ja = uint64_t(blockIdx.x) * (2 * kBlock) + threadIdx.x;
+    const uint64_t jb = ja + kBlock;
+    f32x4* __restrict__ P = reinterpret_cast<f32x4*>(p32);
+    f32x4* __restrict__ M = reinterpret_cast<f32x4*>(m32);
+    f32x4* __restrict__ V = reinterpret_cast<f32x4*>(v32);
+    u32x2* __restrict__ H = reinterpret_cast<u32x2*>(p16);
+    if (jb < ng) {                                // both groups: all loads first
         float g[8];
-        load_grad8(grad, j, g);
-        const f32x4 pa = pv[0], pb = pv[1], ma = mv[0], mb = mv[1], va = vv[0], vb = vv[1];
+        load_grad4(grad, ja, g);
+        load_grad4(grad, jb, g + 4);
+        const f32x4 pa = P[ja], pb = P[jb], ma = M[ja], mb = M[jb], va = V[ja], vb = V[jb];
         float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
         float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
         float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-        f16x8 h;
+        // Keep the scheduler from sinking loads below arithmetic: with all
+        // eight in flight before the first wait the kernel runs about 1%
+        // faster than when it defers the two v loads.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 8; ++k)
             update(g[k], p[k], m[k], v[k], c);
-            h[k] = _Float16(p[k]);                // round to nearest even
-        }
-        __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, pv);
-        __builtin_nontemporal_store(f32x4{p[4], p[5], p[6], p[7]}, pv + 1);
-        __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, mv);
-        __builtin_nontemporal_store(f32x4{m[4], m[5], m[6], m[7]}, mv + 1);
-        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, vv);
-        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, vv + 1);
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(p16) + j);
+        __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, P + ja);
+        __builtin_nontemporal_store(f32x4{p[4], p[5], p[6], p[7]}, P + jb);
+        __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, M + ja);
+        __builtin_nontemporal_store(f32x4{m[4], m[5], m[6], m[7]}, M + jb);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, V + ja);
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, V + jb);
+        __builtin_nontemporal_store(to_f16x4(p), H + ja);
+        __builtin_nontemporal_store(to_f16x4(p + 4), H + jb);
+    } else if (ja < ng) {                         // the last workgroup: group ja only
+        float g[4];
+        load_grad4(grad, ja, g);
+        const f32x4 pa = P[ja], ma = M[ja], va = V[ja];
+        float p[4] = {pa.x, pa.y, pa.z, pa.w};
+        float m[4] = {ma.x, ma.y, ma.z, ma.w};
+        float v[4] = {va.x, va.y, va.z, va.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            update(g[k], p[k], m[k], v[k], c);
+        P[ja] = f32x4{p[0], p[1], p[2], p[3]};
+        M[ja] = f32x4{m[0], m[1], m[2], m[3]};
+        V[ja] = f32x4{v[0], v[1], v[2], v[3]};
+        H[ja] = to_f16x4(p);
     }
 
-    // the last n % 8 parameters, one per thread of the first workgroup
-    if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
-        const uint64_t i = (nvec << 3) + threadIdx.x;
+    // the last n % 4 parameters, one per thread of the first workgroup
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        const uint64_t i = (ng << 2) + threadIdx.x;
         float p = p32[i], m = m32[i], v = v32[i];
         update(grad_at(grad, i), p, m, v, c);
         p32[i] = p;
@@ -156,8 +187,8 @@ int adam_step(uint16_t* p16, float* p32, float* m32, float* v32, const G* grad, 
     if (!is_aligned(p16, 16) || !is_aligned(p32, 16) || !is_aligned(m32, 16) || !is_aligned(v32, 16) ||
         !is_aligned(grad, 16))
         return ZERO_EALIGN;
-    const uint64_t nvec = n >> 3;
-    uint64_t grid = (nvec + kBlock - 1) / kBlock;
+    const uint64_t ng = n >> 2;
+    uint64_t grid = (ng + 2 * kBlock - 1) / (2 * kBlock);
     if (grid < 1) grid = 1;
     if (grid > 0x7fffffffull)
         return ZERO_ERANGE;

@@ -97,16 +97,37 @@ __device__ __forceinline__ void store(V v, V* d)
         *d = v;
 }
 
+// What an accumulating mode reads back from the destination for the 8
+// elements at index i (a multiple of 8): one fp16 vector or two fp32 vectors.
+struct Old {
+    u32x4 a, b;
+};
+
+template <int MODE>
+__device__ __forceinline__ Old load_old(const void* dst, uint64_t i)
+{
+    Old o{};
+    if constexpr (MODE == kAcc16) {
+        o.a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(dst) + i);
+    } else if constexpr (MODE == kAcc32) {
+        const u32x4* d = reinterpret_cast<const u32x4*>(static_cast<const float*>(dst) + i);
+        o.a = d[0];
+        o.b = d[1];
+    }
+    return o;
+}
+
 // Stores 8 elements at dst index i (a multiple of 8), nontemporally in the
-// fused form, which also accumulates the values stored.
+// fused form, which also accumulates the values stored; the accumulating
+// modes add the old destination values o (from load_old).
 template <int MODE, bool NORM>
-__device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s, AccOf<MODE>& acc)
+__device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s, Old o, AccOf<MODE>& acc)
 {
     if constexpr (MODE == kCopy16 || MODE == kAcc16) {
         u32x4* d = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i);
         u32x4 r = s;
         if (MODE == kAcc16)
-            r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, *d) + __builtin_bit_cast(f16x8, s));
+            r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, o.a) + __builtin_bit_cast(f16x8, s));
         store<NORM>(r, d);
         if (NORM)
             acc.vec(r);
@@ -116,8 +137,8 @@ __device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s, AccOf
         f32x4 lo = {float(h[0]), float(h[1]), float(h[2]), float(h[3])};
         f32x4 hi = {float(h[4]), float(h[5]), float(h[6]), float(h[7])};
         if (MODE == kAcc32) {
-            lo = d[0] + lo;
-            hi = d[1] + hi;
+            lo = __builtin_bit_cast(f32x4, o.a) + lo;
+            hi = __builtin_bit_cast(f32x4, o.b) + hi;
         }
         store<NORM>(lo, d);
         store<NORM>(hi, d + 1);
@@ -155,7 +176,24 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     const uint64_t v1 = v0 + kVecsPerBlock < nv ? v0 + kVecsPerBlock : nv;
     const uint16_t* __restrict__ sbody = src + head;
     const uint64_t dbody = doff + head;
-    if (vec_src) {
+    if (vec_src && v1 - v0 == kVecsPerBlock) {
+        // A full workgroup (all but a segment's last): no per-lane guards, so
+        // every load is issued before the first wait.  Under per-lane guards
+        // the compiler moves each load into its store's guarded block and
+        // waits for it there, one load in flight per thread.
+        u32x4 r[kVecsPerThread];
+        Old o[kVecsPerThread];
+#pragma unroll
+        for (int k = 0; k < kVecsPerThread; ++k) {
+            const uint64_t v = v0 + threadIdx.x + k * kBlock;
+            r[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbody) + v);
+            o[k] = load_old<MODE>(dst, dbody + 8 * v);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kVecsPerThread; ++k)
+            put_vector<MODE, NORM>(dst, dbody + 8 * (v0 + threadIdx.x + k * kBlock), r[k], o[k], acc);
+    } else if (vec_src) {
         u32x4 r[kVecsPerThread];
 #pragma unroll
         for (int k = 0; k < kVecsPerThread; ++k) {
@@ -167,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
         for (int k = 0; k < kVecsPerThread; ++k) {
             const uint64_t v = v0 + threadIdx.x + uint64_t(k) * kBlock;
             if (v < v1)
-                put_vector<MODE, NORM>(dst, dbody + 8 * v, r[k], acc);
+                put_vector<MODE, NORM>(dst, dbody + 8 * v, r[k], load_old<MODE>(dst, dbody + 8 * v), acc);
         }
     } else {
         for (uint64_t v = v0 + threadIdx.x; v < v1; v += kBlock) {
@@ -177,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
             r.y = uint32_t(s[2]) | (uint32_t(s[3]) << 16);
             r.z = uint32_t(s[4]) | (uint32_t(s[5]) << 16);
             r.w = uint32_t(s[6]) | (uint32_t(s[7]) << 16);
-            put_vector<MODE, NORM>(dst, dbody + 8 * v, r, acc);
+            put_vector<MODE, NORM>(dst, dbody + 8 * v, r, load_old<MODE>(dst, dbody + 8 * v), acc);
         }
     }
 
