@@ -22,6 +22,13 @@
 //   D  exact sum of u^2, s_s                  as B (u is recomputed from the bits)
 //   E  server compression + update: m, es, bits, p, p16
 // Per-block maxima go to memory (no same-address atomics, which serialise).
+// Element layout of the one-shot kernels: the whole bytes of the sign payload
+// cover groups of 4 elements, g < 2*floor(n/8); thread t of workgroup b owns
+// groups 512b+t and 512b+t+256, so every vector load and store of a wave is
+// one contiguous span.  A thread's 4 sign bits of a group are a nibble; the
+// two lanes of an even/odd pair hold the two nibbles of one byte and join
+// them with a lane shuffle.  The elements past the last whole byte (fewer
+// than 8) are done one by one.
 // The exact windowed square: z = x * 2^(40-E) (exact, |z| < 2^41),
 //   a = fma(z, z, C1) - C1       z^2 to a multiple of 2^41 (C1 = 1.5*2^93)
 //   b = (fma(z, z, -a) + C2) - C2   the rest, to the nearest integer (C2 = 1.5*2^52)
@@ -100,7 +107,48 @@ struct AccWin {
     }
 };
 
+// The two groups of 4 elements a thread of a one-shot kernel owns (see the
+// layout note above), out of ng = 2*floor(n/8); ragged0 = 4*ng is the first
+// element done one by one.
+struct Groups {
+    uint64_t ng, ja, jb, ragged0;
+    __device__ explicit Groups(uint64_t n)
+        : ng((n >> 3) * 2), ja(uint64_t(blockIdx.x) * (2 * kBlock) + threadIdx.x), jb(ja + kBlock),
+          ragged0((n >> 3) * 8)
+    {
+    }
+    __device__ bool both() const { return jb < ng; }
+    __device__ bool first() const { return ja < ng; }
+};
+
+// Joins the sign nibbles of an even/odd lane pair into the byte of group j
+// (j even on the even lane); the even lane stores it.  Called by all lanes.
+__device__ __forceinline__ void store_byte_pair(uint8_t* bits, uint64_t j, uint32_t nib, bool valid)
+{
+    const uint32_t other = uint32_t(__shfl_xor(int(nib), 1, 64));
+    if (valid && (threadIdx.x & 1) == 0)
+        bits[j >> 1] = uint8_t(nib | (other << 4));
+}
+
+// The sign nibble of group j from a byte payload.
+__device__ __forceinline__ uint32_t nibble_of(const uint8_t* bits, uint64_t j)
+{
+    return (uint32_t(bits[j >> 1]) >> (4 * (j & 1))) & 15u;
+}
+
 // ---- A: momentum + block max of |m + ew| ----------------------------------------
+
+__device__ __forceinline__ void momentum4(f16x4 g, f32x4& m, f32x4 e, const Coef& c, uint32_t& mx)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma clang fp contract(off)
+        const float gk = float(g[k]) * c.gmul;
+        m[k] = c.b1 * m[k] + c.omb1 * gk;
+        const uint32_t a = abs_bits(m[k] + e[k]);
+        mx = a > mx ? a : mx;
+    }
+}
 
 __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restrict__ m32, const float* __restrict__ ew,
                                                                  const uint16_t* __restrict__ g16, uint64_t n,
@@ -110,31 +158,28 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
     if (st->skip)
         return;
     const Coef c = coef_of(st);
-    const uint64_t nvec = n >> 3;
-    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
+    const Groups gr(n);
+    f32x4* __restrict__ M = reinterpret_cast<f32x4*>(m32);
+    const f32x4* __restrict__ EW = reinterpret_cast<const f32x4*>(ew);
+    const u32x2* __restrict__ G = reinterpret_cast<const u32x2*>(g16);
     uint32_t mx = 0;
-    if (j < nvec) {
-        const f16x8 g = __builtin_bit_cast(f16x8, reinterpret_cast<const u32x4*>(g16)[j]);
-        f32x4* mv = reinterpret_cast<f32x4*>(m32) + 2 * j;
-        const f32x4* ev = reinterpret_cast<const f32x4*>(ew) + 2 * j;
-        f32x4 m[2] = {mv[0], mv[1]};
-        const f32x4 e[2] = {ev[0], ev[1]};
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-#pragma clang fp contract(off)
-                const float gk = float(g[4 * h + k]) * c.gmul;
-                m[h][k] = c.b1 * m[h][k] + c.omb1 * gk;
-                const uint32_t a = abs_bits(m[h][k] + e[h][k]);
-                mx = a > mx ? a : mx;
-            }
-        mv[0] = m[0];
-        mv[1] = m[1];
+    if (gr.both()) {
+        const f16x4 ga = __builtin_bit_cast(f16x4, G[gr.ja]), gb = __builtin_bit_cast(f16x4, G[gr.jb]);
+        f32x4 ma = M[gr.ja], mb = M[gr.jb];
+        const f32x4 ea = EW[gr.ja], eb = EW[gr.jb];
+        __builtin_amdgcn_sched_barrier(0);
+        momentum4(ga, ma, ea, c, mx);
+        momentum4(gb, mb, eb, c, mx);
+        M[gr.ja] = ma;
+        M[gr.jb] = mb;
+    } else if (gr.first()) {
+        f32x4 ma = M[gr.ja];
+        momentum4(__builtin_bit_cast(f16x4, G[gr.ja]), ma, EW[gr.ja], c, mx);
+        M[gr.ja] = ma;
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
 #pragma clang fp contract(off)
-        const uint64_t i = (nvec << 3) + threadIdx.x;
+        const uint64_t i = gr.ragged0 + threadIdx.x;
         const float gk = float(__builtin_bit_cast(_Float16, g16[i])) * c.gmul;
         const float mi = c.b1 * m32[i] + c.omb1 * gk;
         m32[i] = mi;
@@ -153,17 +198,14 @@ struct WorkerX {
     const float* m;
     const float* ew;
     __device__ __forceinline__ float at(uint64_t i) const { return m[i] + ew[i]; }
-    __device__ __forceinline__ void vec(uint64_t j, float (&x)[8]) const
+    // group j: elements 4j..4j+3
+    __device__ __forceinline__ void vec(uint64_t j, float (&x)[4]) const
     {
-        const f32x4* mv = reinterpret_cast<const f32x4*>(m) + 2 * j;
-        const f32x4* ev = reinterpret_cast<const f32x4*>(ew) + 2 * j;
-        const f32x4 a = __builtin_nontemporal_load(mv), b = __builtin_nontemporal_load(mv + 1);
-        const f32x4 c = __builtin_nontemporal_load(ev), d = __builtin_nontemporal_load(ev + 1);
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m) + j);
+        const f32x4 c = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ew) + j);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 4; ++k)
             x[k] = a[k] + c[k];
-            x[4 + k] = b[k] + d[k];
-        }
     }
 };
 
@@ -176,16 +218,13 @@ struct ServerU {
         const float c = ((bits[i >> 3] >> (i & 7)) & 1) ? sw : -sw;
         return c + es[i];
     }
-    __device__ __forceinline__ void vec(uint64_t j, float (&x)[8]) const
+    __device__ __forceinline__ void vec(uint64_t j, float (&x)[4]) const
     {
-        const uint32_t byte = bits[j];
-        const f32x4* ev = reinterpret_cast<const f32x4*>(es) + 2 * j;
-        const f32x4 a = __builtin_nontemporal_load(ev), b = __builtin_nontemporal_load(ev + 1);
+        const uint32_t nib = nibble_of(bits, j);
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(es) + j);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[k] = (((byte >> k) & 1) ? sw : -sw) + a[k];
-            x[4 + k] = (((byte >> (4 + k)) & 1) ? sw : -sw) + b[k];
-        }
+        for (int k = 0; k < 4; ++k)
+            x[k] = (((nib >> k) & 1) ? sw : -sw) + a[k];
     }
 };
 
@@ -223,29 +262,29 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
 
     AccWin acc;
     if (mx) {
-        const uint64_t nvec = n >> 3;
+        const uint64_t ng = (n >> 3) * 2;                     // groups of 4 in whole payload bytes
         const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
         uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
-        for (; j + 3 * stride < nvec; j += 4 * stride) {      // four vectors' loads in flight
-            float x[4][8];
+        for (; j + 7 * stride < ng; j += 8 * stride) {        // eight groups' loads in flight
+            float x[8][4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 8; ++q)
                 vsrc.vec(j + q * stride, x[q]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
+                for (int k = 0; k < 4; ++k)
                     acc.add(x[q][k], w);
         }
-        for (; j < nvec; j += stride) {
-            float x[8];
+        for (; j < ng; j += stride) {
+            float x[4];
             vsrc.vec(j, x);
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
+            for (int k = 0; k < 4; ++k)
                 acc.add(x[k], w);
         }
         if (blockIdx.x == 0 && threadIdx.x < (n & 7))
-            acc.add(vsrc.at((nvec << 3) + threadIdx.x), w);
+            acc.add(vsrc.at(4 * ng + threadIdx.x), w);   // elements past the last whole byte
     }
     exact::Limbs s = acc.limbs();
     uint32_t flag = 0;
@@ -318,6 +357,22 @@ __global__ __launch_bounds__(kNormBlock) void onebit_sum_server_kernel(const uin
 
 // ---- C: worker compression ----------------------------------------------------------
 
+// x = m + ew -> sign nibble, ew = x - s_w*sgn(x), and the max of |s_w*sgn(x) + es|.
+__device__ __forceinline__ uint32_t compress4(f32x4 m, f32x4& e, f32x4 s, float sw, uint32_t& mx)
+{
+    uint32_t nib = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float x = m[k] + e[k];
+        const float cw = sgn_scale(x, sw);
+        nib |= (x < 0.0f ? 0u : 1u) << k;
+        e[k] = x - cw;
+        const uint32_t a = abs_bits(cw + s[k]);
+        mx = a > mx ? a : mx;
+    }
+    return nib;
+}
+
 __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const float* __restrict__ m32,
                                                                         float* __restrict__ ew,
                                                                         const float* __restrict__ es,
@@ -329,33 +384,29 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
     if (st->skip)
         return;
     const float sw = ob->scale_w;
-    const uint64_t nvec = n >> 3;
-    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
-    uint32_t mx = 0;
-    if (j < nvec) {
-        const f32x4* mv = reinterpret_cast<const f32x4*>(m32) + 2 * j;
-        f32x4* ev = reinterpret_cast<f32x4*>(ew) + 2 * j;
-        const f32x4* sv = reinterpret_cast<const f32x4*>(es) + 2 * j;
-        const f32x4 m[2] = {mv[0], mv[1]};
-        f32x4 e[2] = {ev[0], ev[1]};
-        const f32x4 s[2] = {__builtin_nontemporal_load(sv), __builtin_nontemporal_load(sv + 1)};
-        uint32_t byte = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float x = m[h][k] + e[h][k];
-                const float cw = sgn_scale(x, sw);
-                byte |= (x < 0.0f ? 0u : 1u) << (4 * h + k);
-                e[h][k] = x - cw;
-                const uint32_t a = abs_bits(cw + s[h][k]);
-                mx = a > mx ? a : mx;
-            }
-        __builtin_nontemporal_store(e[0], ev);
-        __builtin_nontemporal_store(e[1], ev + 1);
-        bits_w[j] = uint8_t(byte);
+    const Groups gr(n);
+    const f32x4* __restrict__ M = reinterpret_cast<const f32x4*>(m32);
+    f32x4* __restrict__ EW = reinterpret_cast<f32x4*>(ew);
+    const f32x4* __restrict__ ES = reinterpret_cast<const f32x4*>(es);
+    uint32_t mx = 0, nib_a = 0, nib_b = 0;
+    if (gr.both()) {
+        const f32x4 ma = M[gr.ja], mb = M[gr.jb];
+        f32x4 ea = EW[gr.ja], eb = EW[gr.jb];
+        const f32x4 sa = __builtin_nontemporal_load(ES + gr.ja), sb = __builtin_nontemporal_load(ES + gr.jb);
+        __builtin_amdgcn_sched_barrier(0);
+        nib_a = compress4(ma, ea, sa, sw, mx);
+        nib_b = compress4(mb, eb, sb, sw, mx);
+        __builtin_nontemporal_store(ea, EW + gr.ja);
+        __builtin_nontemporal_store(eb, EW + gr.jb);
+    } else if (gr.first()) {
+        f32x4 ea = EW[gr.ja];
+        nib_a = compress4(M[gr.ja], ea, ES[gr.ja], sw, mx);
+        EW[gr.ja] = ea;
     }
+    store_byte_pair(bits_w, gr.ja, nib_a, gr.first());
+    store_byte_pair(bits_w, gr.jb, nib_b, gr.both());
     if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {     // the ragged last byte
+        const uint64_t nvec = n >> 3;
         uint32_t byte = 0;
         for (uint64_t i = nvec << 3; i < n; ++i) {
             const float x = m32[i] + ew[i];
@@ -381,6 +432,29 @@ __device__ __forceinline__ void update(float m, float& p, float v, const Coef& c
     p = p - c.lr * u;
 }
 
+// One group: u = s_w*sgn_w + es -> server sign nibble (returned), m = s_s*sgn(u),
+// es = u - m, the parameter update and its fp16 copy h.
+__device__ __forceinline__ uint32_t server_update4(uint32_t wnib, f32x4& s, f32x4& p, f32x4 v, f32x4& m, u32x2& h,
+                                                   float sw, float ss, const Coef& c)
+{
+    uint32_t nib = 0;
+    f16x4 h16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float u = (((wnib >> k) & 1) ? sw : -sw) + s[k];
+        const float mi = sgn_scale(u, ss);
+        nib |= (u < 0.0f ? 0u : 1u) << k;
+        s[k] = u - mi;
+        m[k] = mi;
+        float pk = p[k];
+        update(mi, pk, v[k], c);
+        p[k] = pk;
+        h16[k] = _Float16(pk);
+    }
+    h = __builtin_bit_cast(u32x2, h16);
+    return nib;
+}
+
 __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restrict__ p16, float* __restrict__ p32,
                                                                float* __restrict__ m32, const float* __restrict__ v32,
                                                                float* __restrict__ es,
@@ -397,45 +471,43 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
     }
     const Coef c = coef_of(st);
     const float sw = ob->scale_w, ss = ob->scale_s;
-    const uint64_t nvec = n >> 3;
-    const uint64_t j = uint64_t(blockIdx.x) * kBlock + threadIdx.x;
-    if (j < nvec) {
-        const uint32_t bw = bits_w[j];
-        f32x4* sv = reinterpret_cast<f32x4*>(es) + 2 * j;
-        f32x4* pv = reinterpret_cast<f32x4*>(p32) + 2 * j;
-        f32x4* mv = reinterpret_cast<f32x4*>(m32) + 2 * j;
-        const f32x4* vv = reinterpret_cast<const f32x4*>(v32) + 2 * j;
-        f32x4 s[2] = {sv[0], sv[1]};
-        f32x4 p[2] = {pv[0], pv[1]};
-        const f32x4 v[2] = {vv[0], vv[1]};
-        f32x4 m[2];
-        f16x8 h16;
-        uint32_t bs = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = 4 * h + k;
-                const float u = (((bw >> i) & 1) ? sw : -sw) + s[h][k];
-                const float mi = sgn_scale(u, ss);
-                bs |= (u < 0.0f ? 0u : 1u) << i;
-                s[h][k] = u - mi;
-                m[h][k] = mi;
-                float pk = p[h][k];
-                update(mi, pk, v[h][k], c);
-                p[h][k] = pk;
-                h16[i] = _Float16(pk);
-            }
-        __builtin_nontemporal_store(s[0], sv);
-        __builtin_nontemporal_store(s[1], sv + 1);
-        __builtin_nontemporal_store(m[0], mv);
-        __builtin_nontemporal_store(m[1], mv + 1);
-        __builtin_nontemporal_store(p[0], pv);
-        __builtin_nontemporal_store(p[1], pv + 1);
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h16), reinterpret_cast<u32x4*>(p16) + j);
-        bits_s[j] = uint8_t(bs);
+    const Groups gr(n);
+    f32x4* __restrict__ ES = reinterpret_cast<f32x4*>(es);
+    f32x4* __restrict__ P = reinterpret_cast<f32x4*>(p32);
+    f32x4* __restrict__ M = reinterpret_cast<f32x4*>(m32);
+    const f32x4* __restrict__ V = reinterpret_cast<const f32x4*>(v32);
+    u32x2* __restrict__ H = reinterpret_cast<u32x2*>(p16);
+    uint32_t nib_a = 0, nib_b = 0;
+    if (gr.both()) {
+        const uint32_t wa = nibble_of(bits_w, gr.ja), wb = nibble_of(bits_w, gr.jb);
+        f32x4 sa = ES[gr.ja], sb = ES[gr.jb], pa = P[gr.ja], pb = P[gr.jb];
+        const f32x4 va = V[gr.ja], vb = V[gr.jb];
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 ma, mb;
+        u32x2 ha, hb;
+        nib_a = server_update4(wa, sa, pa, va, ma, ha, sw, ss, c);
+        nib_b = server_update4(wb, sb, pb, vb, mb, hb, sw, ss, c);
+        __builtin_nontemporal_store(sa, ES + gr.ja);
+        __builtin_nontemporal_store(sb, ES + gr.jb);
+        __builtin_nontemporal_store(ma, M + gr.ja);
+        __builtin_nontemporal_store(mb, M + gr.jb);
+        __builtin_nontemporal_store(pa, P + gr.ja);
+        __builtin_nontemporal_store(pb, P + gr.jb);
+        __builtin_nontemporal_store(ha, H + gr.ja);
+        __builtin_nontemporal_store(hb, H + gr.jb);
+    } else if (gr.first()) {
+        f32x4 sa = ES[gr.ja], pa = P[gr.ja], ma;
+        u32x2 ha;
+        nib_a = server_update4(nibble_of(bits_w, gr.ja), sa, pa, V[gr.ja], ma, ha, sw, ss, c);
+        ES[gr.ja] = sa;
+        M[gr.ja] = ma;
+        P[gr.ja] = pa;
+        H[gr.ja] = ha;
     }
+    store_byte_pair(bits_s, gr.ja, nib_a, gr.first());
+    store_byte_pair(bits_s, gr.jb, nib_b, gr.both());
     if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {
+        const uint64_t nvec = n >> 3;
         const uint32_t bw = bits_w[nvec];
         uint32_t bs = 0;
         for (uint64_t i = nvec << 3; i < n; ++i) {
