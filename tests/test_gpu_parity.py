@@ -219,6 +219,41 @@ def test_norm_special_values_everywhere():
             assert s.as_dict()["sumsq_units"] == H.exact_units(g)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_standalone_norm_multi_workgroup_fold(dtype):
+    """The standalone norm at a size whose partials (one per 8192 elements)
+    exceed the single-workgroup fold: 32,775 partials, folded by two decide
+    workgroups that meet at the arrival counter.  The exact sum, the flag and
+    the decision equal the oracle's, bit for bit; a second call re-uses the
+    re-armed counter."""
+    n = (1 << 28) + 7 * 8192 + 3
+    rng = np.random.default_rng(90 if dtype == "f16" else 91)
+    g16 = rng.integers(0, 0x7C00, n, dtype=np.uint16) | (rng.integers(0, 2, n, dtype=np.uint16) << 15)
+    if dtype == "f16":
+        dev = H.to_dev16(g16)
+        ref = O.norm_overflow(g16)
+        call = Z.zero_shard_norm_overflow
+    else:
+        g32 = g16.view(np.float16).astype(np.float32) * np.float32(256.0)     # |x| < 2^24, exact
+        del g16
+        dev = torch.from_numpy(g32).cuda()
+        ref = O.norm_overflow_f32(g32)
+        call = Z.zero_shard_norm_overflow_f32
+        del g32
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st, 65536.0)
+    hp_d = Z.hparams()
+    ost = O.new_state(65536.0)
+    for k in range(2):
+        H.log(f"standalone norm {dtype} n={n} call {k}")
+        call(dev, n, hp_d, st, ws)
+        O.decide(ost, O.hparams(), *ref)
+        s = Z.read_state(st)
+        assert (s.overflow, np.float64(s.sumsq).tobytes()) == (ref[1], np.float64(ref[0]).tobytes())
+        H.compare_state(s, ost, None)
+
+
 def test_determinism_two_runs():
     w = _small("det", 777_777, seed=12)
     outs = []
