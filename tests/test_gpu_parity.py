@@ -100,9 +100,10 @@ def test_stress_loss_scale_trajectory_full_size():
     assert (s.loss_scale, s.good_steps, s.step, s.skipped_total) == (2.0 ** 26, 13, 98, 2)
 
 
-def test_100b_shard_full_size():
+@pytest.mark.parametrize("fused", [False, True])
+def test_100b_shard_full_size(fused):
     w = shardgen.workload("100b")
-    r = H.start(w, sample=1 << 20)
+    r = H.start(w, sample=1 << 20, fused=fused)
     for _ in range(2):
         H.step(r)
 
