@@ -245,10 +245,8 @@ size_t zero_decide_workspace_bytes(uint64_t count);
 int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,
                       zero_step_state_t* dev_state, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace zero_shard_norm_overflow (and its fp32 form)
- * needs for n elements: one 32-byte partial sum per 8192 elements (at least
- * one), rounded up to 256 bytes, then the final fold's own partials.  A
- * function of n alone. */
+/* Bytes of device workspace zero_shard_norm_overflow needs for n elements
+ * (per-block partial sums; fixed for a given n). */
 size_t zero_norm_workspace_bytes(uint64_t n);
 
 /* Reduce and decide.  Over the n binary16 gradient elements at grad16:

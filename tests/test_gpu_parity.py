@@ -222,11 +222,10 @@ def test_norm_special_values_everywhere():
 
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 def test_standalone_norm_multi_workgroup_fold(dtype):
-    """The standalone norm at a size whose partials (one per 8192 elements)
-    exceed the single-workgroup fold: 32,775 partials, folded by two decide
-    workgroups that meet at the arrival counter.  The exact sum, the flag and
-    the decision equal the oracle's, bit for bit; a second call re-uses the
-    re-armed counter."""
+    """The standalone norm over a quarter-billion-element partition: every
+    one of its workgroups streams thousands of elements and all of them meet
+    at the arrival counter.  The exact sum, the flag and the decision equal
+    the oracle's, bit for bit; a second call re-uses the re-armed counter."""
     n = (1 << 28) + 7 * 8192 + 3
     rng = np.random.default_rng(90 if dtype == "f16" else 91)
     g16 = rng.integers(0, 0x7C00, n, dtype=np.uint16) | (rng.integers(0, 2, n, dtype=np.uint16) << 15)

@@ -159,19 +159,9 @@ extern "C" int zero_bucket_segments(const zero_segment_t* segs, uint32_t nsegs, 
     return k > cap ? ZERO_ERANGE : ZERO_OK;
 }
 
-NormLayout zero::norm_layout(uint64_t n)
-{
-    NormLayout L;
-    L.partials = (n + kPartElems - 1) / kPartElems;
-    if (L.partials < 1) L.partials = 1;
-    L.decide_off = (L.partials * sizeof(NormPartial) + 255) / 256 * 256;
-    L.bytes = L.decide_off + decide_grid(L.partials) * sizeof(NormPartial);   // decide_grid is monotone
-    return L;
-}
-
 extern "C" size_t zero_norm_workspace_bytes(uint64_t n)
 {
-    return size_t(norm_layout(n).bytes);
+    return size_t(norm_grid(n)) * sizeof(NormPartial);
 }
 
 extern "C" size_t zero_decide_workspace_bytes(uint64_t count)

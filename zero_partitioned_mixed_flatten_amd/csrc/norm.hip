@@ -13,24 +13,20 @@
 // independent of grid shape and schedule, so the clip factor derived from it
 // is bitwise reproducible.
 //
-// Two kernels:
-//   norm_partials_kernel  reads the partition itself, one-shot: a workgroup
-//                         of 256 threads per 8192 elements (four 16-byte
-//                         fp16 vectors or eight fp32 vectors per thread, all
-//                         loads nontemporal and issued before the first
-//                         wait), about 8 VALU operations per fp16 element and
-//                         12 binary64 operations per fp32 element, one 32-byte
-//                         partial per workgroup, written to memory -- no
-//                         atomics, which serialise at this workgroup count;
-//   decide_kernel         folds partials -- this kernel's, or those a fused
-//                         flatten (flatten.hip) computed while copying -- and
-//                         decides: up to 2^15 partials in one workgroup with
-//                         no arrival counter or fence; more over at most 256
-//                         workgroups, each storing its carried partial and
-//                         bumping an agent-scope acq_rel arrival counter
-//                         once, the last to arrive folding them all.
-// The decision is taken in binary64 on one thread, written into the step
-// state, and the counter re-armed.  No MFMA: 2 or 4 bytes per element.
+// Two kernels share the tail:
+//   norm_overflow_kernel  reads the partition itself: 1024-thread workgroups,
+//                         at most one per CU (256), each thread streaming
+//                         16-byte vectors with four nontemporal loads in
+//                         flight; about 8 VALU operations per fp16 element,
+//                         about 12 binary64 operations per fp32 element;
+//   decide_kernel         folds the per-workgroup partials a fused flatten
+//                         (flatten.hip) already computed while copying; up
+//                         to 2^15 partials in a single workgroup, which then
+//                         decides without an arrival counter or fence.
+// In both, every workgroup stores its carried partial, bumps an agent-scope
+// acq_rel arrival counter once, and the last one to arrive folds all
+// partials, takes the decision in binary64 on one thread, writes it into the
+// step state and re-arms the counter.  No MFMA: 2 or 4 bytes per element.
 #include <math.h>
 
 #include "decide.hpp"
@@ -101,46 +97,36 @@ struct Elem<float> {
 __device__ __forceinline__ void acc_vec(exact::Acc16& acc, u32x4 v) { acc.vec(v); }
 __device__ __forceinline__ void acc_vec(exact::Acc32& acc, u32x4 v) { acc.vec(__builtin_bit_cast(f32x4, v)); }
 
-// One partial per kPartElems elements: the exact sum and overflow bits of
-// this workgroup's share.
 template <typename T>
-__global__ __launch_bounds__(kPartBlock) void norm_partials_kernel(const T* __restrict__ g, uint64_t n,
-                                                                   NormPartial* __restrict__ part)
+__global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const T* __restrict__ g, uint64_t n,
+                                                                   zero_step_state_t* __restrict__ st,
+                                                                   NormPartial* __restrict__ ws, DecideArgs d)
 {
     using E = Elem<T>;
-    constexpr int kVecs = int(kPartElems / kPartBlock) / E::kPerVec;      // 4 (fp16) or 8 (fp32)
-    constexpr uint64_t kVecsPerBlock = uint64_t(kPartBlock) * kVecs;
     typename E::Acc acc;
     const uint64_t nvec = n / E::kPerVec;
     const u32x4* __restrict__ gv = reinterpret_cast<const u32x4*>(g);
-    const uint64_t v0 = uint64_t(blockIdx.x) * kVecsPerBlock + threadIdx.x;
-    if (uint64_t(blockIdx.x + 1) * kVecsPerBlock <= nvec) {
-        // a full workgroup: unguarded, so every load is in flight before the
-        // first wait (per-lane guards would let the compiler wait after each)
-        u32x4 r[kVecs];
-#pragma unroll
-        for (int k = 0; k < kVecs; ++k)
-            r[k] = __builtin_nontemporal_load(gv + v0 + k * kPartBlock);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < kVecs; ++k)
-            acc_vec(acc, r[k]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < kVecs; ++k) {
-            const uint64_t v = v0 + k * kPartBlock;
-            if (v < nvec)
-                acc_vec(acc, __builtin_nontemporal_load(gv + v));
-        }
+    const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
+    uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
+    for (; j + 3 * stride < nvec; j += 4 * stride) {      // four 16-byte loads in flight
+        const u32x4 a = __builtin_nontemporal_load(gv + j);
+        const u32x4 b = __builtin_nontemporal_load(gv + j + stride);
+        const u32x4 c = __builtin_nontemporal_load(gv + j + 2 * stride);
+        const u32x4 e = __builtin_nontemporal_load(gv + j + 3 * stride);
+        acc_vec(acc, a);
+        acc_vec(acc, b);
+        acc_vec(acc, c);
+        acc_vec(acc, e);
     }
+    for (; j < nvec; j += stride)
+        acc_vec(acc, __builtin_nontemporal_load(gv + j));
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * E::kPerVec)   // the last n % kPerVec elements
         E::one(acc, g, nvec * E::kPerVec + threadIdx.x);
 
     uint32_t flag = acc.flag;
     Limbs s = acc.limbs();
-    exact::block_fold<kPartBlock>(s, flag);
-    if (threadIdx.x == 0)
-        part[blockIdx.x] = exact::make_partial(s, flag);
+    exact::block_fold<kNormBlock>(s, flag);
+    publish_and_decide(s, flag, st, ws, d);
 }
 
 // Folds `count` carried partials (from a fused flatten) and decides.
@@ -177,21 +163,11 @@ int norm_overflow(const T* grad, uint64_t n, const zero_hparams_t* hp, zero_step
         return ZERO_EALIGN;
     if (n > kNormMaxElems)
         return ZERO_ERANGE;
-    const NormLayout L = norm_layout(n);
-    if (workspace_bytes < L.bytes)
+    const uint64_t grid = norm_grid(n);
+    if (workspace_bytes < grid * sizeof(NormPartial))
         return ZERO_ERANGE;
-    const uint64_t vpb = kPartElems / Elem<T>::kPerVec;             // vectors per workgroup
-    uint64_t grid = (n / Elem<T>::kPerVec + vpb - 1) / vpb;
-    if (grid < 1) grid = 1;                                         // <= L.partials
-    NormPartial* part = static_cast<NormPartial*>(workspace);
-    NormPartial* dws = reinterpret_cast<NormPartial*>(static_cast<char*>(workspace) + L.decide_off);
-    hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(norm_partials_kernel<T>, dim3(uint32_t(grid)), dim3(kPartBlock), 0, s, grad, n, part);
-    int rc = launch_status();
-    if (rc != ZERO_OK)
-        return rc;
-    hipLaunchKernelGGL(decide_kernel, dim3(uint32_t(decide_grid(grid))), dim3(kNormBlock), 0, s, part, grid,
-                       dev_state, dws, decide_args(hp));
+    hipLaunchKernelGGL(norm_overflow_kernel<T>, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
+                       grad, n, dev_state, static_cast<NormPartial*>(workspace), decide_args(hp));
     return launch_status();
 }
 

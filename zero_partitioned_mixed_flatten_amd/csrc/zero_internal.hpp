@@ -59,17 +59,6 @@ static_assert(sizeof(NormPartial) == 32, "partial layout");
 
 uint64_t norm_grid(uint64_t n);
 
-// The standalone norm: one partial per kPartElems elements, from workgroups
-// of kPartBlock threads; its workspace holds the partials (first `partials`
-// entries, the most either element type needs) and, from decide_off, the
-// decide kernel's own partials.
-constexpr int kPartBlock = 256;
-constexpr uint64_t kPartElems = 8192;
-struct NormLayout {
-    uint64_t partials, decide_off, bytes;
-};
-NormLayout norm_layout(uint64_t n);
-
 // Partials folded by the decide-only pass (the fused flatten writes one per
 // workgroup); stored partials are carried, so 2^30 of them fit in int64 sums.
 constexpr uint64_t kMaxPartials = uint64_t(1) << 30;
