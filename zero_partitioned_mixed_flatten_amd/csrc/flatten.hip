@@ -149,6 +149,50 @@ __device__ __forceinline__ void put_vector(void* dst, uint64_t i, u32x4 s, Old o
     }
 }
 
+// The vector body of an fp32 destination, in units of 4 elements: thread t
+// takes units u0 + t + k*kBlock, so each 8-byte fp16 load and each 16-byte
+// fp32 store of a wave covers one contiguous span (8-element units would put
+// a thread's two fp32 vectors 32 bytes apart across the lanes).  d points at
+// element 0 of the body (32-byte aligned), s at its source (16-byte aligned).
+template <int MODE, bool NORM>
+__device__ __forceinline__ void body32(const uint16_t* __restrict__ s, float* __restrict__ d, uint64_t u0,
+                                       uint64_t u1, AccOf<MODE>& acc)
+{
+    constexpr int kUnits = 2 * Geometry<NORM>::kVecsPerThread;
+    const u32x2* __restrict__ S = reinterpret_cast<const u32x2*>(s);
+    f32x4* __restrict__ D = reinterpret_cast<f32x4*>(d);
+    auto put = [&](f32x4* at, u32x2 raw, f32x4 old) {
+        const f16x4 h = __builtin_bit_cast(f16x4, raw);
+        f32x4 r = {float(h[0]), float(h[1]), float(h[2]), float(h[3])};
+        if (MODE == kAcc32)
+            r = old + r;                                      // binary32 add
+        store<NORM>(r, at);
+        if (NORM)
+            acc.vec(r);
+    };
+    if (u1 - u0 == uint64_t(kUnits) * kBlock) {              // a full workgroup: every load first
+        u32x2 r[kUnits];
+        f32x4 o[kUnits];
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            const uint64_t u = u0 + threadIdx.x + k * kBlock;
+            r[k] = __builtin_nontemporal_load(S + u);
+            o[k] = MODE == kAcc32 ? D[u] : f32x4{};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k)
+            put(D + u0 + threadIdx.x + k * kBlock, r[k], o[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            const uint64_t u = u0 + threadIdx.x + k * kBlock;
+            if (u < u1)
+                put(D + u, __builtin_nontemporal_load(S + u), MODE == kAcc32 ? D[u] : f32x4{});
+        }
+    }
+}
+
 template <int MODE, bool NORM>
 __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __restrict__ dst)
 {
@@ -176,7 +220,10 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     const uint64_t v1 = v0 + kVecsPerBlock < nv ? v0 + kVecsPerBlock : nv;
     const uint16_t* __restrict__ sbody = src + head;
     const uint64_t dbody = doff + head;
-    if (vec_src && v1 - v0 == kVecsPerBlock) {
+    if (MODE >= kTo32 && vec_src) {
+        if constexpr (MODE >= kTo32)
+            body32<MODE, NORM>(sbody, static_cast<float*>(dst) + dbody, 2 * v0, 2 * v1, acc);
+    } else if (vec_src && v1 - v0 == kVecsPerBlock) {
         // A full workgroup (all but a segment's last): no per-lane guards, so
         // every load is issued before the first wait.  Under per-lane guards
         // the compiler moves each load into its store's guarded block and
