@@ -9,8 +9,10 @@
 // each workgroup finds its segment by a uniform binary search over a prefix
 // of block counts held in that block.  Within a segment the destination is
 // split into a scalar head that reaches 16-byte alignment, a body of aligned
-// 8-element vectors (one 16-byte fp16 store or two 16-byte fp32 stores per
-// thread-vector) and a scalar tail.  When the source shares the destination's
+// 8-element vectors (one 16-byte fp16 store per thread-vector; an fp32
+// destination takes the body in 4-element units instead, one 16-byte store
+// each, so every store instruction of a wave stays contiguous) and a scalar
+// tail.  When the source shares the destination's
 // 16-byte phase the body loads are 16-byte vector loads; otherwise each
 // thread gathers its 8 source elements with 2-byte loads (still coalesced
 // across the wavefront).  The work is pure streaming: 4 bytes per element
