@@ -15,7 +15,7 @@
 // Five kernels, because two global scales sit on the data path:
 //   A  momentum + per-block max|x|           one-shot, 8 elements per thread
 //   B  exact sum of x^2 in the window, s_w   <= 256 workgroups x 1024, grid-stride
-//      with four vectors' loads in flight; every workgroup first folds A's
+//      with eight 4-element groups' loads in flight; every workgroup first folds A's
 //      block maxima (L2-resident), the last one to arrive folds the limbs and
 //      writes s_w
 //   C  worker compression: sign byte, ew, u = cw + es, per-block max|u|
