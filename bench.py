@@ -58,9 +58,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def code_text(text):
+    """C/C++/HIP source with its comments removed and every run of blank space
+    collapsed to one space (string and character literals kept as written), so
+    that editing a comment does not count as changing a kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def code_hash(path):
+    with open(path, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def measured_traffic(path, n):
@@ -75,7 +101,7 @@ def measured_traffic(path, n):
     if path is None or s.get("n") != n:
         return None
     for src in s.get("sources_for", {}).get(path, []):
-        if s.get("source_sha256_16", {}).get(src) != source_hash(os.path.join(CSRC, src)):
+        if s.get("code_sha256_16", {}).get(src) != code_hash(os.path.join(CSRC, src)):
             return None
     return s.get("hbm_bytes_per_launch", {}).get(path)
 
