@@ -187,9 +187,11 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
     import numpy as np
     import torch
     import zero_partitioned_mixed_flatten_amd as Z
+    from zero_partitioned_mixed_flatten_amd.stepper import host_f32
     n = w.n
+    huge = args.host_pages == "huge"
     dev = Z.OffloadStep(n, threads=args.threads, chunk_elems=args.chunk,
-                        device_decides=(args.offload_decide == "device"))
+                        device_decides=(args.offload_decide == "device"), huge_pages=huge)
     dev.p32.copy_(torch.from_numpy(p32))
     dev.p16.copy_(dev.p32.half().cuda())
     dev.init_state(w.scale0)
@@ -231,8 +233,9 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
     adam_s = timed(lambda: Z.zero_host_adam_step(dev.ctx.ptr, dev.host_p16, dev.p32, dev.m32, dev.v32,
                                                  dev.host_grad16, n, probe))
     nbytes = (ADAM_BYTES // 2) * n // 64 * 64
-    hsrc = torch.empty(nbytes + 64, dtype=torch.uint8)
-    hdst = torch.empty(nbytes + 64, dtype=torch.uint8)
+    # the reference copy runs on the same kind of pages as the fp32 state
+    hsrc = host_f32(nbytes // 4 + 16, huge).view(torch.uint8)
+    hdst = host_f32(nbytes // 4 + 16, huge).view(torch.uint8)
     a_src = hsrc[(-hsrc.data_ptr()) % 64:][:nbytes]
     a_dst = hdst[(-hdst.data_ptr()) % 64:][:nbytes]
     copy_s = timed(lambda: Z.zero_host_stream_copy(dev.ctx.ptr, a_dst, a_src, nbytes))
@@ -264,12 +267,13 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
         "data": "synthetic",
         "config": {"workload": f"{w.layout.model} Nd={w.layout.nd} rank {w.layout.rank} shard, offloaded step",
                    "params": n, "segments": len(w.layout.segments), "path": "offload", "host_threads": threads,
-                   "chunk_elems": args.chunk, "decides": args.offload_decide,
+                   "chunk_elems": args.chunk, "decides": args.offload_decide, "host_pages": args.host_pages,
                    "state": "device: fp16 p, g; host: fp32 p, m, v (+ pinned fp16 g, p staging)"},
         "roofline": {"bound": "host-dram", "kernel": "host_adam_step", "achieved": achieved,
                      "peak": host_copy_gbps, "unit": "GB/s", "frac": achieved / host_copy_gbps, "traffic": None,
                      "algorithmic_bytes": ADAM_BYTES * n,
-                     "peak_source": "measured host streaming copy (zero_host_stream_copy, 14 B/param)"},
+                     "peak_source": "measured host streaming copy (zero_host_stream_copy, 14 B/param, on the "
+                                    "same kind of pages as the fp32 state)"},
         "phases_ms": {"host_norm_decide": 1e3 * norm_s, "host_adam": 1e3 * adam_s, "d2h_grad16": 1e3 * d2h_s,
                       "h2d_p16": 1e3 * h2d_s},
         "pcie_gbps": {"d2h": 2 * n / d2h_s / 1e9, "h2d": 2 * n / h2d_s / 1e9},
@@ -404,6 +408,8 @@ def main():
     ap.add_argument("--threads", type=int, default=None,
                     help="host workers for --path offload (default: all CPUs but one)")
     ap.add_argument("--chunk", type=int, default=1 << 24, help="elements per transfer chunk for --path offload")
+    ap.add_argument("--host-pages", default="huge", choices=["huge", "4k"],
+                    help="--path offload: host fp32 state on transparent huge pages or on 4 KiB pages")
     ap.add_argument("--offload-decide", default="device", choices=["device", "host"],
                     help="--path offload: who reduces and decides (bit-identical either way)")
     ap.add_argument("--micro-batches", type=int, default=4,

@@ -277,3 +277,18 @@ def test_host_step_random_against_oracle(Z, ctxs, n, off, threads, seed, special
     _state_equal(st, ref)
     for a, b in zip(host, orc):
         assert a.tobytes() == b.tobytes()
+
+
+def test_host_f32_is_zeroed_aligned_and_writable():
+    import torch
+
+    from zero_partitioned_mixed_flatten_amd.stepper import host_f32
+    for huge in (True, False):
+        t = host_f32(3_000_007, huge)
+        assert t.dtype == torch.float32 and t.numel() == 3_000_007 and not t.any()
+        if huge:
+            assert t.data_ptr() % (2 << 20) == 0
+        v = t[5:17]                                   # a view keeps the mapping alive with its storage
+        del t
+        v.fill_(2.5)
+        assert float(v.sum()) == 30.0
