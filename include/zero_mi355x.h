@@ -420,8 +420,8 @@ int zero_host_adam_step(zero_host_ctx_t* ctx, uint16_t* p16, float* p32, float* 
  * parameters live on the device and whose fp32 master parameters, momentum
  * and variance live in host memory.  Two ways to decide:
  *   dev_state NULL: the CPU decides.  dev_grad16 is copied to host_grad16
- *     in chunks of chunk_elems on `stream`, each chunk reduced on the CPU as
- *     soon as it has landed; then the decision into the host `state` (as
+ *     in chunks on `stream`, each chunk reduced on the CPU as soon as it has
+ *     landed; then the decision into the host `state` (as
  *     zero_host_norm_overflow; `hp` is required);
  *   dev_state given: the device has already decided on `stream`
  *     (zero_shard_decide over zero_flatten_norm_bucket partials, or
@@ -436,10 +436,15 @@ int zero_host_adam_step(zero_host_ctx_t* ctx, uint16_t* p16, float* p32, float* 
  * (later work on `stream` sees them; the host must not touch host_grad16
  * or host_p16 before they complete).  host_grad16, host_p16 and `state`
  * should be pinned host memory (hipHostMalloc) for the copies to overlap.
+ * chunk_elems is the largest chunk; the first chunks ramp up from
+ * chunk_elems/16 (at least 64) by doubling and the last ones ramp down the
+ * same way, so the CPU starts once a small chunk has landed and the last
+ * parameters go up right after their update; every chunk boundary but n is a
+ * multiple of 64 elements.  The results do not depend on the chunking.
  * dev_grad16, dev_p16, dev_state: device; the other arrays host memory.
  * Errors: ZERO_EINVAL (NULL, hyperparameters out of range), ZERO_EALIGN
  *         (chunk_elems 0 or not a multiple of 64, dev_state not 8-byte
- *         aligned), ZERO_ERANGE (more than 4096 chunks), ZERO_EHIP (a copy,
+ *         aligned), ZERO_ERANGE (n above 4096 * chunk_elems), ZERO_EHIP (a copy,
  *         event or synchronisation failed). */
 int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad16, uint16_t* dev_p16, uint16_t* host_grad16,
                       uint16_t* host_p16, float* p32, float* m32, float* v32, uint64_t n,

@@ -33,6 +33,7 @@
 #include <sched.h>
 #include <string.h>
 
+#include <algorithm>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
@@ -308,6 +309,7 @@ struct zero_host_ctx {
     Pool pool;
     std::vector<NormAcc> acc;
     std::vector<hipEvent_t> events;
+    std::vector<uint64_t> bounds;                // chunk boundaries of the last offloaded step
     int event_device = -1;
 };
 
@@ -439,6 +441,52 @@ extern "C" int zero_host_stream_copy(zero_host_ctx_t* ctx, void* dst, const void
     return ZERO_OK;
 }
 
+namespace {
+
+// Chunk boundaries of an offloaded step over n elements, chunks at most
+// `largest` (a multiple of 64) elements long.  The first chunks ramp up from
+// largest/16 by doubling and the last ones ramp down the same way, so the CPU
+// starts updating once a small first chunk has landed and the last
+// parameters go up right after their update: the copy of a full chunk is
+// neither waited for at the start nor left over at the end.  Every boundary
+// but n is a multiple of 64.
+void chunk_bounds(uint64_t n, uint64_t largest, std::vector<uint64_t>& b)
+{
+    b.clear();
+    b.push_back(0);
+    if (n == 0)
+        return;
+    uint64_t m = (largest / 16) & ~uint64_t(63);
+    if (m < 64) m = 64;
+    std::vector<uint64_t> ramp;                  // m, 2m, 4m, ... below `largest`
+    uint64_t r = 0;
+    for (uint64_t s = m; s < largest; s *= 2) {
+        ramp.push_back(s);
+        r += s;
+    }
+    const uint64_t n64 = n & ~uint64_t(63);
+    auto add = [&](uint64_t len) { b.push_back(b.back() + len); };
+    if (n64 >= 2 * r + largest) {
+        for (uint64_t s : ramp) add(s);
+        const uint64_t mid = n64 - 2 * r;
+        if (mid % largest) add(mid % largest);
+        for (uint64_t q = mid / largest; q; --q) add(largest);
+        for (auto it = ramp.rbegin(); it != ramp.rend(); ++it) add(*it);
+    } else {                                     // too short for both ramps: ramp up only
+        uint64_t s = m;
+        while (b.back() < n64) {
+            add(std::min(s, n64 - b.back()));
+            s = std::min(2 * s, largest);
+        }
+    }
+    if (b.back() == 0)
+        b.push_back(n);                          // fewer than 64 elements: one chunk
+    else
+        b.back() = n;                            // the last chunk takes the ragged end
+}
+
+}  // namespace
+
 extern "C" int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad16, uint16_t* dev_p16,
                                  uint16_t* host_grad16, uint16_t* host_p16, float* p32, float* m32, float* v32,
                                  uint64_t n, const zero_hparams_t* hp, zero_step_state_t* state,
@@ -454,9 +502,10 @@ extern "C" int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad1
     if (chunk_elems == 0 || (chunk_elems & 63))
         return ZERO_EALIGN;
     hipStream_t s = (hipStream_t)stream;
-    const uint64_t chunks = n ? (n + chunk_elems - 1) / chunk_elems : 0;
-    if (chunks > 4096)
+    if ((n + chunk_elems - 1) / chunk_elems > 4096)
         return ZERO_ERANGE;
+    chunk_bounds(n, chunk_elems, ctx->bounds);   // the two ramps add at most 8 chunks
+    const uint64_t chunks = ctx->bounds.size() - 1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return hip_fail(hipGetLastError());
@@ -474,8 +523,9 @@ extern "C" int zero_offload_step(zero_host_ctx_t* ctx, const uint16_t* dev_grad1
         ctx->events.push_back(e);
     }
     hipEvent_t* ev = ctx->events.data();         // ev[0]: the state, ev[1 + c]: gradient chunk c
-    auto lo_of = [&](uint64_t c) { return c * chunk_elems; };
-    auto hi_of = [&](uint64_t c) { return n - c * chunk_elems < chunk_elems ? n : (c + 1) * chunk_elems; };
+    const uint64_t* bnd = ctx->bounds.data();
+    auto lo_of = [&](uint64_t c) { return bnd[c]; };
+    auto hi_of = [&](uint64_t c) { return bnd[c + 1]; };
     // the decision first (when the device has made it), then the gradient, chunk by chunk
     if (dev_state) {
         hipError_t err = hipMemcpyAsync(state, dev_state, sizeof *state, hipMemcpyDeviceToHost, s);
