@@ -321,8 +321,9 @@ class OffloadStep:
     partials and the device decides (a few microseconds), so the CPU can
     update each gradient chunk as soon as it lands.  device_decides=False: the
     CPU reduces the gradient and decides.  Both decide bit-identically.
-    The defaults (16M-element transfer chunks, all CPUs but one) were the
-    fastest measured on the gpt2 shard.  huge_pages: back the host fp32 state
+    The defaults (transfer chunks of at most 16M elements, ramped at both
+    ends by the library; all CPUs but one) were the fastest measured on the
+    gpt2 shard.  huge_pages: back the host fp32 state
     with transparent huge pages (host_f32)."""
 
     def __init__(self, n: int, threads: Optional[int] = None, chunk_elems: int = 1 << 24, device="cuda",
