@@ -294,7 +294,7 @@ class HostContext:
 
     def __init__(self, threads: int = 0):
         self.ptr = Z.zero_host_create(threads)
-        self._destroy = Z.zero_host_destroy       # held, so closing still works at interpreter exit
+        self._destroy = Z.lib().zero_host_destroy  # the C function itself: still callable at interpreter exit
 
     @property
     def threads(self) -> int:
