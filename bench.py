@@ -182,7 +182,7 @@ def run_offload(args, w, p32, grads_host, dev_sets, hp):
     """The ZeRO-Offload form: device flatten, then the gradient down, the CPU's
     exact norm, decision and AdamW on host-resident fp32 state, the fp16
     parameters up.  Its roofline is the host update against the host's own
-    streaming-copy bandwidth (measured here: the pages and the box publish no
+    streaming-copy bandwidth (measured here: the pages and the host publish no
     DRAM figure)."""
     import numpy as np
     import torch
@@ -422,9 +422,8 @@ def main():
                     help="run only the streaming-copy reference (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's shard step only: every box here has a single GPU and this "
-              "build has no multi-GPU path (see DESIGN.md for how the step would shard). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one rank's shard step on one GPU; there is no multi-GPU path (the "
+              "cross-rank exchange of the step is not implemented). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
