@@ -43,6 +43,12 @@ namespace zero {
 namespace {
 
 constexpr int kBlock = 256;                  // one-shot kernels A, C, E
+// The one-shot kernels run at most kOneShotCap workgroups per CU, enforced by
+// a dynamic-LDS reservation they never touch (as the Adam kernel): measured on
+// MI355X, momentum 4.7%, compression 3.2% and the update after it 1.6% faster
+// than at full occupancy.  A and C also hold block_max's few static LDS bytes,
+// which the reservation leaves room for.
+constexpr int kOneShotCap = 2;
 constexpr double kWinHi = 0x1.8p93;          // ulp 2^41
 constexpr double kWinLo = 0x1.8p52;          // ulp 1
 
@@ -155,8 +161,12 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
                                                                  const zero_step_state_t* __restrict__ st,
                                                                  uint32_t* __restrict__ blockmax)
 {
-    if (st->skip)
+    extern __shared__ char occupancy_reserve[];  // see kOneShotCap
+    if (st->skip) {
+        if (n == UINT64_MAX)
+            occupancy_reserve[threadIdx.x] = 0;
         return;
+    }
     const Coef c = coef_of(st);
     const Groups gr(n);
     f32x4* __restrict__ M = reinterpret_cast<f32x4*>(m32);
@@ -383,8 +393,12 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
                                                                         const zero_onebit_state_t* __restrict__ ob,
                                                                         uint32_t* __restrict__ blockmax)
 {
-    if (st->skip)
+    extern __shared__ char occupancy_reserve[];  // see kOneShotCap
+    if (st->skip) {
+        if (n == UINT64_MAX)
+            occupancy_reserve[threadIdx.x] = 0;
         return;
+    }
     const float sw = ob->scale_w;
     const Groups gr(n);
     const f32x4* __restrict__ M = reinterpret_cast<const f32x4*>(m32);
@@ -603,7 +617,10 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const flo
     NormPartial* part_d = reinterpret_cast<NormPartial*>(ws + pl.off_part_d);
     hipStream_t s = (hipStream_t)stream;
     const dim3 g1(uint32_t(pl.grid1)), g2(uint32_t(pl.grid2));
-    hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), 0, s, m32, err_w, grad16, n, dev_state, max_a);
+    const uint32_t cap = lds_reservation(kOneShotCap);
+    const uint32_t cap_ac = cap > 256 ? cap - 256 : 0;     // room for block_max's static LDS
+    hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, grad16, n, dev_state,
+                       max_a);
     int rc = launch_status();
     if (rc != ZERO_OK)
         return rc;
@@ -611,7 +628,7 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const flo
                        dev_state, dev_onebit, part_b);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_compress_worker_kernel, g1, dim3(kBlock), 0, s, m32, err_w, err_s, bits_w, n,
+    hipLaunchKernelGGL(onebit_compress_worker_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, err_s, bits_w, n,
                        dev_state, dev_onebit, max_c);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
@@ -619,7 +636,7 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const flo
                        dev_state, dev_onebit, part_d);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_update_kernel, g1, dim3(kBlock), lds_reservation(2), s, p16, p32, m32, v32, err_s,
+    hipLaunchKernelGGL(onebit_update_kernel, g1, dim3(kBlock), cap, s, p16, p32, m32, v32, err_s,
                        bits_w, bits_s, n, dev_state, dev_onebit);
     return launch_status();
 }
