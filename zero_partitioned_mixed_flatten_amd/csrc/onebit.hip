@@ -496,8 +496,11 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
     uint32_t nib_a = 0, nib_b = 0;
     if (gr.both()) {
         const uint32_t wa = nibble_of(bits_w, gr.ja), wb = nibble_of(bits_w, gr.jb);
-        f32x4 sa = ES[gr.ja], sb = ES[gr.jb], pa = P[gr.ja], pb = P[gr.jb];
-        const f32x4 va = V[gr.ja], vb = V[gr.jb];
+        // v is frozen (read only) and p is read once: nontemporal loads of both
+        // made this kernel 5% faster, and the next momentum pass 1.4% slower
+        f32x4 sa = ES[gr.ja], sb = ES[gr.jb];
+        f32x4 pa = __builtin_nontemporal_load(P + gr.ja), pb = __builtin_nontemporal_load(P + gr.jb);
+        const f32x4 va = __builtin_nontemporal_load(V + gr.ja), vb = __builtin_nontemporal_load(V + gr.jb);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 ma, mb;
         u32x2 ha, hb;
