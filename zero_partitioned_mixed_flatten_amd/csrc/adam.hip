@@ -23,9 +23,10 @@
 //     workgroups sweeps memory once, in order (giving each thread 8 adjacent
 //     parameters instead, with two 16-byte accesses 32 bytes apart across the
 //     lanes, was about 1% slower);
-//   * plain loads of p, m, v, nontemporal loads of the gradient (read once)
-//     and nontemporal stores (nothing written here is read again by this
-//     kernel);
+//   * nontemporal loads (every input is read once) and nontemporal stores
+//     (nothing written here is read again by this kernel); all eight loads
+//     of a thread are issued before the step state is read, so the skip
+//     test does not delay the streams;
 //   * at most kBlocksPerCU workgroups resident per CU, enforced by reserving
 //     LDS the kernel never touches: with all 8 waves per SIMD resident the
 //     8 concurrent read/write streams thrash HBM pages, and 2 waves per SIMD
@@ -59,21 +60,54 @@ __device__ __forceinline__ void update(float gh, float& p, float& m, float& v, c
     v = vn;
 }
 
-// Gradient group j (parameters 4j..4j+3), widened to fp32 (exact for fp16).
-// The gradient is read once and never again this step: nontemporal loads
-// (worth about 2% of the kernel; the same hint on p, m, v costs 3%).
-__device__ __forceinline__ void load_grad4(const uint16_t* g, uint64_t j, float* out)
+// Gradient group j (parameters 4j..4j+3) as loaded: four fp16 bit patterns
+// (8 bytes) or four fp32 values (16 bytes).  The gradient is read once and
+// never again this step: nontemporal loads.  Widening waits for the load, so
+// it is a separate step, done after every load of the thread is in flight.
+__device__ __forceinline__ u32x2 load_grad_raw(const uint16_t* g, uint64_t j)
 {
-    const f16x4 h = __builtin_bit_cast(f16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g) + j));
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g) + j);
+}
+
+__device__ __forceinline__ f32x4 load_grad_raw(const float* g, uint64_t j)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + j);
+}
+
+// Widened to fp32 (exact for fp16).
+__device__ __forceinline__ void widen(u32x2 r, float* out)
+{
+    const f16x4 h = __builtin_bit_cast(f16x4, r);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         out[k] = float(h[k]);
 }
 
-__device__ __forceinline__ void load_grad4(const float* g, uint64_t j, float* out)
+__device__ __forceinline__ void widen(f32x4 r, float* out)
 {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + j);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[0] = r.x; out[1] = r.y; out[2] = r.z; out[3] = r.w;
+}
+
+// fp32 master parameter, momentum or variance group j, read once per step:
+// nontemporal like the gradient.  With the contiguous per-instruction mapping
+// this is about 2% faster than plain loads, which leave lines in the caches
+// that the in-place stores then have to replace.
+__device__ __forceinline__ f32x4 load_state4(const f32x4* q) { return __builtin_nontemporal_load(q); }
+
+__device__ __forceinline__ Coef coef(const zero_step_state_t* st)
+{
+    Coef c;
+    c.gmul = st->gmul;
+    c.b1 = st->beta1;
+    c.b2 = st->beta2;
+    c.omb1 = st->omb1;
+    c.omb2 = st->omb2;
+    c.bc1 = st->bc1;
+    c.bc2 = st->bc2;
+    c.eps = st->eps;
+    c.wd = st->wd;
+    c.lr = st->lr;
+    return c;
 }
 
 __device__ __forceinline__ u32x2 to_f16x4(const float* p)
@@ -98,22 +132,8 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
     // touches (the store below is unreachable for any real n); referencing it
     // keeps the reservation part of the kernel's declared resources.
     extern __shared__ char occupancy_reserve[];
-    if (st->skip) {
-        if (n == UINT64_MAX)
-            occupancy_reserve[threadIdx.x] = 0;
-        return;                                  // overflow: this step changes nothing
-    }
-    Coef c;
-    c.gmul = st->gmul;
-    c.b1 = st->beta1;
-    c.b2 = st->beta2;
-    c.omb1 = st->omb1;
-    c.omb2 = st->omb2;
-    c.bc1 = st->bc1;
-    c.bc2 = st->bc2;
-    c.eps = st->eps;
-    c.wd = st->wd;
-    c.lr = st->lr;
+    if (n == UINT64_MAX)
+        occupancy_reserve[threadIdx.x] = 0;
 
     // groups of 4 parameters: this thread's are ja and jb = ja + kBlock
     const uint64_t ng = n >> 2;
@@ -124,17 +144,24 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
     f32x4* __restrict__ V = reinterpret_cast<f32x4*>(v32);
     u32x2* __restrict__ H = reinterpret_cast<u32x2*>(p16);
     if (jb < ng) {                                // both groups: all loads first
+        // The eight loads go out before the step state is read
+        // (loads_first_use in zero_internal.hpp).
+        const auto ga = load_grad_raw(grad, ja), gb = load_grad_raw(grad, jb);
+        const f32x4 pa = load_state4(P + ja), pb = load_state4(P + jb), ma = load_state4(M + ja),
+                    mb = load_state4(M + jb), va = load_state4(V + ja), vb = load_state4(V + jb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st->skip) {                          // overflow: this step changes nothing
+            if (n == UINT64_MAX)                 // never true: keeps the loads ahead of the test
+                P[ja] = pa + pb + ma + mb + va + vb + bits_of(ga) + bits_of(gb);
+            return;
+        }
+        const Coef c = coef(st);
         float g[8];
-        load_grad4(grad, ja, g);
-        load_grad4(grad, jb, g + 4);
-        const f32x4 pa = P[ja], pb = P[jb], ma = M[ja], mb = M[jb], va = V[ja], vb = V[jb];
+        widen(ga, g);
+        widen(gb, g + 4);
         float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
         float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
         float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-        // Keep the scheduler from sinking loads below arithmetic: with all
-        // eight in flight before the first wait the kernel runs about 1%
-        // faster than when it defers the two v loads.
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             update(g[k], p[k], m[k], v[k], c);
@@ -146,24 +173,30 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
         __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, V + jb);
         __builtin_nontemporal_store(to_f16x4(p), H + ja);
         __builtin_nontemporal_store(to_f16x4(p + 4), H + jb);
-    } else if (ja < ng) {                         // the last workgroup: group ja only
-        float g[4];
-        load_grad4(grad, ja, g);
-        const f32x4 pa = P[ja], ma = M[ja], va = V[ja];
-        float p[4] = {pa.x, pa.y, pa.z, pa.w};
-        float m[4] = {ma.x, ma.y, ma.z, ma.w};
-        float v[4] = {va.x, va.y, va.z, va.w};
+    } else {
+        if (st->skip)
+            return;
+        const Coef c = coef(st);
+        if (ja < ng) {                            // the last workgroup: group ja only
+            float g[4];
+            widen(load_grad_raw(grad, ja), g);
+            const f32x4 pa = P[ja], ma = M[ja], va = V[ja];
+            float p[4] = {pa.x, pa.y, pa.z, pa.w};
+            float m[4] = {ma.x, ma.y, ma.z, ma.w};
+            float v[4] = {va.x, va.y, va.z, va.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            update(g[k], p[k], m[k], v[k], c);
-        P[ja] = f32x4{p[0], p[1], p[2], p[3]};
-        M[ja] = f32x4{m[0], m[1], m[2], m[3]};
-        V[ja] = f32x4{v[0], v[1], v[2], v[3]};
-        H[ja] = to_f16x4(p);
+            for (int k = 0; k < 4; ++k)
+                update(g[k], p[k], m[k], v[k], c);
+            P[ja] = f32x4{p[0], p[1], p[2], p[3]};
+            M[ja] = f32x4{m[0], m[1], m[2], m[3]};
+            V[ja] = f32x4{v[0], v[1], v[2], v[3]};
+            H[ja] = to_f16x4(p);
+        }
     }
 
     // the last n % 4 parameters, one per thread of the first workgroup
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        const Coef c = coef(st);
         const uint64_t i = (ng << 2) + threadIdx.x;
         float p = p32[i], m = m32[i], v = v32[i];
         update(grad_at(grad, i), p, m, v, c);

@@ -162,12 +162,8 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
                                                                  uint32_t* __restrict__ blockmax)
 {
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
-    if (st->skip) {
-        if (n == UINT64_MAX)
-            occupancy_reserve[threadIdx.x] = 0;
-        return;
-    }
-    const Coef c = coef_of(st);
+    if (n == UINT64_MAX)
+        occupancy_reserve[threadIdx.x] = 0;
     const Groups gr(n);
     f32x4* __restrict__ M = reinterpret_cast<f32x4*>(m32);
     const f32x4* __restrict__ EW = reinterpret_cast<const f32x4*>(ew);
@@ -175,22 +171,33 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
     uint32_t mx = 0;
     if (gr.both()) {
         // the gradient is read once: nontemporal (5% faster than plain loads here)
-        const f16x4 ga = __builtin_bit_cast(f16x4, __builtin_nontemporal_load(G + gr.ja));
-        const f16x4 gb = __builtin_bit_cast(f16x4, __builtin_nontemporal_load(G + gr.jb));
+        const u32x2 ga = __builtin_nontemporal_load(G + gr.ja), gb = __builtin_nontemporal_load(G + gr.jb);
         f32x4 ma = M[gr.ja], mb = M[gr.jb];
         const f32x4 ea = EW[gr.ja], eb = EW[gr.jb];
         __builtin_amdgcn_sched_barrier(0);
-        momentum4(ga, ma, ea, c, mx);
-        momentum4(gb, mb, eb, c, mx);
+        // the loads are out before the skip flag is read (see loads_first_use)
+        if (st->skip) {
+            if (n == UINT64_MAX)
+                M[gr.ja] = ma + mb + ea + eb + bits_of(ga) + bits_of(gb);
+            return;
+        }
+        const Coef c = coef_of(st);
+        momentum4(__builtin_bit_cast(f16x4, ga), ma, ea, c, mx);
+        momentum4(__builtin_bit_cast(f16x4, gb), mb, eb, c, mx);
         M[gr.ja] = ma;
         M[gr.jb] = mb;
-    } else if (gr.first()) {
-        f32x4 ma = M[gr.ja];
-        momentum4(__builtin_bit_cast(f16x4, G[gr.ja]), ma, EW[gr.ja], c, mx);
-        M[gr.ja] = ma;
+    } else {
+        if (st->skip)
+            return;
+        if (gr.first()) {
+            f32x4 ma = M[gr.ja];
+            momentum4(__builtin_bit_cast(f16x4, G[gr.ja]), ma, EW[gr.ja], coef_of(st), mx);
+            M[gr.ja] = ma;
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
 #pragma clang fp contract(off)
+        const Coef c = coef_of(st);
         const uint64_t i = gr.ragged0 + threadIdx.x;
         const float gk = float(__builtin_bit_cast(_Float16, g16[i])) * c.gmul;
         const float mi = c.b1 * m32[i] + c.omb1 * gk;
@@ -394,12 +401,8 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
                                                                         uint32_t* __restrict__ blockmax)
 {
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
-    if (st->skip) {
-        if (n == UINT64_MAX)
-            occupancy_reserve[threadIdx.x] = 0;
-        return;
-    }
-    const float sw = ob->scale_w;
+    if (n == UINT64_MAX)
+        occupancy_reserve[threadIdx.x] = 0;
     const Groups gr(n);
     const f32x4* __restrict__ M = reinterpret_cast<const f32x4*>(m32);
     f32x4* __restrict__ EW = reinterpret_cast<f32x4*>(ew);
@@ -410,19 +413,30 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
         f32x4 ea = EW[gr.ja], eb = EW[gr.jb];
         const f32x4 sa = __builtin_nontemporal_load(ES + gr.ja), sb = __builtin_nontemporal_load(ES + gr.jb);
         __builtin_amdgcn_sched_barrier(0);
+        if (st->skip) {                          // loads first (see loads_first_use)
+            if (n == UINT64_MAX)
+                EW[gr.ja] = ma + mb + ea + eb + sa + sb;
+            return;
+        }
+        const float sw = ob->scale_w;
         nib_a = compress4(ma, ea, sa, sw, mx);
         nib_b = compress4(mb, eb, sb, sw, mx);
         __builtin_nontemporal_store(ea, EW + gr.ja);
         __builtin_nontemporal_store(eb, EW + gr.jb);
-    } else if (gr.first()) {
-        f32x4 ea = EW[gr.ja];
-        nib_a = compress4(M[gr.ja], ea, ES[gr.ja], sw, mx);
-        EW[gr.ja] = ea;
+    } else {
+        if (st->skip)
+            return;
+        if (gr.first()) {
+            f32x4 ea = EW[gr.ja];
+            nib_a = compress4(M[gr.ja], ea, ES[gr.ja], ob->scale_w, mx);
+            EW[gr.ja] = ea;
+        }
     }
     store_byte_pair(bits_w, gr.ja, nib_a, gr.first());
     store_byte_pair(bits_w, gr.jb, nib_b, gr.both());
     if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {     // the ragged last byte
         const uint64_t nvec = n >> 3;
+        const float sw = ob->scale_w;
         uint32_t byte = 0;
         for (uint64_t i = nvec << 3; i < n; ++i) {
             const float x = m32[i] + ew[i];
@@ -479,14 +493,9 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
                                                                const zero_step_state_t* __restrict__ st,
                                                                const zero_onebit_state_t* __restrict__ ob)
 {
-    extern __shared__ char occupancy_reserve[];
-    if (st->skip) {
-        if (n == UINT64_MAX)
-            occupancy_reserve[threadIdx.x] = 0;
-        return;
-    }
-    const Coef c = coef_of(st);
-    const float sw = ob->scale_w, ss = ob->scale_s;
+    extern __shared__ char occupancy_reserve[];  // see kOneShotCap
+    if (n == UINT64_MAX)
+        occupancy_reserve[threadIdx.x] = 0;
     const Groups gr(n);
     f32x4* __restrict__ ES = reinterpret_cast<f32x4*>(es);
     f32x4* __restrict__ P = reinterpret_cast<f32x4*>(p32);
@@ -495,13 +504,23 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
     u32x2* __restrict__ H = reinterpret_cast<u32x2*>(p16);
     uint32_t nib_a = 0, nib_b = 0;
     if (gr.both()) {
-        const uint32_t wa = nibble_of(bits_w, gr.ja), wb = nibble_of(bits_w, gr.jb);
+        // the payload bytes are loaded as they are; picking the nibble waits
+        // for them, so it comes after every load is out
+        const uint32_t ba = bits_w[gr.ja >> 1], bb = bits_w[gr.jb >> 1];
         // v is frozen (read only) and p is read once: nontemporal loads of both
         // made this kernel 5% faster, and the next momentum pass 1.4% slower
         f32x4 sa = ES[gr.ja], sb = ES[gr.jb];
         f32x4 pa = __builtin_nontemporal_load(P + gr.ja), pb = __builtin_nontemporal_load(P + gr.jb);
         const f32x4 va = __builtin_nontemporal_load(V + gr.ja), vb = __builtin_nontemporal_load(V + gr.jb);
         __builtin_amdgcn_sched_barrier(0);
+        if (st->skip) {                          // loads first (see loads_first_use)
+            if (n == UINT64_MAX)
+                P[gr.ja] = sa + sb + pa + pb + va + vb + float(ba + bb);
+            return;
+        }
+        const Coef c = coef_of(st);
+        const float sw = ob->scale_w, ss = ob->scale_s;
+        const uint32_t wa = (ba >> (4 * (gr.ja & 1))) & 15u, wb = (bb >> (4 * (gr.jb & 1))) & 15u;
         f32x4 ma, mb;
         u32x2 ha, hb;
         nib_a = server_update4(wa, sa, pa, va, ma, ha, sw, ss, c);
@@ -514,20 +533,27 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
         __builtin_nontemporal_store(pb, P + gr.jb);
         __builtin_nontemporal_store(ha, H + gr.ja);
         __builtin_nontemporal_store(hb, H + gr.jb);
-    } else if (gr.first()) {
-        f32x4 sa = ES[gr.ja], pa = P[gr.ja], ma;
-        u32x2 ha;
-        nib_a = server_update4(nibble_of(bits_w, gr.ja), sa, pa, V[gr.ja], ma, ha, sw, ss, c);
-        ES[gr.ja] = sa;
-        M[gr.ja] = ma;
-        P[gr.ja] = pa;
-        H[gr.ja] = ha;
+    } else {
+        if (st->skip)
+            return;
+        if (gr.first()) {
+            f32x4 sa = ES[gr.ja], pa = P[gr.ja], ma;
+            u32x2 ha;
+            nib_a = server_update4(nibble_of(bits_w, gr.ja), sa, pa, V[gr.ja], ma, ha, ob->scale_w, ob->scale_s,
+                                   coef_of(st));
+            ES[gr.ja] = sa;
+            M[gr.ja] = ma;
+            P[gr.ja] = pa;
+            H[gr.ja] = ha;
+        }
     }
     store_byte_pair(bits_s, gr.ja, nib_a, gr.first());
     store_byte_pair(bits_s, gr.jb, nib_b, gr.both());
     if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {
         const uint64_t nvec = n >> 3;
         const uint32_t bw = bits_w[nvec];
+        const Coef c = coef_of(st);
+        const float sw = ob->scale_w, ss = ob->scale_s;
         uint32_t bs = 0;
         for (uint64_t i = nvec << 3; i < n; ++i) {
             const float u = (((bw >> (i & 7)) & 1) ? sw : -sw) + es[i];

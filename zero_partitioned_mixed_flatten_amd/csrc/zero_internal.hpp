@@ -28,6 +28,22 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
+// ---- loads ahead of the skip test (loads_first_use) ---------------------------
+// The one-shot step kernels issue every load of a thread before they read the
+// step's skip flag: a wave that tests the flag first starts its streams one
+// scalar-load latency late (about 3% of the Adam kernel).  Used only on the
+// update path, the loads would be sunk by the compiler into that path, behind
+// the flag's wait; each kernel therefore also uses them on the skip path,
+// inside a test that no valid call passes (n == UINT64_MAX, which no launch
+// can have), so they stay ahead of the branch.  bits_of gathers a raw fp16
+// group's bits into one fp32 vector for that use.
+__device__ __forceinline__ f32x4 bits_of(u32x2 r)
+{
+    return f32x4{__builtin_bit_cast(float, r.x), __builtin_bit_cast(float, r.y), 0.0f, 0.0f};
+}
+
+__device__ __forceinline__ f32x4 bits_of(f32x4 r) { return r; }
+
 __host__ __device__ inline bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Records a HIP error for zero_status_string and maps it to ZERO_EHIP.
