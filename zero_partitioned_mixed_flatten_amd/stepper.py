@@ -42,6 +42,36 @@ def host_f32(n: int, huge_pages: bool = True):
     return t
 
 
+ARENA_ALIGN = 2 << 20      # every array starts at a 2 MiB boundary of the device address space ...
+ARENA_STAGGER = 64 << 10   # ... plus 64 KiB times its index in the arena
+
+
+def state_arena(device, specs):
+    """The flat per-parameter arrays of a shard, carved out of ONE zeroed device
+    allocation: specs is a sequence of (name, numel, torch dtype); array k
+    starts at a 2 MiB-aligned device address plus k * 64 KiB, and the arrays
+    follow each other in the given order.  Returns {name: tensor view}.
+
+    Why: the update streams all of these arrays at once, front by front.  On
+    MI355X the same Adam launch ran 1.4-3% faster on the gpt2 shard and 4-5%
+    faster on the 1T rank in this layout than on separate allocations, and
+    slower with no stagger or with a stagger of 16 KiB or 512 KiB (HIP events,
+    two boxes).  The views keep the arena alive."""
+    import torch
+    offs, end = [], 0
+    for k, (_, numel, dtype) in enumerate(specs):
+        start = -(-end // ARENA_ALIGN) * ARENA_ALIGN + k * ARENA_STAGGER
+        offs.append(start)
+        end = start + max(1, int(numel)) * torch.empty((), dtype=dtype).element_size()
+    arena = torch.zeros(end + ARENA_ALIGN, dtype=torch.uint8, device=device)
+    skip = (-arena.data_ptr()) % ARENA_ALIGN
+    out = {}
+    for (name, numel, dtype), off in zip(specs, offs):
+        nbytes = max(1, int(numel)) * torch.empty((), dtype=dtype).element_size()
+        out[name] = arena[skip + off:skip + off + nbytes].view(dtype)
+    return out
+
+
 def _segments(sources, segments, fn):
     """(tensor index, src_off, dst_off, count) -> ctypes segments, with every
     source range checked against its tensor on the host."""
@@ -58,16 +88,18 @@ class ShardStep:
     it copies and a decide-only pass folds them (no second read of the
     partition).  Both take bit-identical decisions."""
 
-    def __init__(self, n: int, device="cuda", fused: bool = False):
+    def __init__(self, n: int, device="cuda", fused: bool = False, extra=()):
+        """extra: further (name, numel, dtype) arrays placed in the same arena
+        after the five of the step (attributes of the same names)."""
         import torch
         self.n = int(n)
         alloc = max(1, self.n)
         self.device = torch.device(device)
-        self.p16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
-        self.grad16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
-        self.p32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
-        self.m32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
-        self.v32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        f32, f16 = torch.float32, torch.float16
+        arrays = state_arena(self.device, [("p32", alloc, f32), ("m32", alloc, f32), ("v32", alloc, f32),
+                                           ("grad16", alloc, f16), ("p16", alloc, f16), *extra])
+        for name, t in arrays.items():
+            setattr(self, name, t)
         self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
         ws = Z.zero_norm_workspace_bytes(self.n)
         self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
@@ -157,11 +189,11 @@ class AccumStep:
         self.n = int(n)
         alloc = max(1, self.n)
         self.device = torch.device(device)
-        self.p16 = torch.zeros(alloc, dtype=torch.float16, device=self.device)
-        self.grad32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
-        self.p32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
-        self.m32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
-        self.v32 = torch.zeros(alloc, dtype=torch.float32, device=self.device)
+        f32 = torch.float32
+        arrays = state_arena(self.device, [("p32", alloc, f32), ("m32", alloc, f32), ("v32", alloc, f32),
+                                           ("grad32", alloc, f32), ("p16", alloc, torch.float16)])
+        for name, t in arrays.items():
+            setattr(self, name, t)
         self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
         ws = Z.zero_norm_workspace_bytes(self.n)
         self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
@@ -251,11 +283,10 @@ class OneBitStep(ShardStep):
 
     def __init__(self, n: int, warmup: int, device="cuda"):
         import torch
-        super().__init__(n, device=device, fused=True)
-        alloc = max(1, self.n)
+        alloc = max(1, int(n))
+        super().__init__(n, device=device, fused=True,
+                         extra=[("err_w", alloc, torch.float32), ("err_s", alloc, torch.float32)])
         self.warmup = int(warmup)
-        self.err_w = torch.zeros(alloc, dtype=torch.float32, device=self.device)
-        self.err_s = torch.zeros(alloc, dtype=torch.float32, device=self.device)
         self.bits_w = torch.zeros((alloc + 7) // 8, dtype=torch.uint8, device=self.device)
         self.bits_s = torch.zeros((alloc + 7) // 8, dtype=torch.uint8, device=self.device)
         self.onebit = torch.zeros(Z.ONEBIT_STATE_BYTES, dtype=torch.uint8, device=self.device)
