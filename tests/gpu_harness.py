@@ -189,6 +189,7 @@ def step(r: Run, check: bool = True, check_full_cast: bool = True, exact: bool =
         assert e <= FP32_REL_TOL, (name, e)
     if check_full_cast and w.n:
         assert torch.equal(r.dev.p16[:w.n].view(torch.int16), r.dev.p32[:w.n].half().view(torch.int16))
+    assert r.dev.guard_intact(), "a kernel stored outside the shard's arrays (arena canary changed)"
     del dsrcs
     return {"gen_s": t1 - t0, "step_s": t2 - t1}
 
@@ -309,4 +310,5 @@ def step_accum(r: AccumRun, check: bool = True, exact: bool = True) -> None:
         assert e <= FP32_REL_TOL, (name, e)
     if w.n:
         assert torch.equal(r.dev.p16[:w.n].view(torch.int16), r.dev.p32[:w.n].half().view(torch.int16))
+    assert r.dev.guard_intact(), "a kernel stored outside the shard's arrays (arena canary changed)"
     del keep

@@ -90,6 +90,7 @@ class OneBitRun:
             got = _f32(t)[:n]
             assert np.array_equal(got, ref.view(np.uint32)), (name, int(np.sum(got != ref.view(np.uint32))))
         assert np.array_equal(H.bits16(self.dev.p16)[:n], self.p16)
+        assert self.dev.guard_intact(), "a kernel stored outside the shard's arrays (arena canary changed)"
         del dsrcs
 
 

@@ -44,32 +44,55 @@ def host_f32(n: int, huge_pages: bool = True):
 
 ARENA_ALIGN = 2 << 20      # every array starts at a 2 MiB boundary of the device address space ...
 ARENA_STAGGER = 64 << 10   # ... plus 64 KiB times its index in the arena
+ARENA_CANARY = 0xA5        # the byte every gap of the arena holds
 
 
-def state_arena(device, specs):
-    """The flat per-parameter arrays of a shard, carved out of ONE zeroed device
-    allocation: specs is a sequence of (name, numel, torch dtype); array k
-    starts at a 2 MiB-aligned device address plus k * 64 KiB, and the arrays
-    follow each other in the given order.  Returns {name: tensor view}.
+class StateArena:
+    """The flat per-parameter arrays of a shard, carved out of ONE device
+    allocation.  specs is a sequence of (name, numel, torch dtype); array k
+    starts at a 2 MiB-aligned device address plus k * 64 KiB, the arrays
+    follow each other in the given order, each zero-filled, and `arrays` maps
+    each name to its tensor view (the views keep the allocation alive).
 
     Why: the update streams all of these arrays at once, front by front.  On
     MI355X the same Adam launch ran 1.4-3% faster on the gpt2 shard and 4-5%
     faster on the 1T rank in this layout than on separate allocations, and
     slower with no stagger or with a stagger of 16 KiB or 512 KiB (HIP events,
-    two boxes).  The views keep the arena alive."""
-    import torch
-    offs, end = [], 0
-    for k, (_, numel, dtype) in enumerate(specs):
-        start = -(-end // ARENA_ALIGN) * ARENA_ALIGN + k * ARENA_STAGGER
-        offs.append(start)
-        end = start + max(1, int(numel)) * torch.empty((), dtype=dtype).element_size()
-    arena = torch.zeros(end + ARENA_ALIGN, dtype=torch.uint8, device=device)
-    skip = (-arena.data_ptr()) % ARENA_ALIGN
-    out = {}
-    for (name, numel, dtype), off in zip(specs, offs):
-        nbytes = max(1, int(numel)) * torch.empty((), dtype=dtype).element_size()
-        out[name] = arena[skip + off:skip + off + nbytes].view(dtype)
-    return out
+    two boxes).
+
+    Every byte outside the arrays -- at least 2 MiB before the first, at least
+    64 KiB between two, and the tail -- holds ARENA_CANARY, so a kernel that
+    stores past either end of an array changes a gap; `intact()` checks them
+    all (one device reduction and one host read)."""
+
+    def __init__(self, device, specs, canary: int = ARENA_CANARY):
+        import torch
+        layout, end = [], ARENA_ALIGN                # the first array starts one alignment in
+        for k, (_, numel, dtype) in enumerate(specs):
+            size = max(1, int(numel)) * torch.empty((), dtype=dtype).element_size()
+            start = -(-end // ARENA_ALIGN) * ARENA_ALIGN + k * ARENA_STAGGER
+            layout.append((start, size))
+            end = start + size
+        self.canary = int(canary)
+        self.tensor = torch.full((end + 2 * ARENA_ALIGN,), self.canary, dtype=torch.uint8, device=device)
+        skip = (-self.tensor.data_ptr()) % ARENA_ALIGN
+        self.arrays = {}
+        self.gaps = []
+        pos = 0
+        for (name, _, dtype), (start, size) in zip(specs, layout):
+            lo = skip + start
+            self.gaps.append((pos, lo))
+            view = self.tensor[lo:lo + size]
+            view.zero_()
+            self.arrays[name] = view.view(dtype)
+            pos = lo + size
+        self.gaps.append((pos, self.tensor.numel()))
+
+    def intact(self) -> bool:
+        """True if every gap still holds the canary byte (synchronises)."""
+        import torch
+        bad = torch.stack([(self.tensor[lo:hi] != self.canary).any() for lo, hi in self.gaps])
+        return not bool(bad.any().item())
 
 
 def _segments(sources, segments, fn):
@@ -96,9 +119,9 @@ class ShardStep:
         alloc = max(1, self.n)
         self.device = torch.device(device)
         f32, f16 = torch.float32, torch.float16
-        arrays = state_arena(self.device, [("p32", alloc, f32), ("m32", alloc, f32), ("v32", alloc, f32),
-                                           ("grad16", alloc, f16), ("p16", alloc, f16), *extra])
-        for name, t in arrays.items():
+        self.arena = StateArena(self.device, [("p32", alloc, f32), ("m32", alloc, f32), ("v32", alloc, f32),
+                                              ("grad16", alloc, f16), ("p16", alloc, f16), *extra])
+        for name, t in self.arena.arrays.items():
             setattr(self, name, t)
         self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
         ws = Z.zero_norm_workspace_bytes(self.n)
@@ -171,6 +194,11 @@ class ShardStep:
             self.norm_overflow(hp)
         self.adam()
 
+    def guard_intact(self) -> bool:
+        """True if no kernel has stored outside the shard's arrays (the
+        arena's canary gaps are unchanged); synchronises."""
+        return self.arena.intact()
+
     def read_state(self) -> Z.StepState:
         return Z.read_state(self.state)
 
@@ -190,9 +218,9 @@ class AccumStep:
         alloc = max(1, self.n)
         self.device = torch.device(device)
         f32 = torch.float32
-        arrays = state_arena(self.device, [("p32", alloc, f32), ("m32", alloc, f32), ("v32", alloc, f32),
-                                           ("grad32", alloc, f32), ("p16", alloc, torch.float16)])
-        for name, t in arrays.items():
+        self.arena = StateArena(self.device, [("p32", alloc, f32), ("m32", alloc, f32), ("v32", alloc, f32),
+                                              ("grad32", alloc, f32), ("p16", alloc, torch.float16)])
+        for name, t in self.arena.arrays.items():
             setattr(self, name, t)
         self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
         ws = Z.zero_norm_workspace_bytes(self.n)
@@ -269,6 +297,11 @@ class AccumStep:
             self.norm_overflow(hp)
         self.adam()
 
+    def guard_intact(self) -> bool:
+        """True if no kernel has stored outside the shard's arrays (the
+        arena's canary gaps are unchanged); synchronises."""
+        return self.arena.intact()
+
     def read_state(self) -> Z.StepState:
         return Z.read_state(self.state)
 
@@ -285,10 +318,9 @@ class OneBitStep(ShardStep):
         import torch
         alloc = max(1, int(n))
         super().__init__(n, device=device, fused=True,
-                         extra=[("err_w", alloc, torch.float32), ("err_s", alloc, torch.float32)])
+                         extra=[("err_w", alloc, torch.float32), ("err_s", alloc, torch.float32),
+                                ("bits_w", (alloc + 7) // 8, torch.uint8), ("bits_s", (alloc + 7) // 8, torch.uint8)])
         self.warmup = int(warmup)
-        self.bits_w = torch.zeros((alloc + 7) // 8, dtype=torch.uint8, device=self.device)
-        self.bits_s = torch.zeros((alloc + 7) // 8, dtype=torch.uint8, device=self.device)
         self.onebit = torch.zeros(Z.ONEBIT_STATE_BYTES, dtype=torch.uint8, device=self.device)
         self.onebit_ws = torch.empty(max(256, Z.zero_onebit_workspace_bytes(self.n)), dtype=torch.uint8,
                                      device=self.device)
