@@ -305,6 +305,10 @@ int zero_shard_norm_overflow_f32(const float* grad32, uint64_t n, const zero_hpa
  * It reads 2 + 12 bytes and writes 12 + 2 bytes per parameter.
  * All five arrays: device, n elements, 16-byte aligned, index-aligned with
  * each other and with the grad16 the decision was made on; n may be 0.
+ * Placement (performance only): the five arrays are streamed together; on
+ * MI355X the update is 1-5% faster when they share one allocation with array
+ * k (p32, m32, v32, grad16, p16) starting at a 2 MiB boundary plus k * 64 KiB,
+ * as the Python binding's StateArena lays them out.
  * dev_state: as left by zero_shard_norm_overflow (read only here).
  * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_ERANGE (n above about 2^42:
  *         more than 2^31 - 1 workgroups of 2048 parameters), ZERO_EHIP. */
