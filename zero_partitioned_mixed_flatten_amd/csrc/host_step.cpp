@@ -12,9 +12,12 @@
 //     every parallel phase splits its range into contiguous per-worker slices
 //     aligned to 64 elements, and the calling thread works as worker 0;
 //   * the update: 16 parameters per AVX-512 iteration, masked loads/stores at
-//     the slice edges, nontemporal stores for the body when the arrays are
-//     64-byte aligned (no read-for-ownership: 28 bytes of DRAM traffic per
-//     parameter instead of 42); every operation is one binary32
+//     the slice edges; in the body (arrays 64-byte aligned) plain stores of the
+//     fp32 p, m, v, which go back to the lines just loaded (no
+//     read-for-ownership; a nontemporal store to a line the core holds was
+//     8-28% slower on the two CPUs measured), and a nontemporal store of the
+//     fp16 copy, whose staging buffer is not read here (28 bytes of DRAM
+//     traffic per parameter); every operation is one binary32
 //     round-to-nearest-even operation in the order of the device kernel, and
 //     the fp16 copy is VCVTPS2PH with round-to-nearest-even;
 //   * the exact norm: the device's binary64 split (h = fma(x,x,C) - C,
@@ -225,10 +228,10 @@ ZERO_HOST_ISA inline void adam16(uint16_t* p16, float* p32, float* m32, float* v
                                    _mm512_mul_ps(_mm512_set1_ps(c.wd), p));
     const __m512 pn = _mm512_sub_ps(p, _mm512_mul_ps(_mm512_set1_ps(c.lr), u));
     const __m256i h = _mm512_cvtps_ph(pn, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
-    if (NT) {
-        _mm512_stream_ps(p32, pn);
-        _mm512_stream_ps(m32, mn);
-        _mm512_stream_ps(v32, vn);
+    if (NT) {                                    // aligned body: only the fp16 copy bypasses the caches
+        _mm512_store_ps(p32, pn);
+        _mm512_store_ps(m32, mn);
+        _mm512_store_ps(v32, vn);
         _mm256_stream_si256(reinterpret_cast<__m256i*>(p16), h);
     } else {
         _mm512_mask_storeu_ps(p32, mk, pn);
@@ -258,7 +261,7 @@ ZERO_HOST_ISA void adam_range(uint16_t* p16, float* p32, float* m32, float* v32,
         i = body;
         for (; i + 16 <= b; i += 16)
             adam16<true>(p16 + i, p32 + i, m32 + i, v32 + i, g16 + i, 0xFFFF, c);
-        _mm_sfence();                            // nontemporal stores visible before the pool returns
+        _mm_sfence();                            // the fp16 copy's nontemporal stores visible before the pool returns
     }
     for (; i < b; i += 16) {
         const uint64_t left = b - i;
