@@ -43,7 +43,7 @@ def _draw(case: int, tag: str) -> shardgen.Workload:
     return w
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(64))
 def test_random_fp16_step(case):
     w = _draw(case, "f16-")
     r = H.start(w, fused=bool(case % 2))
@@ -52,7 +52,7 @@ def test_random_fp16_step(case):
     assert r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(32))
 def test_random_accumulation_step(case):
     w = _draw(case, "f32-")
     r = H.start_accum(w, int(1 + case % 3), fused=bool(case % 2))
@@ -60,7 +60,7 @@ def test_random_accumulation_step(case):
         H.step_accum(r)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(32))
 def test_random_onebit_steps(case):
     from test_gpu_onebit import OneBitRun
     w = _draw(case, "1b-")
