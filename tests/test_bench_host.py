@@ -28,3 +28,18 @@ def test_code_hash_ignores_comment_edits_but_not_code(tmp_path):
 def test_measured_traffic_only_for_the_profiled_shard():
     assert bench.measured_traffic("fused", 12345) is None
     assert bench.measured_traffic(None, 97_350_700) is None
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    """bench.py measures one rank's shard on one GPU; asked for more (by flag or
+    by a distributed launcher's WORLD_SIZE) it exits with status 2 and says so,
+    before importing torch or touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           timeout=120, env=dict(os.environ, **env))
+        assert r.returncode == 2, (args, env, r.returncode, r.stderr[-500:])
+        assert "one GPU" in r.stderr and r.stdout == "", r.stderr[-500:]
