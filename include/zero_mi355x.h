@@ -275,6 +275,26 @@ int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hpar
                              zero_step_state_t* dev_state, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* zero_shard_norm_overflow without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same reduction, same kernels,
+ * same result bits and errors, except:
+ *   - the per-workgroup partials live in a fixed device array inside the
+ *     library (256 partials, 8 KiB), which each GPU the library runs on holds
+ *     from the first call on that GPU until the process ends; its device
+ *     address is looked up once per GPU, on that call, with that GPU current;
+ *   - hence n <= 2^30 (ZERO_ERANGE above; the largest n whose grid of at
+ *     most 256 workgroups fits the array);
+ *   - every call on one GPU shares that array, and each call leaves its
+ *     partials there: calls that overlap in time on one GPU (on different
+ *     streams, or from different host threads) race and give undefined
+ *     results -- order them on one stream.  Nothing in the array needs to
+ *     start at zero (every partial a call reads, the same call wrote).
+ * The call allocates nothing (no hipMalloc/hipFree, no allocating library
+ * routine).  The stream must belong to the current device. */
+int zero_shard_norm_overflow_noalloc(const uint16_t* grad16, uint64_t n, const zero_hparams_t* hp,
+                                     zero_step_state_t* dev_state, void* stream);
+
 /* Reduce and decide over an fp32 gradient partition (gradient
  * accumulation: a binary32 sum of micro-batch fp16 gradients).
  *   overflow = 1 if any element is inf or NaN or has |x| >= 2^24 (a sum of

@@ -1,0 +1,68 @@
+"""The fp16 reduction that allocates nothing (zero_shard_norm_overflow_noalloc)
+against the entry point it varies (zero_shard_norm_overflow with a caller
+workspace), through the C ABI: the whole 128-byte step state bit for bit,
+on calls in a row whose sizes shrink, so that the second call reads the
+library's scratch array right after a larger call has left its partials
+there; and the decision against the oracle."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import shardgen
+
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as H  # noqa: E402
+import zero_partitioned_mixed_flatten_amd as Z  # noqa: E402
+
+
+def _grad(n, seed, inject=None):
+    rng = np.random.default_rng(seed)
+    g = shardgen.to_f16_bits((rng.standard_normal(n) * 1e-3 * 2.0 ** 16).astype(np.float32))
+    if inject is not None:
+        g[inject[0]] = inject[1]
+    return g
+
+
+def _state_bytes(dev_state):
+    torch.cuda.synchronize()
+    return bytes(dev_state.cpu().numpy().tobytes())
+
+
+def test_noalloc_matches_workspace_form_on_shrinking_calls():
+    hp = Z.hparams()
+    hp_o = O.hparams()
+    st_ws = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    st_na = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st_ws, 2.0 ** 16)
+    Z.zero_step_state_init(st_na, 2.0 ** 16)
+    ref = O.new_state(2.0 ** 16)
+    # 256 workgroups, then 193 (an inf in the middle), then 2, then one
+    cases = [((1 << 26) + 5, 1, None), (3 * (1 << 20) + 7, 2, (1_234_567, 0x7C00)), (20_000, 3, None),
+             (1000, 4, None)]
+    for n, seed, inject in cases:
+        g = _grad(n, seed, inject)
+        dg = H.to_dev16(g)
+        ws = torch.empty(max(16, Z.zero_norm_workspace_bytes(n)), dtype=torch.uint8, device="cuda")
+        H.log(f"noalloc: n={n} seed={seed} inject={inject}")
+        Z.zero_shard_norm_overflow(dg, n, hp, st_ws, ws)
+        Z.zero_shard_norm_overflow_noalloc(dg, n, hp, st_na)
+        a, b = _state_bytes(st_ws), _state_bytes(st_na)
+        assert a == b, f"n={n}: step states differ"
+        O.decide(ref, hp_o, *O.norm_overflow(g))
+        H.compare_state(Z.read_state(st_na), ref, None if inject else H.exact_units(g))
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch():
+    # checked on the host before any device work: no launch happens
+    hp = Z.hparams()
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    g = torch.zeros(16, dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = Z.lib().zero_shard_norm_overflow_noalloc(g.data_ptr(), (1 << 30) + 1, C.byref(hp), st.data_ptr(), stream)
+    assert rc == -3                          # ZERO_ERANGE
+    rc = Z.lib().zero_shard_norm_overflow_noalloc(g.data_ptr(), 16, None, st.data_ptr(), stream)
+    assert rc == -1                          # ZERO_EINVAL

@@ -23,7 +23,7 @@ EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "ze
            "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32", "zero_host_create", "zero_host_destroy",
            "zero_host_threads", "zero_host_state_init", "zero_host_norm_overflow", "zero_host_adam_step",
            "zero_offload_step", "zero_host_stream_copy", "zero_onebit_state_init", "zero_onebit_workspace_bytes",
-           "zero_onebit_step")
+           "zero_onebit_step", "zero_shard_norm_overflow_noalloc")
 NORM_PARTIAL_BYTES = 32
 
 
@@ -97,6 +97,7 @@ def lib():
         L.zero_norm_workspace_bytes.restype = C.c_size_t
         L.zero_shard_norm_overflow.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
         L.zero_shard_norm_overflow_f32.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
+        L.zero_shard_norm_overflow_noalloc.argtypes = [vp, u64, C.POINTER(HParams), vp, vp]
         L.zero_shard_adam_step.argtypes = [vp, vp, vp, vp, vp, u64, vp, vp]
         L.zero_shard_adam_step_f32.argtypes = [vp, vp, vp, vp, vp, u64, vp, vp]
         L.zero_stream_copy.argtypes = [vp, vp, u64, vp]
@@ -225,6 +226,13 @@ def zero_shard_norm_overflow(grad16, n: int, hp: HParams, dev_state, workspace, 
     _check("zero_shard_norm_overflow",
            lib().zero_shard_norm_overflow(_ptr(grad16), n, C.byref(hp), _ptr(dev_state), _ptr(workspace),
                                           ws_bytes, _stream(stream)))
+
+
+def zero_shard_norm_overflow_noalloc(grad16, n: int, hp: HParams, dev_state, stream=None) -> None:
+    _need("zero_shard_norm_overflow_noalloc", grad16, 2 * n)
+    _need("zero_shard_norm_overflow_noalloc", dev_state, STATE_BYTES)
+    _check("zero_shard_norm_overflow_noalloc",
+           lib().zero_shard_norm_overflow_noalloc(_ptr(grad16), n, C.byref(hp), _ptr(dev_state), _stream(stream)))
 
 
 def zero_shard_norm_overflow_f32(grad32, n: int, hp: HParams, dev_state, workspace, stream=None) -> None:

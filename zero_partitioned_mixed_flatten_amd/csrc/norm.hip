@@ -29,6 +29,8 @@
 // step state and re-arms the counter.  No MFMA: 2 or 4 bytes per element.
 #include <math.h>
 
+#include <mutex>
+
 #include "decide.hpp"
 #include "exact_norm.hpp"
 
@@ -188,6 +190,71 @@ extern "C" int zero_shard_norm_overflow_f32(const float* grad32, uint64_t n, con
                                             size_t workspace_bytes, void* stream)
 {
     return norm_overflow(grad32, n, hp, dev_state, workspace, workspace_bytes, stream);
+}
+
+// ---- the fp16 reduction without a workspace argument ------------------------------
+
+namespace zero {
+namespace {
+
+// Scratch of zero_shard_norm_overflow_noalloc: the per-workgroup partials of
+// the standalone fp16 reduction, one per workgroup of its grid.  The array is
+// a host-side stand-in in host code; kernels get its device address from
+// scratch_address(), never its name.
+constexpr uint64_t kScratchPartials = kNormMaxBlocks;
+static __device__ __align__(256) NormPartial scratch[kScratchPartials];
+
+// The largest n whose grid fits the scratch array (norm_grid(n) <= 256: at
+// most 4096 elements per thread of 256 workgroups of 1024).
+constexpr uint64_t kNoAllocMaxElems = kScratchPartials * kNormBlock * kNormMaxPerThread;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy of the array).
+int scratch_address(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return ZERO_ERANGE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zero
+
+extern "C" int zero_shard_norm_overflow_noalloc(const uint16_t* grad16, uint64_t n, const zero_hparams_t* hp,
+                                                zero_step_state_t* dev_state, void* stream)
+{
+    if (!hp || !dev_state || (n && !grad16))
+        return ZERO_EINVAL;
+    if (!hparams_ok(hp))
+        return ZERO_EINVAL;
+    if ((n && !is_aligned(grad16, 16)) || !is_aligned(dev_state, 8))
+        return ZERO_EALIGN;
+    if (n > kNoAllocMaxElems)
+        return ZERO_ERANGE;
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc != ZERO_OK)
+        return rc;
+    // Every workgroup writes its own partial before the last one reads them,
+    // so nothing in the scratch array has to start at zero.
+    return norm_overflow(grad16, n, hp, dev_state, ws, kScratchPartials * sizeof(NormPartial), stream);
 }
 
 extern "C" int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,
