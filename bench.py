@@ -11,9 +11,11 @@ over the partition instead.  Both take bit-identical decisions.
 per-layer fp16 gradient sets added into an fp32 partition (the last one with
 the exact-norm partials), decide, and the update reading the fp32 gradient
 (30 bytes per parameter); a step is then one optimizer step over K
-micro-batches.  Default workload: the
-GPT-2 1.5B-like model (48 layers, hidden 1600, vocab 50257) partitioned over
-Nd = 16, rank 8: 97,350,700 parameters from 39 per-layer gradient segments.
+micro-batches.  Default workload: the largest shard that fits one GPU, the
+1T-parameter model over Nd = 1024 (ZeRO paper card, "Evidence": about 16 GB
+of model state per GPU), rank 512: 976,562,500 parameters from 17 per-layer
+gradient segments, flattened in 40 bucket calls of 25,000,000 elements
+(--workload gpt2 / 100b / tiny select the smaller shards).
 Inputs (fp32 masters, per-layer fp16 gradients) are synthetic, seeded, and
 resident in HBM before the timed region; four gradient sets are generated up
 front and used in turn.
@@ -26,8 +28,8 @@ stdout: one JSON line.  Progress goes to stderr.
                    against the 8 TB/s HBM peak; `traffic` is the measured HBM
                    bytes per launch from the committed rocprofv3 counter
                    summary when it was taken on the current kernel source
-  cpu_baseline     the CPU oracle (single thread) on a bounded number of full
-                   steps of the same shard
+  cpu_baseline     the CPU oracle (single thread) on at least 3 full steps of
+                   the same shard (more while --cpu-seconds lasts)
 """
 import argparse
 import hashlib
@@ -50,7 +52,7 @@ ACCUM_BYTES = 10         # read fp16 source and fp32 partition, write fp32 parti
 # 1-bit Adam compression stage, per parameter: momentum 14, worker sum 8, worker
 # compression 16 + 1/8, server sum 4 + 1/8, server compression + update 26 + 1/4
 ONEBIT_BYTES = 14 + 8 + 16.125 + 4.125 + 26.25
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "step_kernels_gpt2_shard_pmc.json")
+PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc")
 
 
@@ -89,12 +91,17 @@ def code_hash(path):
         return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
-def measured_traffic(path, n):
+def pmc_summary(workload):
+    """The committed counter summary of a workload's shard."""
+    return os.path.join(PROFILES, f"step_kernels_{workload}_shard_pmc.json")
+
+
+def measured_traffic(path, n, workload):
     """HBM bytes per step of the path's roofline kernel(s) from the committed
-    counter summary, or None when it is missing, for another shard size, for
-    another path, or taken on other kernel sources."""
+    counter summary of the workload, or None when it is missing, for another
+    shard size, for another path, or taken on other kernel sources."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(pmc_summary(workload)) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
@@ -138,10 +145,10 @@ class one_core:
         return False
 
 
-def cpu_baseline(w, p32, grads_host, budget_s, micro=0):
-    """The oracle on whole steps of the same shard until budget_s has passed
-    (at most 20 steps).  micro > 0: the gradient-accumulation step over that
-    many micro-batches."""
+def cpu_baseline(w, p32, grads_host, budget_s, micro=0, min_steps=3):
+    """The oracle on whole steps of the same shard: at least min_steps, then
+    more until budget_s has passed (at most 20 steps).  micro > 0: the
+    gradient-accumulation step over that many micro-batches."""
     import numpy as np
     import oracle as O
     import shardgen
@@ -164,7 +171,7 @@ def cpu_baseline(w, p32, grads_host, budget_s, micro=0):
             O.step(hp, st, srcs, w.layout.segments, grad, p16, p, m, v)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 20:
+        if (el >= budget_s and steps >= min_steps) or steps >= 20:
             break
     what = (f"{micro} fp16 micro-batches accumulated in fp32 + exact fp32 norm + decision + fp32 AdamW + "
             f"fp16 copy" if micro else "flatten + exact norm + decision + fp32 AdamW + fp16 copy")
@@ -361,7 +368,8 @@ def run_onebit(args, w, p32, grads_host, dev_sets, hp):
                    "step_bytes_per_param": FLATTEN_BYTES + ONEBIT_BYTES},
         "roofline": {"bound": "hbm", "kernel": "onebit_step (5 kernels)", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic("onebit", n), "algorithmic_bytes": ONEBIT_BYTES * n},
+                     "traffic": measured_traffic("onebit", n, args.workload),
+                     "algorithmic_bytes": ONEBIT_BYTES * n},
         "kernels_us": {"flatten_norm+decide": 1e3 * front_ms, "onebit_step": 1e3 * comp_ms},
         "scales": {"worker": ob.scale_w, "server": ob.scale_s},
         "cpu_baseline": cpu,
@@ -403,7 +411,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gpt2", choices=["tiny", "gpt2", "100b", "1t"])
+    ap.add_argument("--workload", default="1t", choices=["tiny", "gpt2", "100b", "1t"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate", "accum32", "offload", "onebit"])
     ap.add_argument("--threads", type=int, default=None,
                     help="host workers for --path offload (default: all CPUs but one)")
@@ -416,7 +424,8 @@ def main():
                     help="micro-batches per optimizer step for --path accum32")
     ap.add_argument("--graph", action="store_true",
                     help="fused/separate paths: replay each step as a captured HIP graph (one per gradient set)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="CPU-baseline budget; at least 3 whole oracle steps run whatever it is")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only the streaming-copy reference (for counter calibration)")
@@ -612,7 +621,7 @@ def main():
         with one_core():
             cpu = cpu_baseline(w, p32, grads_host, args.cpu_seconds, K if accum else 0)
 
-    traffic = measured_traffic(args.path if (not accum or K == 4) else None, n)
+    traffic = measured_traffic(args.path if (not accum or K == 4) else None, n, args.workload)
     if accum:
         step_bpp = WIDEN_BYTES + ACCUM_BYTES * (K - 1) + ADAM32_BYTES
     else:

@@ -26,8 +26,9 @@ def test_code_hash_ignores_comment_edits_but_not_code(tmp_path):
 
 
 def test_measured_traffic_only_for_the_profiled_shard():
-    assert bench.measured_traffic("fused", 12345) is None
-    assert bench.measured_traffic(None, 97_350_700) is None
+    assert bench.measured_traffic("fused", 12345, "gpt2") is None
+    assert bench.measured_traffic(None, 97_350_700, "gpt2") is None
+    assert bench.measured_traffic("fused", 97_350_700, "no-such-workload") is None
 
 
 def test_more_than_one_gpu_is_refused_before_any_device_work():
