@@ -8,10 +8,10 @@ zero_oracle.c; zero_oracle.py only marshals numpy arrays.
 """
 from .zero_oracle import (OracleHParams, OracleState, adam_update, adam_update_f32, decide,
                           f16_from_f32, f32_from_f16, flatten, hparams, lib, new_state,
-                          norm_overflow, norm_overflow_f32, onebit_pack, onebit_scale, onebit_scale_units, onebit_step,
+                          norm_overflow, norm_overflow_f32, onebit_pack, onebit_scale, onebit_step,
                           state_bytes, step)
 
 __all__ = ["OracleHParams", "OracleState", "adam_update", "adam_update_f32", "decide",
            "f16_from_f32", "f32_from_f16", "flatten", "hparams", "lib", "new_state",
-           "norm_overflow", "norm_overflow_f32", "onebit_pack", "onebit_scale", "onebit_scale_units", "onebit_step", "state_bytes",
+           "norm_overflow", "norm_overflow_f32", "onebit_pack", "onebit_scale", "onebit_step", "state_bytes",
            "step"]

@@ -32,6 +32,10 @@
  * Every function here is pinned by a CPU test against something other than
  * itself (page figures, closed forms, numpy's binary16 routines, exact
  * rational sums, math.fsum).  No function is "parity unpinned".
+ *
+ * The sums of squares are the plain definition: every square exact, the
+ * sum exact, one rounding to binary64 at the end (wide_t below).  No
+ * window, grid or domain bound enters them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -199,79 +203,133 @@ void oracle_flatten(const oracle_segment_t* segs, uint32_t nsegs, void* dst,
 }
 
 /* ------------------------------------------------------------------ */
-/* Exact sums of squares are held as integer counts of 2^-48 units in   */
-/* 128 bits.  A sum that reaches 2^128 units (2^80) cannot be held; it  */
-/* is reported like an inf/NaN gradient (overflow, step skipped, scale  */
-/* backed off).  Neither gradient type can get there on a real shard:   */
-/* binary16 squares stay below 2^80 units, so it takes 2^48 elements.   */
+/* Exact sum of squares, rounded once.  Every binary32 value (and so    */
+/* every binary16 value) is x = M * 2^e with M an integer below 2^24   */
+/* and e >= -149, so x^2 = M^2 * 2^(2e) is an integer number of units   */
+/* of 2^-298 (the square of the smallest subnormal), below 2^256.  The  */
+/* sum is kept as that integer, in base-2^32 digits (one per 64-bit    */
+/* word, carried every 2^31 additions), converted to binary64 once,   */
+/* rounding to nearest with ties to even.  640 bits hold the sum of    */
+/* more than 2^80 squares of the largest binary32, so the integer never */
+/* wraps on any input this oracle can be given.                        */
 /* ------------------------------------------------------------------ */
-static int add_units(unsigned __int128* acc, unsigned __int128 u)
+#define WIDE_DIGITS 20
+#define WIDE_UNIT_EXP (-298)
+
+typedef struct {
+    uint64_t d[WIDE_DIGITS];                 /* digit k weighs 2^(32k) units */
+    uint64_t adds;                           /* additions since the last carry */
+} wide_t;
+
+/* Brings every digit back below 2^32 (the value is unchanged). */
+static void wide_carry(wide_t* w)
 {
-    unsigned __int128 t = *acc + u;
-    if (t < *acc)
-        return 1;                                       /* wrapped: >= 2^128 */
-    *acc = t;
-    return 0;
+    for (int j = 0; j < WIDE_DIGITS - 1; ++j) {
+        w->d[j + 1] += w->d[j] >> 32;
+        w->d[j] &= 0xffffffffu;
+    }
+    w->adds = 0;
+}
+
+static void wide_add_square(wide_t* w, float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, sizeof b);
+    uint32_t field = (b >> 23) & 0xffu;      /* the caller passes finite values only */
+    uint64_t M = b & 0x7fffffu;              /* |x| = M * 2^e (IEEE-754 binary32): */
+    int e = -149;                            /*   subnormal or zero: e = -149 */
+    if (field != 0) {                        /*   normal: hidden bit, e = field - 150 */
+        M |= 0x800000u;
+        e = (int)field - 150;
+    }
+    int pos = 2 * e - WIDE_UNIT_EXP;         /* x^2 = M^2 * 2^pos units, pos >= 0 */
+    unsigned __int128 v = (unsigned __int128)(M * M) << (pos % 32);   /* below 2^80 */
+    int k = pos / 32;
+    /* Each digit gets less than 2^32 per addition, so 2^31 additions fit in
+     * its 64-bit word before the carry. */
+    w->d[k] += (uint64_t)v & 0xffffffffu;
+    w->d[k + 1] += (uint64_t)(v >> 32) & 0xffffffffu;
+    w->d[k + 2] += (uint64_t)(v >> 64);
+    if (++w->adds == (1u << 31))
+        wide_carry(w);
+}
+
+static int wide_bit(const wide_t* w, int i)
+{
+    return (int)((w->d[i / 32] >> (i % 32)) & 1u);
+}
+
+/* The integer times 2^-298, rounded to the nearest binary64, ties to even. */
+static double wide_to_double(wide_t* w)
+{
+    wide_carry(w);
+    int top = -1;                            /* index of the highest set bit */
+    for (int i = 32 * WIDE_DIGITS - 1; i >= 0 && top < 0; --i)
+        if (wide_bit(w, i))
+            top = i;
+    if (top < 0)
+        return 0.0;
+    int low = top - 52;                      /* the lowest bit a binary64 significand keeps */
+    if (low < 0)
+        low = 0;
+    uint64_t m = 0;                          /* bits top..low: at most 53 of them */
+    for (int i = top; i >= low; --i)
+        m = (m << 1) | (uint64_t)wide_bit(w, i);
+    if (low > 0) {
+        int round = wide_bit(w, low - 1);
+        int sticky = 0;
+        for (int i = low - 2; i >= 0; --i)
+            sticky |= wide_bit(w, i);
+        if (round && (sticky || (m & 1u)))
+            m += 1;                          /* may reach 2^53: still exact in binary64 */
+    }
+    return ldexp((double)m, low + WIDE_UNIT_EXP);
 }
 
 /* ------------------------------------------------------------------ */
 /* Squared L2 norm and the inf/NaN test of the flat binary16 gradient.  */
 /* overflow = some element has an all-ones exponent (inf or NaN).       */
-/* sumsq    = sum over i of g_i^2, computed EXACTLY and rounded once to  */
-/*            binary64.  Each g_i^2 is an integer multiple of 2^-48 (the */
-/*            square of the smallest subnormal, 2^-24) below 2^32, so   */
-/*            the sum is an integer count of 2^-48 units, converted     */
-/*            with one rounding.  When overflow is set the sum has no   */
-/*            meaning and is +inf.                                      */
+/* sumsq    = sum over i of g_i^2, exact, rounded once to binary64.    */
+/* When overflow is set the sum has no meaning and is +inf.            */
 /* ------------------------------------------------------------------ */
 void oracle_norm_overflow(const uint16_t* g, uint64_t n, double* sumsq, int32_t* overflow)
 {
-    unsigned __int128 units = 0;
-    int32_t ovf = 0;
-    for (uint64_t i = 0; i < n && !ovf; ++i) {
+    wide_t w;
+    memset(&w, 0, sizeof w);
+    for (uint64_t i = 0; i < n; ++i) {
         if ((g[i] & 0x7c00u) == 0x7c00u) {
-            ovf = 1;
-            break;
+            *overflow = 1;
+            *sumsq = INFINITY;
+            return;
         }
-        double x = (double)oracle_f32_from_f16(g[i]);
-        double sq = x * x;                              /* exact: 22 bits */
-        ovf = add_units(&units, (unsigned __int128)(sq * 0x1p48));   /* integer < 2^80 */
+        wide_add_square(&w, oracle_f32_from_f16(g[i]));
     }
-    *overflow = ovf;
-    *sumsq = ovf ? INFINITY : (double)units * 0x1p-48;  /* one rounding */
+    *overflow = 0;
+    *sumsq = wide_to_double(&w);
 }
 
 /* ------------------------------------------------------------------ */
 /* The same reduction over an fp32 gradient partition (the gradient-    */
 /* accumulation form: micro-batch fp16 gradients summed in fp32; the    */
 /* DeepSpeed article leaves gradient accumulation to the library).      */
-/* overflow = some element is inf or NaN or has |x| >= 2^24.  A sum of  */
-/*            at most 256 binary16 values stays below 2^24, so on the   */
-/*            accumulation domain this is the inf/NaN test; larger      */
-/*            values are treated as an overflow of the scaled gradient. */
-/* sumsq    = sum over i of x_i^2, each square rounded to the nearest   */
-/*            multiple of 2^-48, summed exactly and rounded once to     */
-/*            binary64.  A binary32 sum of binary16 values is a        */
-/*            multiple of 2^-24, so on the accumulation domain every    */
-/*            square is already on that grid and this is the exact sum. */
-/*            (A square x^2 = M^2 2^(2E) never lies exactly halfway     */
-/*            between two multiples of 2^-48, so no tie rule is needed.)*/
+/* overflow = some element is inf or NaN.                               */
+/* sumsq    = sum over i of x_i^2, exact, rounded once to binary64     */
+/*            (never infinite: every square is below 2^256).           */
 /* ------------------------------------------------------------------ */
 void oracle_norm_overflow_f32(const float* g, uint64_t n, double* sumsq, int32_t* overflow)
 {
-    unsigned __int128 units = 0;
-    int32_t ovf = 0;
-    for (uint64_t i = 0; i < n && !ovf; ++i) {
-        double x = (double)g[i];
-        if (!(fabs(x) < 0x1p24)) {                      /* inf, NaN or out of domain */
-            ovf = 1;
-            break;
+    wide_t w;
+    memset(&w, 0, sizeof w);
+    for (uint64_t i = 0; i < n; ++i) {
+        if (!isfinite(g[i])) {
+            *overflow = 1;
+            *sumsq = INFINITY;
+            return;
         }
-        double sq = x * x;                              /* exact: 48 bits, < 2^48 */
-        ovf = add_units(&units, (unsigned __int128)nearbyint(sq * 0x1p48));   /* < 2^96 */
+        wide_add_square(&w, g[i]);
     }
-    *overflow = ovf;
-    *sumsq = ovf ? INFINITY : (double)units * 0x1p-48;
+    *overflow = 0;
+    *sumsq = wide_to_double(&w);
 }
 
 /* ------------------------------------------------------------------ */
@@ -445,55 +503,20 @@ void oracle_step(const oracle_hparams_t* hp, oracle_state_t* st,
 /* The compressor C[x] = s * sgn(x), one bit per element plus one       */
 /* scale per vector: sgn(x) = +1 for x >= 0 (zeros included) and -1     */
 /* otherwise; s = ||x||_2 / sqrt(d) in fp32, so that C[x] keeps the L2  */
-/* norm of x.  The sum of squares is exact: with E the binary exponent  */
-/* of max|x|, each square is rounded to the nearest multiple of         */
-/* q = 2^(2E-80) (no square is ever halfway: x^2/q is an integer times  */
-/* an even power of two), the integers are summed exactly (each is      */
-/* below 2^82), and S = sum*q is rounded once to binary64; then         */
-/* s = fp32(sqrt(S / d)).  A square below q/2 (below 2^-81 of the       */
-/* largest) contributes nothing.                                        */
+/* norm of x.  S = sum of x_i^2 exactly, rounded once to binary64 (the  */
+/* same exact sum as the gradient norm), then s = fp32(sqrt(S / d))     */
+/* with correctly rounded binary64 division and square root.            */
 /* ------------------------------------------------------------------ */
-/* units_out (optional): the exact integer sum (low, high 64 bits) and the
- * window exponent 2E-80, so that S = units * 2^(2E-80) before rounding. */
-float oracle_onebit_scale_units(const float* x, uint64_t n, double* sumsq_out, uint64_t* units_out, int* qexp_out)
-{
-    double big = 0.0;
-    for (uint64_t i = 0; i < n; ++i)
-        if (fabs((double)x[i]) > big)
-            big = fabs((double)x[i]);
-    if (big == 0.0) {
-        if (sumsq_out)
-            *sumsq_out = 0.0;
-        if (units_out)
-            units_out[0] = units_out[1] = 0;
-        if (qexp_out)
-            *qexp_out = 0;
-        return 0.0f;
-    }
-    int ex;
-    frexp(big, &ex);                                    /* big = f * 2^ex, f in [0.5, 1) */
-    const int E = ex - 1;                               /* 2^E <= max|x| < 2^(E+1) */
-    unsigned __int128 units = 0;
-    for (uint64_t i = 0; i < n; ++i) {
-        double sq = (double)x[i] * (double)x[i];        /* exact: 48 bits */
-        double y = ldexp(sq, 80 - 2 * E);               /* exact power-of-two scaling, < 2^82 */
-        units += (unsigned __int128)nearbyint(y);
-    }
-    double S = ldexp((double)units, 2 * E - 80);        /* one rounding */
-    if (sumsq_out)
-        *sumsq_out = S;
-    if (units_out) {
-        units_out[0] = (uint64_t)units;
-        units_out[1] = (uint64_t)(units >> 64);
-    }
-    if (qexp_out)
-        *qexp_out = 2 * E - 80;
-    return (float)sqrt(S / (double)n);
-}
-
 float oracle_onebit_scale(const float* x, uint64_t n, double* sumsq_out)
 {
-    return oracle_onebit_scale_units(x, n, sumsq_out, 0, 0);
+    wide_t w;
+    memset(&w, 0, sizeof w);
+    for (uint64_t i = 0; i < n; ++i)
+        wide_add_square(&w, x[i]);
+    double S = wide_to_double(&w);
+    if (sumsq_out)
+        *sumsq_out = S;
+    return n ? (float)sqrt(S / (double)n) : 0.0f;
 }
 
 /* Sign bits, little-endian within each byte: bit k of byte j is element 8j+k,

@@ -63,8 +63,6 @@ def lib():
         L.oracle_adam_update_f32.argtypes = [C.POINTER(OracleState), vp, vp, vp, vp, vp, u64]
         L.oracle_onebit_scale.argtypes = [vp, u64, C.POINTER(C.c_double)]
         L.oracle_onebit_scale.restype = C.c_float
-        L.oracle_onebit_scale_units.argtypes = [vp, u64, C.POINTER(C.c_double), vp, C.POINTER(C.c_int)]
-        L.oracle_onebit_scale_units.restype = C.c_float
         L.oracle_onebit_pack.argtypes = [vp, u64, vp]
         L.oracle_onebit_step.argtypes = [C.POINTER(OracleState), vp, vp, vp, vp, vp, vp, vp, u64, vp, vp, vp]
         L.oracle_onebit_step.restype = C.c_int
@@ -196,21 +194,11 @@ def step(hp: OracleHParams, st: OracleState, srcs, segments, grad16, p16, p32, m
 # ---- 1-bit Adam, compression stage -----------------------------------------------
 
 def onebit_scale(x: np.ndarray):
-    """-> (s, S): the fp32 scale ||x||_2/sqrt(d) from the exact windowed sum S."""
+    """-> (s, S): the fp32 scale ||x||_2/sqrt(d) from the exact sum of squares S."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     S = C.c_double()
     s = lib().oracle_onebit_scale(_ptr(x, np.float32), x.size, C.byref(S))
     return float(np.float32(s)), S.value
-
-
-def onebit_scale_units(x: np.ndarray):
-    """-> (s, S, units, qexp): also the exact integer sum and the window exponent."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    S = C.c_double()
-    u = np.zeros(2, np.uint64)
-    e = C.c_int()
-    s = lib().oracle_onebit_scale_units(_ptr(x, np.float32), x.size, C.byref(S), u.ctypes.data, C.byref(e))
-    return float(np.float32(s)), S.value, (int(u[1]) << 64) | int(u[0]), e.value
 
 
 def onebit_pack(x: np.ndarray) -> np.ndarray:

@@ -82,9 +82,8 @@ int main(void)
                 return 3;
             oracle_step(&hp, &st, segs, ns, g16, p16, p32, m32, v32, n);
         }
-        uint64_t units[2];
-        int qexp;
-        (void)oracle_onebit_scale_units(p32, n, NULL, units, &qexp);
+        double scale_sum;
+        (void)oracle_onebit_scale(p32, n, &scale_sum);
         oracle_onebit_pack(p32, n, bw);
         oracle_f32_from_f16_array(p16, g32, n);
         oracle_f16_from_f32_array(g32, p16, n);

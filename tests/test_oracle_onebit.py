@@ -2,13 +2,14 @@
 Algorithm 1: frozen variance, scaled-sign momentum compression with worker and
 server error feedback; one data-parallel rank is its own server).
 
-The scale s = ||x||_2/sqrt(d) comes from an exact windowed sum; it is checked
-against exact rational arithmetic in Python integers, against closed forms
-(equal magnitudes, one nonzero element, powers of two), and by its norm-
-preserving property.  The sign bits are checked against numpy's packbits.
-The step is checked against closed forms of the algorithm (equal-magnitude
-momentum compresses without error, error feedback telescopes, the variance
-stays frozen) rather than a retyped copy of it."""
+The scale s = ||x||_2/sqrt(d) comes from the exact sum of squares rounded once
+to binary64; the sum is checked against exact rational arithmetic
+(fractions.Fraction, whose float() rounds correctly) and math.fsum, and s
+against closed forms (equal magnitudes, one nonzero element, powers of two)
+and its norm-preserving property.  The sign bits are checked against numpy's
+packbits.  The step is checked against closed forms of the algorithm
+(equal-magnitude momentum compresses without error, error feedback
+telescopes, the variance stays frozen) rather than a retyped copy of it."""
 import math
 from fractions import Fraction
 
@@ -20,43 +21,35 @@ import shardgen
 LR, B1, EPS, WD = 1e-4, 0.9, 1e-8, 0.01
 
 
-def _exact_scale(x):
-    """The definition in exact rationals: window from max|x|, each square
-    rounded half-even to q = 2^(2E-80), the sum rounded once to binary64,
-    s = fp32(sqrt(S/d)) with correctly rounded binary64 sqrt and division.
-    -> (s, S, units, qexp)."""
-    xs = [Fraction(float(v)) for v in x.astype(np.float64)]
-    big = max((abs(v) for v in xs), default=Fraction(0))
-    if big == 0:
-        return 0.0, 0.0, 0, 0
-    E = math.frexp(float(big))[1] - 1
-    q = Fraction(2) ** (2 * E - 80)
-    units = sum(round(v * v / q) for v in xs)
-    S = float(units * q)
-    return float(np.float32(math.sqrt(S / len(xs)))), S, units, 2 * E - 80
+def _exact_sum(x):
+    """The sum of squares as an exact rational, rounded once by float()."""
+    return float(sum((Fraction(float(v)) ** 2 for v in x.astype(np.float64)), Fraction(0)))
 
 
 @pytest.mark.parametrize("seed", range(6))
-def test_scale_matches_exact_rationals(oracle, seed):
+def test_scale_sum_matches_exact_rationals(oracle, seed):
+    # magnitudes spread over 40 binades starting anywhere from 2^-140
     rng = np.random.default_rng(seed)
     n = int(rng.integers(1, 500))
     mant = rng.integers(1 << 23, 1 << 24, n).astype(np.float64)
     lo = int(rng.integers(-140, -10))
     x = (mant * np.exp2(rng.integers(lo, lo + 40, n).astype(np.float64))).astype(np.float32)
     x *= np.where(rng.integers(0, 2, n) == 1, -1, 1).astype(np.float32)
-    assert oracle.onebit_scale_units(x) == _exact_scale(x)
-    assert oracle.onebit_scale(x) == _exact_scale(x)[:2]
+    s, S = oracle.onebit_scale(x)
+    assert S == _exact_sum(x)
+    assert S == math.fsum(x.astype(np.float64) ** 2)
+    assert s == np.float32(math.sqrt(S / n))        # correctly rounded binary64 division and root
 
 
-def test_scale_window_rounds_each_square(oracle):
-    # 1.0 sets E = 0 and q = 2^-80.  2^-41 squared is 0.25 q -> 0; 3*2^-41
-    # squared is 2.25 q -> 2; 3*2^-42 squared is 0.5625 q -> 1; 7*2^-42 squared
-    # is 3.0625 q -> 3
-    x = np.array([1.0, 2.0 ** -41, 3 * 2.0 ** -41, 3 * 2.0 ** -42, 7 * 2.0 ** -42], np.float32)
-    s, S, units, qexp = oracle.onebit_scale_units(x)
-    assert qexp == -80 and units == (1 << 80) + 2 + 1 + 3
-    assert S == float(Fraction(units, 1 << 80))
-    assert s == np.float32(math.sqrt(S / 5))
+def test_scale_keeps_squares_far_below_the_largest(oracle):
+    # 1 + 2 * 2^-54 lies exactly halfway between 1 and 1 + 2^-52, so the
+    # 2^-120 from 2^-60 decides the rounding of the sum (upward); without it
+    # the tie goes to even.
+    x = np.array([1.0, 2.0 ** -27, -(2.0 ** -27), 2.0 ** -60], np.float32)
+    assert oracle.onebit_scale(x)[1] == 1.0 + 2.0 ** -52
+    assert oracle.onebit_scale(x[:3])[1] == 1.0
+    y = np.array([2.0 ** 100, 2.0 ** -149], np.float32)              # 2^200 + 2^-298: rounds to 2^200
+    assert oracle.onebit_scale(y)[1] == 2.0 ** 200
 
 
 def test_scale_closed_forms(oracle):
