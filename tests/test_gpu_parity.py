@@ -71,13 +71,27 @@ def test_empty_shard(fused):
     assert s.sumsq == 0.0 and s.step == 1 and s.overflow == 0
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_gpt2_shard_full_size(fused):
+def test_gpt2_shard_full_size_separate_path():
     w = shardgen.workload("gpt2")
-    r = H.start(w, sample=1 << 20, fused=fused)
+    r = H.start(w, sample=1 << 20, fused=False)
     for _ in range(3):
         t = H.step(r)
         H.log(f"gpt2 timings {t}")
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+@pytest.mark.timeout(900)
+def test_gpt2_shard_all_100_steps():
+    """The GPT-2 1.5B-like workload at its stated length: 100 fused steps on
+    the full rank-8 shard, every step's decision and state bitwise, sampled
+    elements against the oracle, the whole-shard fp16 cast every 10th step."""
+    w = shardgen.workload("gpt2")
+    assert w.steps == 100
+    r = H.start(w, sample=1 << 16, fused=True)
+    for k in range(1, w.steps + 1):
+        H.step(r, check_full_cast=(k % 10 == 0), exact=(k % 25 == 0))
+    s = r.dev.read_state()
+    assert (s.step, s.skipped_total) == (100, 0) and s.loss_scale == 2.0 ** (16 + 5), s.as_dict()
     assert r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
@@ -100,22 +114,44 @@ def test_stress_loss_scale_trajectory_full_size():
     assert (s.loss_scale, s.good_steps, s.step, s.skipped_total) == (2.0 ** 26, 13, 98, 2)
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_100b_shard_full_size(fused):
+def test_100b_shard_full_size_separate_path():
     w = shardgen.workload("100b")
-    r = H.start(w, sample=1 << 20, fused=fused)
+    r = H.start(w, sample=1 << 20, fused=False)
     for _ in range(2):
         H.step(r)
 
 
 @pytest.mark.timeout(900)
-def test_1t_shard_full_size_bucketed():
+def test_100b_shard_all_50_steps_clipping():
+    """The 100B workload at its stated length: 50 fused steps on the rank-12
+    shard with clipping active on every step (the gradient norm stays above
+    1), so the bias corrections ramp through 50 clipped updates."""
+    w = shardgen.workload("100b")
+    assert w.steps == 50
+    r = H.start(w, sample=1 << 16, fused=True)
+    for k in range(1, w.steps + 1):
+        H.step(r, check_full_cast=(k % 10 == 0), exact=False)
+        assert r.st.grad_norm > w.hp.max_grad_norm, (k, r.st.grad_norm)
+    s = r.dev.read_state()
+    assert (s.step, s.skipped_total) == (50, 0), s.as_dict()
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+@pytest.mark.timeout(900)
+def test_1t_shard_all_20_steps_bucketed():
+    """The 1T workload at its stated length: 20 fused steps on the rank-512
+    shard, each flattened in 40 bucket calls of 25M elements; the loss scale
+    grows at the 20th clean step."""
     w = shardgen.workload("1t")
-    r = H.start(w, sample=1 << 20, fused=True)
+    assert w.steps == 20
+    r = H.start(w, sample=1 << 16, fused=True)
     assert len(r.dev.buckets) == 0
-    for _ in range(2):
-        H.step(r)
+    for k in range(1, w.steps + 1):
+        H.step(r, check_full_cast=(k % 10 == 0), exact=False)
         assert len(r.dev.buckets) == 40
+    s = r.dev.read_state()
+    assert (s.step, s.skipped_total, s.good_steps) == (20, 0, 0) and s.loss_scale == 2.0 ** 17, s.as_dict()
+    assert r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
 @pytest.mark.parametrize("dtype,acc", [(Z.ZERO_F16, False), (Z.ZERO_F16, True), (Z.ZERO_F32, False),
