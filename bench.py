@@ -309,7 +309,7 @@ def run_onebit(args, w, p32, grads_host, dev_sets, hp):
         dev.set_segments(d, w.layout.segments, w.bucket_elems)
         plans.append(dev.buckets)
     k = 0
-    while not dev.compressing():                      # the warm-up, with its host read-back
+    while not dev.compressing():                      # the warm-up (compressing() reads the state back)
         dev.buckets = plans[k % len(plans)]
         dev.step(hp)
         k += 1
@@ -322,7 +322,7 @@ def run_onebit(args, w, p32, grads_host, dev_sets, hp):
         dev.flatten_norm()
         dev.decide(hp)
         rec(1)
-        dev.compress()
+        dev.update()                                  # the compression stage (the device chooses it)
         rec(2)
 
     for i in range(args.warmup):

@@ -36,9 +36,9 @@
  *     fused zero_flatten_norm_bucket_f32 for the last micro-batch), and the
  *     *_f32 reduction and update read that fp32 gradient (30 bytes per
  *     parameter in the update);
- *   - 1-bit Adam (DeepSpeed article): after a warm-up of ordinary steps,
- *     zero_onebit_step compresses the momentum to one bit per element with
- *     error feedback and updates with the frozen variance;
+ *   - 1-bit Adam (DeepSpeed article): zero_onebit_step runs ordinary steps
+ *     for a warm-up, then compresses the momentum to one bit per element
+ *     with error feedback and updates with the frozen variance;
  *   - host step (ZeRO-Offload, in the DeepSpeed article: ZeRO-2 plus CPU
  *     memory): the fp32 master parameters, momentum and variance live in host
  *     memory and the CPU steps them (zero_host_*, zero_offload_step), with
@@ -130,17 +130,23 @@ typedef struct {
                                    gradient, rounded once to binary64;
                                    +inf when overflow is set */
     double   grad_norm;         /* sqrt(sumsq) / S (unscaled norm); +inf on overflow */
-    int32_t  overflow;          /* 1 if the gradient holds an inf or NaN (or,
-                                   in fp32, a value of magnitude >= 2^24) */
-    int32_t  skip;              /* 1 if this step is skipped (== overflow) */
+    int32_t  overflow;          /* 1 if the gradient holds an inf or NaN */
+    int32_t  skip;              /* 1 if this step is skipped (== overflow,
+                                   or while wide_pending) */
     float    gmul;              /* fp32(coef / S): unscale and clip factor */
     float    bc1, bc2;          /* fp32(1 - beta1^t), fp32(1 - beta2^t) */
     float    lr, beta1, beta2;  /* fp32 hyperparameters of this step */
     float    omb1, omb2;        /* fp32(1 - beta1), fp32(1 - beta2) */
     float    eps, wd;
     uint32_t done_blocks;       /* internal arrival counter; 0 between calls */
-    uint32_t reserved;
-    uint64_t sumsq_units[2];    /* the exact sum in units of 2^-48 (low, high) */
+    uint32_t wide_pending;      /* internal: 1 while an fp32 reduction waits
+                                   for its wide pass (see
+                                   zero_shard_norm_overflow_f32); 0 after it */
+    uint64_t sumsq_units[2];    /* the exact sum in units of 2^-48 (low,
+                                   high) when it is a whole number of them
+                                   below 2^128 (always, for binary16
+                                   gradients); otherwise both words are
+                                   all ones */
 } zero_step_state_t;
 
 /* ---- model-state arithmetic (host only, no device work) ------------- */
@@ -235,15 +241,30 @@ int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t nsegs, flo
 /* Bytes of device workspace zero_shard_decide needs to fold `count` partials. */
 size_t zero_decide_workspace_bytes(uint64_t count);
 
-/* Folds `count` partials written by zero_flatten_norm_bucket (or its fp32
- * form) into the exact sum and overflow flag, then takes exactly the
- * decision that zero_shard_norm_overflow (resp. its fp32 form) takes (same
- * fields of dev_state, bit for bit).
- * partials, workspace: device, 16-byte aligned; hp: host.
+/* Folds `count` partials written by zero_flatten_norm_bucket into the
+ * exact sum and overflow flag, then takes exactly the decision that
+ * zero_shard_norm_overflow takes (same fields of dev_state, bit for bit).
+ * Partials of zero_flatten_norm_bucket_f32 go to zero_shard_decide_f32:
+ * folded here, a partition off the fast path (see
+ * zero_shard_norm_overflow_f32) leaves the step pending and skipped with
+ * the loss scale and counters untouched.
+ * partials, workspace: device, 16-byte aligned; hp: host; workspace of at
+ * least zero_decide_workspace_bytes(count).
  * Errors: as zero_shard_norm_overflow (ZERO_ERANGE: count > 2^30 or
  *         workspace too small). */
 int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,
                       zero_step_state_t* dev_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The decision over the partials of zero_flatten_norm_bucket_f32 calls that
+ * together wrote the fp32 partition grad32[0..n): the fold of
+ * zero_shard_decide, then the wide pass over grad32 when the fold left the
+ * step pending.  The result is exactly zero_shard_norm_overflow_f32's on
+ * the same partition, bit for bit.  grad32: device, 4-byte aligned (NULL
+ * allowed when n = 0); the rest as zero_shard_decide.
+ * Errors: those of zero_shard_decide, and ZERO_ERANGE (n > 2^40). */
+int zero_shard_decide_f32(const void* partials, uint64_t count, const float* grad32, uint64_t n,
+                          const zero_hparams_t* hp, zero_step_state_t* dev_state, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace zero_shard_norm_overflow needs for n elements
  * (per-block partial sums; fixed for a given n). */
@@ -297,19 +318,21 @@ int zero_shard_norm_overflow_noalloc(const uint16_t* grad16, uint64_t n, const z
 
 /* Reduce and decide over an fp32 gradient partition (gradient
  * accumulation: a binary32 sum of micro-batch fp16 gradients).
- *   overflow = 1 if any element is inf or NaN or has |x| >= 2^24 (a sum of
- *              at most 256 binary16 values stays below 2^24; larger values
- *              count as an overflow of the scaled gradient);
- *   sumsq    = sum of x^2 with each square rounded to the nearest multiple
- *              of 2^-48, summed exactly and rounded once to binary64 (for
- *              sums of binary16 values every square is already on that
- *              grid, so this is the exact sum of squares);
- * then the same decision as zero_shard_norm_overflow.  An exact sum of
- * 2^80 or more (more than 2^128 units of 2^-48) also counts as overflow in
- * both forms; only a partition of billions of elements near 2^24 gets there.
- * grad32: device, 16-byte aligned; everything else as for
+ *   overflow = 1 if any element is inf or NaN;
+ *   sumsq    = the exact sum of the squares of all n values, rounded once
+ *              to binary64 (any finite binary32 values);
+ * then the same decision as zero_shard_norm_overflow.  Two kernels: the
+ * fast reduction sums exactly when every value is a multiple of 2^-24 below
+ * 2^24 in magnitude (true of any binary32 sum of at most 256 binary16
+ * values); when one is not, it leaves the decision pending
+ * (wide_pending = 1) and the wide pass that follows sums the squares of any
+ * binary32 values exactly (slower: LDS-atomic bound) and decides.  On the
+ * fast path the wide pass returns at once.  sumsq_units holds the exact sum
+ * in 2^-48 units when it is a whole number of them below 2^128, else all
+ * ones.  grad32: device, 16-byte aligned; everything else as for
  * zero_shard_norm_overflow, including the workspace size
- * (zero_norm_workspace_bytes(n)) and the errors. */
+ * (zero_norm_workspace_bytes(n), which covers both kernels) and the
+ * errors. */
 int zero_shard_norm_overflow_f32(const float* grad32, uint64_t n, const zero_hparams_t* hp,
                                  zero_step_state_t* dev_state, void* workspace,
                                  size_t workspace_bytes, void* stream);
@@ -354,12 +377,14 @@ int zero_shard_adam_step_f32(uint16_t* p16, float* p32, float* m32, float* v32,
  * holds the two scales and their exact sums. */
 typedef struct {
     float    scale_w, scale_s;  /* worker and server scales of the last step */
-    double   sumsq_w, sumsq_s;  /* the exact windowed sums, rounded to binary64 */
-    int32_t  qexp_w, qexp_s;    /* window exponents: sum = units * 2^qexp */
-    uint32_t done_blocks;       /* internal arrival counter; 0 between calls */
-    uint32_t reserved;
-    uint64_t units_w[2];        /* exact integer sums (low, high) */
-    uint64_t units_s[2];
+    double   sumsq_w, sumsq_s;  /* the exact sums of squares, rounded once to binary64 */
+    int32_t  qexp_w, qexp_s;    /* diagnostics of the fast windowed sums: the */
+    uint32_t done_blocks;       /*   window's unit 2^qexp; internal arrival
+                                     counter (0 between calls) */
+    uint32_t wide_pending;      /* internal: bit 0 / bit 1 while the worker /
+                                   server scale waits for its wide pass */
+    uint64_t units_w[2];        /* the windowed sums as integers of 2^qexp */
+    uint64_t units_s[2];        /* units (low, high), each square rounded */
 } zero_onebit_state_t;
 
 /* Enqueue the zeroing of a compression-stage state.
@@ -369,32 +394,41 @@ int zero_onebit_state_init(zero_onebit_state_t* dev_onebit, void* stream);
 /* Bytes of device workspace zero_onebit_step needs for n elements. */
 size_t zero_onebit_workspace_bytes(uint64_t n);
 
-/* One compression-stage step of 1-bit Adam (the DeepSpeed article: 1-bit
- * Adam cuts communication up to 5x with Adam-like convergence; the
- * algorithm is Tang et al. 2021, Algorithm 1), run after a warm-up of
- * ordinary steps (zero_shard_adam_step) with the variance v32 frozen.  With
- * the decision in dev_state (gmul, beta1, lr, eps, wd; nothing happens when
- * it says skip), on this rank, which is its own server:
- *   g = fp32(grad16)*gmul;  m = beta1*m + (1-beta1)*g
- *   x = m + err_w;  s_w = S(x);  bits_w = sgn(x);  err_w = x - s_w*sgn(x)
- *   u = s_w*sgn(x) + err_s;  s_s = S(u);  bits_s = sgn(u)
- *   m = s_s*sgn(u);  err_s = u - m
- *   p = p - lr*(m/(sqrt(v)+eps) + wd*p);  p16 = fp16(p)
+/* One step of 1-bit Adam (the DeepSpeed article: 1-bit Adam cuts
+ * communication up to 5x with Adam-like convergence; the algorithm is Tang
+ * et al. 2021, Algorithm 1), after zero_shard_decide (or
+ * zero_shard_norm_overflow) has decided it.  The device chooses the stage
+ * from the applied-step count in dev_state, so the host never reads it back
+ * and one captured graph can cross from one stage to the other:
+ *   warm-up (the applied steps before this one number fewer than `warmup`,
+ *   i.e. dev_state->step <= warmup after the decision): the ordinary update
+ *   of zero_shard_adam_step, which also builds the variance v32;
+ *   compression stage (otherwise): v32 frozen, and with the decision in
+ *   dev_state (gmul, beta1, lr, eps, wd), on this rank, its own server:
+ *     g = fp32(grad16)*gmul;  m = beta1*m + (1-beta1)*g
+ *     x = m + err_w;  s_w = S(x);  bits_w = sgn(x);  err_w = x - s_w*sgn(x)
+ *     u = s_w*sgn(x) + err_s;  s_s = S(u);  bits_s = sgn(u)
+ *     m = s_s*sgn(u);  err_s = u - m
+ *     p = p - lr*(m/(sqrt(v)+eps) + wd*p);  p16 = fp16(p)
+ * A skipped step (overflow) changes nothing, errors and bits included; the
+ * kernels of the stage not taken return at once, before any load.
  * sgn(x) = +1 for x >= 0 (zeros too), -1 otherwise; bit k of byte j of a
  * bits array is element 8j+k, 1 for +1.  S(x) = fp32(sqrt(sum/n)) with the
- * sum of squares EXACT in a window set by max|x|: with 2^E <= max|x| <
- * 2^(E+1), each square is rounded to the nearest multiple of 2^(2E-80),
- * the integers are summed exactly and the total is rounded once to
- * binary64.  Every elementwise operation is one binary32 operation in the
- * order above.  Results do not depend on the launch configuration.
+ * sum of squares exact and rounded once to binary64.  The fast sum works in
+ * a window set by max|x| (each square rounded to a multiple of 2^(2E-80),
+ * 2^E <= max|x| < 2^(E+1)); it keeps its result when the binary64 rounding
+ * is the same at both ends of the window's error interval, and otherwise
+ * hands the sum to a wide pass that is exact for any binary32 values.
+ * Every elementwise operation is one binary32 operation in the order
+ * above.  Results do not depend on the launch configuration.
  * p16, p32, m32, v32, err_w, err_s, grad16: device, n elements, 16-byte
  * aligned; bits_w, bits_s: device, (n+7)/8 bytes; workspace: device,
  * 256-byte aligned, >= zero_onebit_workspace_bytes(n).
- * Errors: ZERO_EINVAL (NULL), ZERO_EALIGN, ZERO_ERANGE (n > 2^40,
- *         workspace too small), ZERO_EHIP. */
-int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const float* v32, float* err_w, float* err_s,
+ * Errors: ZERO_EINVAL (NULL, warmup < 0), ZERO_EALIGN, ZERO_ERANGE
+ *         (n > 2^40, workspace too small), ZERO_EHIP. */
+int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v32, float* err_w, float* err_s,
                      const uint16_t* grad16, uint64_t n, uint8_t* bits_w, uint8_t* bits_s,
-                     const zero_step_state_t* dev_state, zero_onebit_state_t* dev_onebit,
+                     const zero_step_state_t* dev_state, zero_onebit_state_t* dev_onebit, int64_t warmup,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- host step (ZeRO-Offload form) ----------------------------------- */

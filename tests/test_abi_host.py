@@ -110,8 +110,8 @@ def test_bucket_segments_capacity_error(Z):
 def test_workspace_size_is_stable_and_bounded(Z):
     for n in (0, 1, 8, 8191, 1 << 20, 97_350_700, 976_562_500):
         b = Z.zero_norm_workspace_bytes(n)
-        assert b == Z.zero_norm_workspace_bytes(n) and 32 <= b <= 2048 * 32
-    assert Z.zero_norm_workspace_bytes(1 << 40) > 2048 * 32       # per-thread bound grows the grid
+        assert b == Z.zero_norm_workspace_bytes(n) and 160 <= b <= 512 * 160       # <= 512 wide partials
+    assert Z.zero_norm_workspace_bytes(1 << 40) > 512 * 160       # per-thread bound grows the fast grid
 
 
 # ---- argument validation: every case returns before any device work ---------
@@ -226,15 +226,29 @@ def test_decide_validation(Z):
     assert L.zero_shard_decide(FAKE, 10, C.byref(bad), FAKE, FAKE, ws, None) == E.ZERO_EINVAL
 
 
+def test_decide_f32_validation(Z):
+    L, E = Z.lib(), Z._lib
+    ws = Z.zero_decide_workspace_bytes(100)
+    hp = Z.hparams()
+    call = lambda p=FAKE, c=100, g=FAKE, n=1000, h=C.byref(hp), st=FAKE, w=FAKE, wb=ws: L.zero_shard_decide_f32(
+        p, c, g, n, h, st, w, wb, None)
+    assert call(g=0) == E.ZERO_EINVAL and call(h=None) == E.ZERO_EINVAL and call(st=0) == E.ZERO_EINVAL
+    assert call(g=FAKE + 2) == E.ZERO_EALIGN and call(p=FAKE + 8) == E.ZERO_EALIGN
+    assert call(wb=ws - 1) == E.ZERO_ERANGE
+    assert call(n=(1 << 40) + 1, wb=1 << 62) == E.ZERO_ERANGE
+    assert ws >= 512 * 160                                          # room for the wide pass at any n
+
+
 def test_onebit_validation(Z):
     L, E = Z.lib(), Z._lib
     n = 1000
     ws = Z.zero_onebit_workspace_bytes(n)
     assert ws > 0 and Z.zero_onebit_workspace_bytes(n) == ws
     ok = [FAKE] * 7
-    call = lambda ptrs=ok, nn=n, bw=FAKE, bs=FAKE, st=FAKE, ob=FAKE, w=FAKE, wb=ws: L.zero_onebit_step(
-        *ptrs, nn, bw, bs, st, ob, w, wb, None)
+    call = lambda ptrs=ok, nn=n, bw=FAKE, bs=FAKE, st=FAKE, ob=FAKE, wu=2, w=FAKE, wb=ws: L.zero_onebit_step(
+        *ptrs, nn, bw, bs, st, ob, wu, w, wb, None)
     assert call(st=0) == E.ZERO_EINVAL and call(ob=0) == E.ZERO_EINVAL and call(w=0) == E.ZERO_EINVAL
+    assert call(wu=-1) == E.ZERO_EINVAL
     assert call(bw=0) == E.ZERO_EINVAL
     assert call(ptrs=[FAKE] * 6 + [0]) == E.ZERO_EINVAL
     assert call(ptrs=[FAKE + 8] + [FAKE] * 6) == E.ZERO_EALIGN

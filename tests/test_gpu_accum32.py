@@ -89,18 +89,34 @@ def test_accum_fused_and_separate_identical():
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
 
 
-def _crafted_f32(n, seed, top=16777215.0, expo_hi=1):
-    """binary32 values off the 2^-24 grid at every magnitude the domain allows
-    (|x| < 2^(24 + expo_hi - 1)), plus `top` (by default the largest in-domain
-    value) every 97th element."""
+def _crafted_f32(n, seed, lo=-80, hi=1, top=16777215.0):
+    """binary32 values with random significands and exponents in [lo, hi)
+    (most off the 2^-24 grid), random signs, plus `top` every 97th element."""
     rng = np.random.default_rng(seed)
     mant = rng.integers(1 << 23, 1 << 24, n).astype(np.float64)
-    expo = rng.integers(-80, expo_hi, n).astype(np.float64)
-    x = (mant * np.exp2(expo)).astype(np.float32)
+    expo = rng.integers(lo, hi, n).astype(np.float64)
+    x = np.minimum(mant * np.exp2(expo), float(np.finfo(np.float32).max)).astype(np.float32)
     x *= np.where(rng.integers(0, 2, n) == 1, -1, 1).astype(np.float32)
     x[::97] = np.float32(top)
     x[1::101] = np.float32(3 * 2.0 ** -26)
     return x
+
+
+def _units48(g32):
+    """The exact sum of squares in 2^-48 units when it is a whole number of
+    them below 2^128, else the all-ones sentinel: Python integers, from the
+    IEEE binary32 fields (x = M * 2^e)."""
+    b = g32.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    field = (b >> np.uint32(23)).astype(np.int64)
+    mant = (b & np.uint32(0x7FFFFF)).astype(np.int64) | np.where(field > 0, 1 << 23, 0)
+    e = np.where(field > 0, field - 150, -149)
+    total = 0                                        # in units of 2^-298
+    for m, k in zip(mant.tolist(), (2 * e + 298).tolist()):
+        total += (m * m) << k
+    if total % (1 << 250):
+        return (1 << 128) - 1
+    u = total >> 250
+    return u if u < (1 << 128) else (1 << 128) - 1
 
 
 def _decide_standalone(g32):
@@ -112,16 +128,37 @@ def _decide_standalone(g32):
     return Z.read_state(st)
 
 
-@pytest.mark.parametrize("n,small", [(5, False), (4096 * 3 + 1, False), (1_000_003, False), (1_000_003, True)])
-def test_norm_f32_rounds_each_square_to_grid(n, small):
-    # small: |x| < 2^-9, so the total stays below 2^53 units, sumsq is the
-    # exact integer and every per-square rounding shows in it
-    g = _crafted_f32(n, seed=n, top=2.0 ** -10, expo_hi=-32) if small else _crafted_f32(n, seed=n)
-    H.log(f"norm f32 crafted n={n} small={small}")
-    s = _decide_standalone(g)
+def _check_sum(s, g, scale0=1024.0):
     sumsq, ovf = O.norm_overflow_f32(g)
-    assert s.overflow == ovf == 0
-    assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+    assert s.overflow == ovf and s.wide_pending == 0
+    assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes(), (s.sumsq, sumsq)
+    if not ovf:
+        ref = O.new_state(scale0)
+        O.decide(ref, O.hparams(), sumsq, ovf)
+        H.compare_state(s, ref, _units48(g) if g.size <= 300_000 else None)
+    return ovf
+
+
+@pytest.mark.parametrize("n,lo,hi", [(5, -149, 128), (4096 * 3 + 1, -149, 128), (4096 * 3 + 1, -149, -120),
+                                     (1_000_003, -80, 1), (1_000_003, -40, -32), (65_537, 100, 128)])
+def test_norm_f32_exact_over_the_whole_binary32_range(n, lo, hi):
+    """Values off the fast path (off the 2^-24 grid, subnormal, up to the
+    largest binary32) go through the wide pass: the decision and the exact
+    sum bit for bit against the oracle."""
+    g = _crafted_f32(n, seed=n + lo + 1000, lo=lo, hi=hi, top=2.0 ** (hi - 1) if hi < 24 else 16777215.0)
+    H.log(f"norm f32 crafted n={n} exponents [{lo}, {hi})")
+    _check_sum(_decide_standalone(g), g)
+
+
+def test_norm_f32_tie_needs_every_square():
+    # 1 + 2 * 2^-54 is halfway between two binary64 values; the square of
+    # 2^-60 (2^-120) breaks the tie upward -- only an exact sum sees it
+    for n in (4, 50_000, 1_000_000):
+        g = np.zeros(n, np.float32)
+        g[[0, n // 3, n // 2, n - 1]] = [1.0, 2.0 ** -27, -(2.0 ** -27), 2.0 ** -60]
+        s = _decide_standalone(g)
+        assert s.sumsq == 1.0 + 2.0 ** -52
+        _check_sum(s, g)
 
 
 def test_norm_f32_special_values_everywhere():
@@ -138,18 +175,17 @@ def test_norm_f32_special_values_everywhere():
         else:
             g[pos] = val
         H.log(f"norm f32 special pos={pos} val={val}")
-        s = _decide_standalone(g)
-        sumsq, ovf = O.norm_overflow_f32(g)
-        assert s.overflow == ovf == (1 if pos is not None else 0)
-        assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
-        if not ovf:
-            assert s.as_dict()["sumsq_units"] == H.exact_units32(g)
+        ovf = _check_sum(_decide_standalone(g), g)
+        assert ovf == (1 if not np.isfinite(val) else 0)
 
 
 def test_fused_f32_accumulate_into_crafted_partition():
-    """The fused fp32 flatten sums squares of the values it stores: a partition
-    holding off-grid values, values that the added micro-batch pushes to
-    2^24 (overflow) or keeps just below it."""
+    """The fused fp32 flatten sums squares of the values it stores, and
+    zero_shard_decide_f32 completes the sum with the wide pass when a value is
+    off the fast path: a partition holding off-grid values, and one where the
+    added micro-batch lands a value exactly on 2^24.  Folded by
+    zero_shard_decide alone, such partials leave the step pending: skipped,
+    loss scale and counters untouched."""
     rng = np.random.default_rng(44)
     n = 300_007
     numels, segs = shardgen.random_segments(rng, n, 40_000)
@@ -170,16 +206,22 @@ def test_fused_f32_accumulate_into_crafted_partition():
     for name, dst0 in cases:
         ref = dst0.copy()
         O.flatten(srcs, segs, ref, accumulate=True)
-        dst = torch.from_numpy(dst0.copy()).cuda()
-        H.log(f"fused f32 accumulate: {name}, partials={count}")
-        Z.zero_flatten_norm_bucket_f32(arr, k, dst, partials, n, True)
-        Z.zero_step_state_init(st, 1.0)
-        Z.zero_shard_decide(partials, count, Z.hparams(), st, ws)
-        s = Z.read_state(st)
-        assert np.array_equal(dst.cpu().numpy().view(np.uint32), ref.view(np.uint32))
-        sumsq, ovf = O.norm_overflow_f32(ref)
-        assert s.overflow == ovf == (name != "off-grid")
-        assert np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
+        for f32_decide in (True, False):
+            dst = torch.from_numpy(dst0.copy()).cuda()
+            H.log(f"fused f32 accumulate: {name}, partials={count}, decide_f32={f32_decide}")
+            Z.zero_flatten_norm_bucket_f32(arr, k, dst, partials, n, True)
+            Z.zero_step_state_init(st, 1.0)
+            if f32_decide:
+                Z.zero_shard_decide_f32(partials, count, dst, n, Z.hparams(), st, ws)
+            else:
+                Z.zero_shard_decide(partials, count, Z.hparams(), st, ws)
+            s = Z.read_state(st)
+            assert np.array_equal(dst.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+            if f32_decide:
+                assert _check_sum(s, ref, scale0=1.0) == 0
+            else:
+                assert (s.wide_pending, s.skip, s.overflow, s.step, s.loss_scale, s.skipped_total) == \
+                    (1, 1, 0, 0, 1.0, 0)
 
 
 def test_accum_skip_and_resume():

@@ -3,10 +3,10 @@ step, then the compression stage with frozen variance): the HIP path through
 the C ABI against the oracle on the same seeded inputs.
 
 Contract, every step: the step state bitwise; in the compression stage both
-scales, their exact integer sums and window exponents bitwise, both sign-bit
-payloads bitwise, the momentum, both error buffers, p32 and p16 bitwise over
-the whole shard (every operation is one binary32 operation in the same order
-on both sides, and the scales come from exact sums), and v32 unchanged."""
+scales and their exact sums of squares bitwise, both sign-bit payloads
+bitwise, the momentum, both error buffers, p32 and p16 bitwise over the
+whole shard (every operation is one binary32 operation in the same order on
+both sides, and the scales come from exact sums), and v32 unchanged."""
 import numpy as np
 import pytest
 import torch
@@ -146,13 +146,16 @@ def _crafted(n, seed, lo, hi):
     return x * np.where(rng.integers(0, 2, n) == 1, -1, 1).astype(np.float32)
 
 
-@pytest.mark.parametrize("case", ["wide", "subnormal", "zeros", "huge"])
+@pytest.mark.parametrize("case", ["wide", "subnormal", "zeros", "huge", "tie", "span"])
 def test_onebit_window_extremes(case):
     """One compression step from crafted momentum and error buffers: values
     spanning 40 binades, binary32 subnormals, all-zero vectors (scale 0, with
-    -0.0 entries) and magnitudes near 2^100."""
+    -0.0 entries), magnitudes near 2^100; a worker vector whose sum of
+    squares is a binary64 tie broken only by a square 2^-120 below the
+    largest (the window cannot round it, the wide pass must); and one whose
+    squares span from 2^-298 to 2^200."""
     n = 40_009
-    rng = np.random.default_rng({"wide": 11, "subnormal": 12, "zeros": 13, "huge": 14}[case])
+    rng = np.random.default_rng({"wide": 11, "subnormal": 12, "zeros": 13, "huge": 14, "tie": 15, "span": 16}[case])
     if case == "wide":
         m, ew, es = (_crafted(n, s, -60, -20) for s in (1, 2, 3))
     elif case == "subnormal":
@@ -161,6 +164,13 @@ def test_onebit_window_extremes(case):
         m = np.zeros(n, np.float32)
         m[::3] = -0.0
         ew, es = m.copy(), m.copy()
+    elif case == "tie":
+        m, es = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        ew = np.zeros(n, np.float32)                   # x = 0 * beta1 + ew = ew
+        ew[[0, 7, 1000, n - 1]] = [1.0, 2.0 ** -27, -(2.0 ** -27), 2.0 ** -60]
+    elif case == "span":
+        m, es = np.zeros(n, np.float32), _crafted(n, 17, -20, 0)
+        ew = _crafted(n, 18, -172, 101)
     else:
         m, ew, es = (_crafted(n, s, 80, 100) for s in (7, 8, 9))
     p32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
@@ -175,17 +185,19 @@ def test_onebit_window_extremes(case):
     hp = Z.hparams(max_grad_norm=0.0)
     Z.zero_shard_norm_overflow(dev.grad16, n, hp, dev.state, dev.workspace)
     H.log(f"onebit window case {case}")
-    dev.compress()
+    dev.update()
     st = O.new_state(1.0)
     O.decide(st, O.hparams(max_grad_norm=0.0), *O.norm_overflow(g16))
     refs = [shardgen.to_f16_bits(p32), p32.copy(), m.copy(), v32.copy(), ew.copy(), es.copy()]
-    x_w = (np.float32(st.beta1) * m + np.float32(st.omb1) * np.float32(0.0)) + ew   # the worker's input, for units
+    x_w = (np.float32(st.beta1) * m + np.float32(st.omb1) * np.float32(0.0)) + ew   # the worker's input
     bw, bs, (sw, ss) = O.onebit_step(st, *refs, g16)
     torch.cuda.synchronize()
     ob = dev.read_onebit()
-    _, S, units, qexp = O.onebit_scale_units(x_w)
+    _, S = O.onebit_scale(x_w)
+    if case == "tie":
+        assert S == 1.0 + 2.0 ** -52                    # the tie broken upward
     assert (ob.scale_w, ob.scale_s) == (np.float32(sw), np.float32(ss))
-    assert ob.units("w") == units and ob.qexp_w == qexp and ob.sumsq_w == S
+    assert ob.sumsq_w == S and ob.wide_pending == 0
     assert np.array_equal(dev.bits_w.cpu().numpy(), bw) and np.array_equal(dev.bits_s.cpu().numpy(), bs)
     for t, ref in ((dev.p32, refs[1]), (dev.m32, refs[2]), (dev.err_w, refs[4]), (dev.err_s, refs[5])):
         assert np.array_equal(_f32(t), ref.view(np.uint32))

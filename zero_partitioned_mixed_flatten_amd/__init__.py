@@ -12,7 +12,7 @@ from ._lib import (EXPORTS, NORM_PARTIAL_BYTES, ONEBIT_STATE_BYTES, STATE_BYTES,
                    ZeroError, lib, make_segments, read_state, zero_bucket_segments, zero_decide_workspace_bytes,
                    zero_flatten_bucket, zero_flatten_norm_bucket, zero_flatten_norm_bucket_f32,
                    zero_flatten_norm_partials, zero_norm_workspace_bytes, zero_shard_adam_step,
-                   zero_shard_adam_step_f32, zero_shard_decide, zero_shard_norm_overflow,
+                   zero_shard_adam_step_f32, zero_shard_decide, zero_shard_decide_f32, zero_shard_norm_overflow,
                    zero_shard_norm_overflow_f32, zero_shard_norm_overflow_noalloc, zero_state_bytes,
                    zero_status_string, zero_step_state_init,
                    zero_stream_copy, zero_host_create, zero_host_destroy, zero_host_threads, zero_host_state_init,
@@ -25,7 +25,7 @@ __all__ = ["EXPORTS", "NORM_PARTIAL_BYTES", "STATE_BYTES", "ZERO_F16", "ZERO_F32
            "Segment", "ShardStep", "StepState", "ZeroError", "hparams", "lib", "make_segments", "read_state",
            "zero_bucket_segments", "zero_decide_workspace_bytes", "zero_flatten_bucket",
            "zero_flatten_norm_bucket", "zero_flatten_norm_bucket_f32", "zero_flatten_norm_partials",
-           "zero_norm_workspace_bytes", "zero_shard_adam_step", "zero_shard_adam_step_f32", "zero_shard_decide",
+           "zero_norm_workspace_bytes", "zero_shard_adam_step", "zero_shard_adam_step_f32", "zero_shard_decide", "zero_shard_decide_f32",
            "zero_shard_norm_overflow", "zero_shard_norm_overflow_f32", "zero_shard_norm_overflow_noalloc",
            "zero_state_bytes", "zero_status_string",
            "zero_step_state_init", "zero_stream_copy", "HostContext", "OffloadStep", "zero_host_create",

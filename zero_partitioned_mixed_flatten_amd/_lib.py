@@ -23,7 +23,7 @@ EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "ze
            "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32", "zero_host_create", "zero_host_destroy",
            "zero_host_threads", "zero_host_state_init", "zero_host_norm_overflow", "zero_host_adam_step",
            "zero_offload_step", "zero_host_stream_copy", "zero_onebit_state_init", "zero_onebit_workspace_bytes",
-           "zero_onebit_step", "zero_shard_norm_overflow_noalloc")
+           "zero_onebit_step", "zero_shard_norm_overflow_noalloc", "zero_shard_decide_f32")
 NORM_PARTIAL_BYTES = 32
 
 
@@ -52,7 +52,7 @@ class StepState(C.Structure):
                 ("skip", C.c_int32), ("gmul", C.c_float), ("bc1", C.c_float), ("bc2", C.c_float),
                 ("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("omb1", C.c_float),
                 ("omb2", C.c_float), ("eps", C.c_float), ("wd", C.c_float), ("done_blocks", C.c_uint32),
-                ("reserved", C.c_uint32), ("sumsq_units", C.c_uint64 * 2)]
+                ("wide_pending", C.c_uint32), ("sumsq_units", C.c_uint64 * 2)]
 
     def as_dict(self):
         d = {name: getattr(self, name) for name, _ in self._fields_ if name != "sumsq_units"}
@@ -62,8 +62,8 @@ class StepState(C.Structure):
 
 class OneBitState(C.Structure):
     _fields_ = [("scale_w", C.c_float), ("scale_s", C.c_float), ("sumsq_w", C.c_double), ("sumsq_s", C.c_double),
-                ("qexp_w", C.c_int32), ("qexp_s", C.c_int32), ("done_blocks", C.c_uint32), ("reserved", C.c_uint32),
-                ("units_w", C.c_uint64 * 2), ("units_s", C.c_uint64 * 2)]
+                ("qexp_w", C.c_int32), ("qexp_s", C.c_int32), ("done_blocks", C.c_uint32),
+                ("wide_pending", C.c_uint32), ("units_w", C.c_uint64 * 2), ("units_s", C.c_uint64 * 2)]
 
     def units(self, which: str) -> int:
         u = getattr(self, f"units_{which}")
@@ -108,6 +108,7 @@ def lib():
         L.zero_decide_workspace_bytes.argtypes = [u64]
         L.zero_decide_workspace_bytes.restype = C.c_size_t
         L.zero_shard_decide.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
+        L.zero_shard_decide_f32.argtypes = [vp, u64, vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
         L.zero_host_create.argtypes = [i32, C.POINTER(vp)]
         L.zero_host_destroy.argtypes = [vp]
         L.zero_host_destroy.restype = None
@@ -120,7 +121,8 @@ def lib():
         L.zero_onebit_state_init.argtypes = [vp, vp]
         L.zero_onebit_workspace_bytes.argtypes = [u64]
         L.zero_onebit_workspace_bytes.restype = C.c_size_t
-        L.zero_onebit_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, u64, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.zero_onebit_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, u64, vp, vp, vp, vp, C.c_int64, vp, C.c_size_t,
+                                       vp]
         for name in EXPORTS:
             if name not in ("zero_status_string", "zero_norm_workspace_bytes", "zero_flatten_norm_partials",
                             "zero_decide_workspace_bytes", "zero_host_destroy", "zero_onebit_workspace_bytes"):
@@ -313,6 +315,17 @@ def zero_shard_decide(partials, count: int, hp: HParams, dev_state, workspace, s
                                    _stream(stream)))
 
 
+def zero_shard_decide_f32(partials, count: int, grad32, n: int, hp: HParams, dev_state, workspace,
+                          stream=None) -> None:
+    _need("zero_shard_decide_f32", partials, count * NORM_PARTIAL_BYTES)
+    _need("zero_shard_decide_f32", grad32, 4 * n)
+    _need("zero_shard_decide_f32", dev_state, STATE_BYTES)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_shard_decide_f32",
+           lib().zero_shard_decide_f32(_ptr(partials), count, _ptr(grad32), n, C.byref(hp), _ptr(dev_state),
+                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def read_state(dev_state) -> StepState:
     """Copy a device step state to the host (synchronises the current stream)."""
     raw = dev_state.detach().to("cpu").numpy().tobytes()
@@ -414,7 +427,7 @@ def zero_onebit_workspace_bytes(n: int) -> int:
 
 
 def zero_onebit_step(p16, p32, m32, v32, err_w, err_s, grad16, n: int, bits_w, bits_s, dev_state, dev_onebit,
-                     workspace, stream=None) -> None:
+                     warmup: int, workspace, stream=None) -> None:
     for t, b in ((p16, 2), (p32, 4), (m32, 4), (v32, 4), (err_w, 4), (err_s, 4), (grad16, 2)):
         _need("zero_onebit_step", t, b * n)
     for t in (bits_w, bits_s):
@@ -425,7 +438,7 @@ def zero_onebit_step(p16, p32, m32, v32, err_w, err_s, grad16, n: int, bits_w, b
     _check("zero_onebit_step",
            lib().zero_onebit_step(_ptr(p16), _ptr(p32), _ptr(m32), _ptr(v32), _ptr(err_w), _ptr(err_s),
                                   _ptr(grad16), n, _ptr(bits_w), _ptr(bits_s), _ptr(dev_state), _ptr(dev_onebit),
-                                  _ptr(workspace), ws_bytes, _stream(stream)))
+                                  int(warmup), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def read_onebit_state(dev_onebit) -> OneBitState:

@@ -122,12 +122,17 @@ __device__ __forceinline__ u32x2 to_f16x4(const float* p)
 __device__ __forceinline__ float grad_at(const uint16_t* g, uint64_t i) { return float(__builtin_bit_cast(_Float16, g[i])); }
 __device__ __forceinline__ float grad_at(const float* g, uint64_t i) { return g[i]; }
 
-template <typename G>
+// GATED (the warm-up steps of 1-bit Adam, zero_onebit_step): the update
+// runs only while st->step <= gate, tested before any load, so a step of the
+// compression stage pays no traffic here.
+template <typename G, bool GATED>
 __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict__ p16, float* __restrict__ p32,
                                                            float* __restrict__ m32, float* __restrict__ v32,
                                                            const G* __restrict__ grad, uint64_t n,
-                                                           const zero_step_state_t* __restrict__ st)
+                                                           const zero_step_state_t* __restrict__ st, int64_t gate)
 {
+    if (GATED && st->step > gate)
+        return;
     // The occupancy cap: the launch reserves dynamic LDS that no thread
     // touches (the store below is unreachable for any real n); referencing it
     // keeps the reservation part of the kernel's declared resources.
@@ -207,9 +212,11 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(uint16_t* __restrict_
     }
 }
 
-template <typename G>
+}  // namespace
+
+template <typename G, bool GATED>
 int adam_step(uint16_t* p16, float* p32, float* m32, float* v32, const G* grad, uint64_t n,
-              const zero_step_state_t* dev_state, void* stream)
+              const zero_step_state_t* dev_state, void* stream, int64_t gate)
 {
     if (!dev_state || (n && (!p16 || !p32 || !m32 || !v32 || !grad)))
         return ZERO_EINVAL;
@@ -225,12 +232,18 @@ int adam_step(uint16_t* p16, float* p32, float* m32, float* v32, const G* grad, 
     if (grid < 1) grid = 1;
     if (grid > 0x7fffffffull)
         return ZERO_ERANGE;
-    hipLaunchKernelGGL(adam_step_kernel<G>, dim3(uint32_t(grid)), dim3(kBlock), lds_reservation(kBlocksPerCU),
-                       (hipStream_t)stream, p16, p32, m32, v32, grad, n, dev_state);
+    hipLaunchKernelGGL((adam_step_kernel<G, GATED>), dim3(uint32_t(grid)), dim3(kBlock),
+                       lds_reservation(kBlocksPerCU), (hipStream_t)stream, p16, p32, m32, v32, grad, n, dev_state,
+                       gate);
     return launch_status();
 }
 
-}  // namespace
+int adam_step_gated(uint16_t* p16, float* p32, float* m32, float* v32, const uint16_t* grad16, uint64_t n,
+                    const zero_step_state_t* dev_state, void* stream, int64_t gate)
+{
+    return adam_step<uint16_t, true>(p16, p32, m32, v32, grad16, n, dev_state, stream, gate);
+}
+
 }  // namespace zero
 
 using namespace zero;
@@ -238,11 +251,11 @@ using namespace zero;
 extern "C" int zero_shard_adam_step(uint16_t* p16, float* p32, float* m32, float* v32, const uint16_t* grad16,
                                     uint64_t n, const zero_step_state_t* dev_state, void* stream)
 {
-    return adam_step(p16, p32, m32, v32, grad16, n, dev_state, stream);
+    return adam_step<uint16_t, false>(p16, p32, m32, v32, grad16, n, dev_state, stream, 0);
 }
 
 extern "C" int zero_shard_adam_step_f32(uint16_t* p16, float* p32, float* m32, float* v32, const float* grad32,
                                         uint64_t n, const zero_step_state_t* dev_state, void* stream)
 {
-    return adam_step(p16, p32, m32, v32, grad32, n, dev_state, stream);
+    return adam_step<float, false>(p16, p32, m32, v32, grad32, n, dev_state, stream, 0);
 }

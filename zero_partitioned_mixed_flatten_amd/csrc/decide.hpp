@@ -34,15 +34,13 @@ __host__ __device__ inline double u128_to_f64(uint64_t hi, uint64_t lo)
     return ldexp(double(top | (rest != 0 ? 1u : 0u)), 64 - lz);
 }
 
-// The decision from the exact sum (hi:lo, units of 2^-48) and the overflow
-// flag, written into the step state.
-__host__ __device__ inline void decide_state(zero_step_state_t* st, const DecideArgs& d, uint64_t hi, uint64_t lo,
-                                             bool ovf)
+// The decision from the exactly rounded sum of squares and the overflow flag,
+// written into the step state (sumsq_units is the caller's business).
+__host__ __device__ inline void decide_sum(zero_step_state_t* st, const DecideArgs& d, double sumsq, bool ovf)
 {
     const double S = st->loss_scale;
-    st->sumsq_units[0] = lo;
-    st->sumsq_units[1] = hi;
     st->overflow = ovf ? 1 : 0;
+    st->wide_pending = 0;
     if (ovf) {
         const double s2 = S * d.backoff;
         st->loss_scale = s2 < d.min_scale ? d.min_scale : s2;
@@ -54,7 +52,6 @@ __host__ __device__ inline void decide_state(zero_step_state_t* st, const Decide
         st->gmul = 0.0f;
         return;
     }
-    const double sumsq = ldexp(u128_to_f64(hi, lo), -48);
     const double norm = sqrt(sumsq) / S;
     st->skip = 0;
     st->sumsq = sumsq;
@@ -81,6 +78,26 @@ __host__ __device__ inline void decide_state(zero_step_state_t* st, const Decide
         good = 0;
     }
     st->good_steps = good;
+}
+
+// The decision from the exact sum as a count of 2^-48 units (hi:lo).
+__host__ __device__ inline void decide_state(zero_step_state_t* st, const DecideArgs& d, uint64_t hi, uint64_t lo,
+                                             bool ovf)
+{
+    st->sumsq_units[0] = lo;
+    st->sumsq_units[1] = hi;
+    decide_sum(st, d, ovf ? 0.0 : ldexp(u128_to_f64(hi, lo), -48), ovf);
+}
+
+// A fast fp32 reduction that cannot vouch for its sum leaves the step
+// undecided for the wide pass: skipped until then, loss scale and counters
+// untouched.
+__host__ __device__ inline void defer_to_wide(zero_step_state_t* st)
+{
+    st->wide_pending = 1;
+    st->overflow = 0;
+    st->skip = 1;
+    st->gmul = 0.0f;
 }
 
 inline bool hparams_ok(const zero_hparams_t* hp)

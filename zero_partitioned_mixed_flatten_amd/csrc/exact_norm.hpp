@@ -13,25 +13,28 @@
 //     sum(h) stays a multiple of 2^-8 below 2^44, sum(l) a multiple of 2^-48
 //     below 2^3.
 //
-//   binary32 gradients (the accumulation form): |x| < 2^24 on the domain, so
-//   x^2 is exact in binary64 and below 2^48; each square is rounded to the
-//   nearest multiple of 2^-48 (a no-op for sums of binary16 values, which are
-//   multiples of 2^-24).
+//   binary32 gradients (the accumulation form): on the fast path every value
+//   is a multiple of 2^-24 below 2^24 in magnitude (any binary32 sum of at
+//   most 256 binary16 values is), so x^2 is a multiple of 2^-48 below 2^48.
 //     a = x^2 rounded to a multiple of 2^16   (fma(x, x, C1) - C1, C1 = 1.5*2^68)
 //     r = x^2 - a, exactly, |r| <= 2^15       (fma(x, x, -a))
 //     b = r rounded to a multiple of 2^-16    ((r + C2) - C2, C2 = 1.5*2^36)
-//     c = r - b rounded to a multiple of 2^-48 ((. + C3) - C3, C3 = 24): the
-//         one rounding, to nearest (a square never lies halfway)
+//     c = r - b, a multiple of 2^-48 on the fast path: ((. + C3) - C3,
+//         C3 = 24) leaves it unchanged, and a value it changes marks a square
+//         off the 2^-48 grid
 //     sum(a) < 2^60 in steps of 2^16, sum(b) < 2^27 in steps of 2^-16,
 //     sum(c) < 2^-5 in steps of 2^-48: 44 significant bits at most.
-//
+//   A value off the fast path (|x| >= 2^24, or a square off the grid) makes
+//   the partial ask for the wide pass (wide_sum.hpp), which sums the squares
+//   of any binary32 values exactly; an inf or NaN is an overflow.
+
 // The sums become signed base-2^32 limbs that threads, workgroups and the
 // grid add without carries.  A workgroup's partial is stored carried (each
 // limb below 2^32), so any number of partials up to 2^30 adds inside int64.
 // At the end one thread carries the total into 128 bits and converts it to
 // binary64 with a single round-to-nearest-even: the exactly rounded sum,
 // independent of grid shape and schedule.  A total of 2^128 units or more
-// (2^80) is reported as an overflow, like an inf/NaN gradient.
+// (2^80; only binary32 values can get there) also asks for the wide pass.
 #pragma once
 
 #include <math.h>
@@ -41,11 +44,9 @@
 namespace zero {
 namespace exact {
 
-// Flag bits: any of them set means overflow.  Bits 15 and 31 come from the
-// binary16 exponent test; bit 31 from the binary32 domain test; bit 15 also
-// marks a partial whose sum does not fit 128 bits.
-constexpr uint32_t kOverflowBits = 0x80008000u;
-constexpr uint32_t kSumTooLarge = 0x00008000u;
+// Status bits of a thread, a workgroup partial and a whole reduction.
+constexpr uint32_t kOvf = 1u;       // an inf or NaN: the step is skipped
+constexpr uint32_t kWide = 2u;      // the fast sum does not hold: the wide pass sums exactly
 
 // ---- binary16 gradients ------------------------------------------------------------
 
@@ -69,7 +70,7 @@ struct Limbs {
 
 struct Acc16 {
     double h = 0.0, l = 0.0;
-    uint32_t flag = 0;
+    uint32_t flag = 0;           // bit 15 or 31 set: an all-ones exponent was seen
 
     __device__ __forceinline__ void square(_Float16 v)
     {
@@ -93,11 +94,12 @@ struct Acc16 {
         flag |= (uint32_t(b) & 0x7C00u) + 0x0400u;
         square(__builtin_bit_cast(_Float16, b));
     }
+    __device__ __forceinline__ uint32_t status() const { return (flag & 0x80008000u) ? kOvf : 0u; }
     // The thread's sum as limbs; an inf/NaN seen by the thread voids it
     // (the overflow flag makes the sum irrelevant anyway).
     __device__ __forceinline__ Limbs limbs() const
     {
-        const bool bad = (flag & kOverflowBits) != 0;
+        const bool bad = status() != 0;
         const int64_t hu = bad ? 0 : int64_t(h * 256.0);    // sum(h) / 2^-8, < 2^52
         const int64_t lu = bad ? 0 : int64_t(l * 0x1p48);   // sum(l) / 2^-48, |.| < 2^51
         const int64_t hs = hu << 8;                         // hu * 2^40 = hs * 2^32
@@ -111,21 +113,24 @@ constexpr double kSplit32Hi = 0x1.8p68;        // ulp 2^16
 constexpr double kSplit32Mid = 0x1.8p36;       // ulp 2^-16
 constexpr double kSplit32Lo = 0x1.8p4;         // ulp 2^-48
 
-// Bit 31 set iff |x| >= 2^24 or x is inf/NaN (0x4B800000 is 2^24).
-__device__ __forceinline__ uint32_t dom_test(uint32_t b) { return ((b & 0x7FFFFFFFu) + 0x34800000u) & 0x80000000u; }
-
 struct Acc32 {
     double a = 0.0, b = 0.0, c = 0.0;
-    uint32_t flag = 0;
+    uint32_t big = 0;            // bit 31: some |x| >= 2^24 (0x4B800000), inf and NaN included
+    uint32_t infnan = 0;         // bit 31: some inf or NaN (0x7F800000)
+    bool off = false;            // some square off the 2^-48 grid
 
     __device__ __forceinline__ void add(float v)
     {
-        flag |= dom_test(__builtin_bit_cast(uint32_t, v));
+        const uint32_t u = __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu;
+        big |= u + 0x34800000u;
+        infnan |= u + 0x00800000u;
         const double x = double(v);
         const double ha = __builtin_fma(x, x, kSplit32Hi) - kSplit32Hi;  // to a multiple of 2^16
         const double r = __builtin_fma(x, x, -ha);                        // exact, |r| <= 2^15
         const double hb = (r + kSplit32Mid) - kSplit32Mid;                // to a multiple of 2^-16
-        const double hc = ((r - hb) + kSplit32Lo) - kSplit32Lo;           // nearest multiple of 2^-48
+        const double d = r - hb;                                          // exact
+        const double hc = (d + kSplit32Lo) - kSplit32Lo;                  // d itself on the fast path
+        off |= hc != d;
         a += ha;
         b += hb;
         c += hc;
@@ -137,9 +142,15 @@ struct Acc32 {
         add(v.z);
         add(v.w);
     }
+    __device__ __forceinline__ uint32_t status() const
+    {
+        if (infnan & 0x80000000u)
+            return kOvf;
+        return ((big & 0x80000000u) || off) ? kWide : 0u;
+    }
     __device__ __forceinline__ Limbs limbs() const
     {
-        const bool bad = (flag & kOverflowBits) != 0;
+        const bool bad = status() != 0;
         const int64_t la = bad ? 0 : int64_t(a * 0x1p-16);   // units of 2^16 = 2^64 * 2^-48, < 2^44
         const int64_t lb = bad ? 0 : int64_t(b * 0x1p16);    // units of 2^-16 = 2^32 * 2^-48, |.| < 2^43
         const int64_t lc = bad ? 0 : int64_t(c * 0x1p48);    // units of 2^-48, |.| < 2^43
@@ -220,15 +231,15 @@ __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
     }
 }
 
-// A workgroup's partial: the carried sum in two words; a sum of 2^128 units
-// or more is marked as an overflow.
-__device__ __forceinline__ NormPartial make_partial(Limbs s, uint32_t flag)
+// A workgroup's partial: the carried sum in two words and the status bits; a
+// sum of 2^128 units or more asks for the wide pass.
+__device__ __forceinline__ NormPartial make_partial(Limbs s, uint32_t status)
 {
     s = carry(s);
     NormPartial p;
     p.w0 = uint64_t(s.l0) | (uint64_t(s.l1) << 32);
     p.w1 = uint64_t(s.l2) | (uint64_t(s.l3) << 32);
-    p.flag = flag | ((s.l3 >> 32) != 0 ? kSumTooLarge : 0u);
+    p.flag = status | ((s.l3 >> 32) != 0 ? kWide : 0u);
     p.pad[0] = p.pad[1] = p.pad[2] = 0;
     return p;
 }

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     }
 
     if (NORM) {                                 // every thread reaches this point
-        uint32_t flag = acc.flag;
+        uint32_t flag = acc.status();
         exact::Limbs s = acc.limbs();
         exact::block_fold<kBlock>(s, flag);
         if (threadIdx.x == 0)

@@ -6,6 +6,7 @@
 
 #include <atomic>
 
+#include "wide_sum.hpp"
 #include "zero_internal.hpp"
 
 namespace zero {
@@ -159,14 +160,20 @@ extern "C" int zero_bucket_segments(const zero_segment_t* segs, uint32_t nsegs, 
     return k > cap ? ZERO_ERANGE : ZERO_OK;
 }
 
+// The fast reductions' partials and, for the fp32 forms, the wide pass's
+// partials (the two passes run one after the other and share the space).
 extern "C" size_t zero_norm_workspace_bytes(uint64_t n)
 {
-    return size_t(norm_grid(n)) * sizeof(NormPartial);
+    const uint64_t fast = norm_grid(n) * sizeof(NormPartial);
+    const uint64_t wide = wide::grid(n) * sizeof(wide::WidePartial);
+    return size_t(fast > wide ? fast : wide);
 }
 
 extern "C" size_t zero_decide_workspace_bytes(uint64_t count)
 {
-    return size_t(decide_grid(count)) * sizeof(NormPartial);
+    const uint64_t fast = decide_grid(count) * sizeof(NormPartial);
+    const uint64_t wide = wide::kMaxBlocks * sizeof(wide::WidePartial);
+    return size_t(fast > wide ? fast : wide);
 }
 
 extern "C" int zero_step_state_init(zero_step_state_t* dev_state, double initial_scale, void* stream)

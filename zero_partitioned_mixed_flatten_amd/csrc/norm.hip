@@ -33,23 +33,35 @@
 
 #include "decide.hpp"
 #include "exact_norm.hpp"
+#include "wide_sum.hpp"
 
 namespace zero {
 namespace {
 
 using exact::Limbs;
 
+// The reduction's end, on one thread: overflow -> the skip decision; a sum
+// the fast form cannot vouch for -> left to the wide pass; else the decision.
+__device__ __forceinline__ void conclude(zero_step_state_t* st, const DecideArgs& d, Limbs t, uint32_t status)
+{
+    uint64_t hi, lo;
+    const bool fits = exact::limbs_to_u128(t, hi, lo);
+    if (status & exact::kOvf)
+        decide_state(st, d, hi, lo, true);
+    else if (!fits || (status & exact::kWide))
+        defer_to_wide(st);
+    else
+        decide_state(st, d, hi, lo, false);
+}
+
 // Called by every thread of every workgroup with that workgroup's limbs and
-// flag (valid in thread 0): publish, and let the last workgroup decide.
+// status (valid in thread 0): publish, and let the last workgroup decide.
 __device__ __forceinline__ void publish_and_decide(Limbs s, uint32_t flag, zero_step_state_t* st,
                                                    NormPartial* ws, const DecideArgs& d)
 {
     if (gridDim.x == 1) {          // one workgroup holds the whole sum: no arrival counter, no fence
-        if (threadIdx.x == 0) {
-            uint64_t hi, lo;
-            const bool fits = exact::limbs_to_u128(s, hi, lo);
-            decide_state(st, d, hi, lo, !fits || (flag & exact::kOverflowBits) != 0);
-        }
+        if (threadIdx.x == 0)
+            conclude(st, d, s, flag);
         return;
     }
     __shared__ uint32_t s_last;
@@ -72,11 +84,41 @@ __device__ __forceinline__ void publish_and_decide(Limbs s, uint32_t flag, zero_
         exact::fold_partial(t, tflag, ws[b]);
     exact::block_fold<kNormBlock>(t, tflag);
     if (threadIdx.x == 0) {
-        uint64_t hi, lo;
-        const bool fits = exact::limbs_to_u128(t, hi, lo);
-        decide_state(st, d, hi, lo, !fits || (tflag & exact::kOverflowBits) != 0);
+        conclude(st, d, t, tflag);
         st->done_blocks = 0;                                 // re-arm for the next call
     }
+}
+
+// The wide pass over an fp32 partition (wide_sum.hpp), and how it ends: the
+// exact sum of squares rounded once, then the decision.
+struct F32Values {
+    const float* g;
+    __device__ float at(uint64_t i) const { return g[i]; }
+};
+
+struct NormFinish {
+    zero_step_state_t* st;
+    DecideArgs d;
+    __device__ bool pending() const { return st->wide_pending != 0; }
+    __device__ uint32_t* counter() const { return &st->done_blocks; }
+    __device__ void finish(const uint64_t* digits) const
+    {
+        uint64_t hi, lo;
+        if (!wide::to_units48(digits, hi, lo))
+            hi = lo = ~uint64_t(0);
+        st->sumsq_units[0] = lo;
+        st->sumsq_units[1] = hi;
+        decide_sum(st, d, wide::to_f64(digits), false);
+    }
+};
+
+int launch_wide(const float* grad, uint64_t n, zero_step_state_t* st, const DecideArgs& d, void* workspace,
+                hipStream_t s)
+{
+    hipLaunchKernelGGL((wide::wide_sum_kernel<F32Values, NormFinish>), dim3(uint32_t(wide::grid(n))),
+                       dim3(wide::kBlock), 0, s, F32Values{grad}, n, NormFinish{st, d},
+                       static_cast<wide::WidePartial*>(workspace));
+    return launch_status();
 }
 
 // Element type of the partition: 16-byte vectors, the exact accumulator, and
@@ -125,7 +167,7 @@ __global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const T* __re
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * E::kPerVec)   // the last n % kPerVec elements
         E::one(acc, g, nvec * E::kPerVec + threadIdx.x);
 
-    uint32_t flag = acc.flag;
+    uint32_t flag = acc.status();
     Limbs s = acc.limbs();
     exact::block_fold<kNormBlock>(s, flag);
     publish_and_decide(s, flag, st, ws, d);
@@ -153,6 +195,9 @@ __global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* _
     publish_and_decide(s, flag, st, ws, d);
 }
 
+// `workspace_bytes` must cover what this call uses: the fast reduction's
+// partials and, for fp32, the wide pass's (the public entry points ask for
+// zero_norm_workspace_bytes(n), which covers both forms).
 template <typename T>
 int norm_overflow(const T* grad, uint64_t n, const zero_hparams_t* hp, zero_step_state_t* dev_state,
                   void* workspace, size_t workspace_bytes, void* stream)
@@ -166,11 +211,18 @@ int norm_overflow(const T* grad, uint64_t n, const zero_hparams_t* hp, zero_step
     if (n > kNormMaxElems)
         return ZERO_ERANGE;
     const uint64_t grid = norm_grid(n);
-    if (workspace_bytes < grid * sizeof(NormPartial))
+    uint64_t need = grid * sizeof(NormPartial);
+    if (sizeof(T) == 4 && need < wide::grid(n) * sizeof(wide::WidePartial))
+        need = wide::grid(n) * sizeof(wide::WidePartial);
+    if (workspace_bytes < need)
         return ZERO_ERANGE;
+    const DecideArgs d = decide_args(hp);
     hipLaunchKernelGGL(norm_overflow_kernel<T>, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
-                       grad, n, dev_state, static_cast<NormPartial*>(workspace), decide_args(hp));
-    return launch_status();
+                       grad, n, dev_state, static_cast<NormPartial*>(workspace), d);
+    int rc = launch_status();
+    if (rc == ZERO_OK && sizeof(T) == 4)       // fp32: the wide pass, a no-op unless the fast sum asked for it
+        rc = launch_wide(reinterpret_cast<const float*>(grad), n, dev_state, d, workspace, (hipStream_t)stream);
+    return rc;
 }
 
 }  // namespace
@@ -182,6 +234,8 @@ extern "C" int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, cons
                                         zero_step_state_t* dev_state, void* workspace,
                                         size_t workspace_bytes, void* stream)
 {
+    if (n <= kNormMaxElems && workspace_bytes < zero_norm_workspace_bytes(n))
+        return (!hp || !dev_state || !workspace || (n && !grad16)) ? ZERO_EINVAL : ZERO_ERANGE;
     return norm_overflow(grad16, n, hp, dev_state, workspace, workspace_bytes, stream);
 }
 
@@ -257,9 +311,11 @@ extern "C" int zero_shard_norm_overflow_noalloc(const uint16_t* grad16, uint64_t
     return norm_overflow(grad16, n, hp, dev_state, ws, kScratchPartials * sizeof(NormPartial), stream);
 }
 
-extern "C" int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,
-                                 zero_step_state_t* dev_state, void* workspace, size_t workspace_bytes,
-                                 void* stream)
+namespace zero {
+namespace {
+
+int decide(const void* partials, uint64_t count, const float* grad32, uint64_t n, const zero_hparams_t* hp,
+           zero_step_state_t* dev_state, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!hp || !dev_state || !workspace || (count && !partials))
         return ZERO_EINVAL;
@@ -267,13 +323,39 @@ extern "C" int zero_shard_decide(const void* partials, uint64_t count, const zer
         return ZERO_EINVAL;
     if ((count && !is_aligned(partials, 16)) || !is_aligned(dev_state, 8) || !is_aligned(workspace, 16))
         return ZERO_EALIGN;
-    if (count > kMaxPartials)
+    if (count > kMaxPartials || (grad32 && n > kNormMaxElems))
+        return ZERO_ERANGE;
+    if (workspace_bytes < zero_decide_workspace_bytes(count))     // covers both passes
         return ZERO_ERANGE;
     const uint64_t grid = decide_grid(count);
-    if (workspace_bytes < grid * sizeof(NormPartial))
-        return ZERO_ERANGE;
+    const DecideArgs d = decide_args(hp);
     hipLaunchKernelGGL(decide_kernel, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
                        static_cast<const NormPartial*>(partials), count, dev_state,
-                       static_cast<NormPartial*>(workspace), decide_args(hp));
-    return launch_status();
+                       static_cast<NormPartial*>(workspace), d);
+    int rc = launch_status();
+    if (rc == ZERO_OK && grad32)
+        rc = launch_wide(grad32, n, dev_state, d, workspace, (hipStream_t)stream);
+    return rc;
+}
+
+}  // namespace
+}  // namespace zero
+
+extern "C" int zero_shard_decide(const void* partials, uint64_t count, const zero_hparams_t* hp,
+                                 zero_step_state_t* dev_state, void* workspace, size_t workspace_bytes,
+                                 void* stream)
+{
+    return decide(partials, count, nullptr, 0, hp, dev_state, workspace, workspace_bytes, stream);
+}
+
+extern "C" int zero_shard_decide_f32(const void* partials, uint64_t count, const float* grad32, uint64_t n,
+                                     const zero_hparams_t* hp, zero_step_state_t* dev_state, void* workspace,
+                                     size_t workspace_bytes, void* stream)
+{
+    if (n && !grad32)
+        return ZERO_EINVAL;
+    if (n && !is_aligned(grad32, 4))
+        return ZERO_EALIGN;
+    // n == 0: an empty partition needs no wide pass (its fast sum is exact)
+    return decide(partials, count, n ? grad32 : nullptr, n, hp, dev_state, workspace, workspace_bytes, stream);
 }

@@ -38,6 +38,7 @@
 
 #include "decide.hpp"
 #include "exact_norm.hpp"
+#include "wide_sum.hpp"
 
 namespace zero {
 namespace {
@@ -159,8 +160,10 @@ __device__ __forceinline__ void momentum4(f16x4 g, f32x4& m, f32x4 e, const Coef
 __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restrict__ m32, const float* __restrict__ ew,
                                                                  const uint16_t* __restrict__ g16, uint64_t n,
                                                                  const zero_step_state_t* __restrict__ st,
-                                                                 uint32_t* __restrict__ blockmax)
+                                                                 int64_t warmup, uint32_t* __restrict__ blockmax)
 {
+    if (st->step <= warmup)                      // a warm-up step: the Adam update runs instead
+        return;
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
     if (n == UINT64_MAX)
         occupancy_reserve[threadIdx.x] = 0;
@@ -252,6 +255,33 @@ struct ServerU {
 // Which scale a sum kernel writes.
 enum Which { kWorker = 0, kServer = 1 };
 
+// The scale from the exactly rounded sum of squares S of n values.
+template <int WHICH>
+__device__ __forceinline__ void set_scale(zero_onebit_state_t* ob, double S, uint64_t n)
+{
+    const float scale = n ? float(sqrt(S / double(n))) : 0.0f;
+    if (WHICH == kWorker) {
+        ob->scale_w = scale;
+        ob->sumsq_w = S;
+    } else {
+        ob->scale_s = scale;
+        ob->sumsq_s = S;
+    }
+}
+
+// The window rounds each of the n squares to a whole number of units (off by
+// at most half a unit each), so the exact sum lies within n/2 units of the
+// window's integer W.  Rounding to binary64 is monotonic: when W - n/2 and
+// W + n/2 round to the same value, every sum between them does, and RNE(W)
+// is the exactly rounded sum.  (W >= 2^80 whenever a value is nonzero, so
+// 2W - n > 0.)  Otherwise the wide pass decides.
+__device__ __forceinline__ bool window_decides(uint64_t hi, uint64_t lo, uint64_t n)
+{
+    const unsigned __int128 w2 = ((unsigned __int128)hi << 65) | ((unsigned __int128)lo << 1);   // 2W < 2^124
+    const unsigned __int128 a = w2 - n, b = w2 + n;
+    return u128_to_f64(uint64_t(a >> 64), uint64_t(a)) == u128_to_f64(uint64_t(b >> 64), uint64_t(b));
+}
+
 template <int WHICH, typename V>
 __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restrict__ blockmax, uint64_t nmax,
                               const zero_step_state_t* __restrict__ st, zero_onebit_state_t* __restrict__ ob,
@@ -331,20 +361,20 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
         uint64_t hi = 0, lo = 0;
         exact::limbs_to_u128(t, hi, lo);                        // < n * 2^82: always fits
         const int qexp = 2 * E - 80;
-        const double S = mx ? ldexp(u128_to_f64(hi, lo), qexp) : 0.0;
-        const float scale = n ? float(sqrt(S / double(n))) : 0.0f;
         if (WHICH == kWorker) {
-            ob->scale_w = scale;
-            ob->sumsq_w = S;
             ob->qexp_w = mx ? qexp : 0;
             ob->units_w[0] = lo;
             ob->units_w[1] = hi;
         } else {
-            ob->scale_s = scale;
-            ob->sumsq_s = S;
             ob->qexp_s = mx ? qexp : 0;
             ob->units_s[0] = lo;
             ob->units_s[1] = hi;
+        }
+        if (!mx || window_decides(hi, lo, n)) {
+            const double S = mx ? ldexp(u128_to_f64(hi, lo), qexp) : 0.0;
+            set_scale<WHICH>(ob, S, n);
+        } else {
+            ob->wide_pending |= 1u << WHICH;                    // the wide pass sets the scale
         }
         ob->done_blocks = 0;                                    // re-arm for the next sum
     }
@@ -355,10 +385,11 @@ __global__ __launch_bounds__(kNormBlock) void onebit_sum_worker_kernel(const flo
                                                                        const uint32_t* __restrict__ blockmax,
                                                                        uint64_t nmax,
                                                                        const zero_step_state_t* __restrict__ st,
+                                                                       int64_t warmup,
                                                                        zero_onebit_state_t* __restrict__ ob,
                                                                        NormPartial* __restrict__ ws)
 {
-    if (st->skip)
+    if (st->skip || st->step <= warmup)
         return;
     sum_and_scale<kWorker>(WorkerX{m32, ew}, n, blockmax, nmax, st, ob, ws);
 }
@@ -368,10 +399,11 @@ __global__ __launch_bounds__(kNormBlock) void onebit_sum_server_kernel(const uin
                                                                        const uint32_t* __restrict__ blockmax,
                                                                        uint64_t nmax,
                                                                        const zero_step_state_t* __restrict__ st,
+                                                                       int64_t warmup,
                                                                        zero_onebit_state_t* __restrict__ ob,
                                                                        NormPartial* __restrict__ ws)
 {
-    if (st->skip)
+    if (st->skip || st->step <= warmup)
         return;
     sum_and_scale<kServer>(ServerU{bits_w, es, ob->scale_w}, n, blockmax, nmax, st, ob, ws);
 }
@@ -399,9 +431,12 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
                                                                         const float* __restrict__ es,
                                                                         uint8_t* __restrict__ bits_w, uint64_t n,
                                                                         const zero_step_state_t* __restrict__ st,
+                                                                        int64_t warmup,
                                                                         const zero_onebit_state_t* __restrict__ ob,
                                                                         uint32_t* __restrict__ blockmax)
 {
+    if (st->step <= warmup)
+        return;
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
     if (n == UINT64_MAX)
         occupancy_reserve[threadIdx.x] = 0;
@@ -495,8 +530,11 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
                                                                const uint8_t* __restrict__ bits_w,
                                                                uint8_t* __restrict__ bits_s, uint64_t n,
                                                                const zero_step_state_t* __restrict__ st,
+                                                               int64_t warmup,
                                                                const zero_onebit_state_t* __restrict__ ob)
 {
+    if (st->step <= warmup)
+        return;
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
     if (n == UINT64_MAX)
         occupancy_reserve[threadIdx.x] = 0;
@@ -575,6 +613,39 @@ __global__ __launch_bounds__(kBlock) void onebit_update_kernel(uint16_t* __restr
     }
 }
 
+// ---- the wide pass for a scale the window could not round (wide_sum.hpp) --------------
+
+struct WorkerValues {
+    const float* m;
+    const float* ew;
+    __device__ float at(uint64_t i) const { return m[i] + ew[i]; }
+};
+
+// u = s_w*sgn(x) + es, rebuilt from the worker's sign bits as the D kernel does
+struct ServerValues {
+    const uint8_t* bits;
+    const float* es;
+    const zero_onebit_state_t* ob;
+    __device__ float at(uint64_t i) const
+    {
+        const float sw = ob->scale_w;
+        return (((bits[i >> 3] >> (i & 7)) & 1) ? sw : -sw) + es[i];
+    }
+};
+
+template <int WHICH>
+struct ScaleFinish {
+    zero_onebit_state_t* ob;
+    uint64_t n;
+    __device__ bool pending() const { return ((ob->wide_pending >> WHICH) & 1u) != 0; }
+    __device__ uint32_t* counter() const { return &ob->done_blocks; }
+    __device__ void finish(const uint64_t* digits) const
+    {
+        set_scale<WHICH>(ob, wide::to_f64(digits), n);
+        ob->wide_pending &= ~(1u << WHICH);
+    }
+};
+
 __global__ void onebit_state_init_kernel(zero_onebit_state_t* ob)
 {
     zero_onebit_state_t s;
@@ -586,7 +657,7 @@ __global__ void onebit_state_init_kernel(zero_onebit_state_t* ob)
 struct Plan {
     uint64_t grid1;                 // one-shot kernels (A, C, E)
     uint64_t grid2;                 // sums (B, D)
-    uint64_t off_max_a, off_max_c, off_part_b, off_part_d, bytes;
+    uint64_t off_max_a, off_max_c, off_part_b, off_part_d, off_wide, bytes;
 };
 
 Plan plan(uint64_t n)
@@ -605,7 +676,8 @@ Plan plan(uint64_t n)
     p.off_max_c = up(p.grid1 * 4);
     p.off_part_b = p.off_max_c + up(p.grid1 * 4);
     p.off_part_d = p.off_part_b + up(p.grid2 * sizeof(NormPartial));
-    p.bytes = p.off_part_d + up(p.grid2 * sizeof(NormPartial));
+    p.off_wide = p.off_part_d + up(p.grid2 * sizeof(NormPartial));
+    p.bytes = p.off_wide + up(wide::grid(n) * sizeof(wide::WidePartial));
     return p;
 }
 
@@ -626,11 +698,13 @@ extern "C" int zero_onebit_state_init(zero_onebit_state_t* dev_onebit, void* str
     return launch_status();
 }
 
-extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const float* v32, float* err_w,
+extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v32, float* err_w,
                                 float* err_s, const uint16_t* grad16, uint64_t n, uint8_t* bits_w, uint8_t* bits_s,
                                 const zero_step_state_t* dev_state, zero_onebit_state_t* dev_onebit,
-                                void* workspace, size_t workspace_bytes, void* stream)
+                                int64_t warmup, void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (warmup < 0)
+        return ZERO_EINVAL;
     if (!dev_state || !dev_onebit || !workspace ||
         (n && (!p16 || !p32 || !m32 || !v32 || !err_w || !err_s || !grad16 || !bits_w || !bits_s)))
         return ZERO_EINVAL;
@@ -649,28 +723,41 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, const flo
     uint32_t* max_c = reinterpret_cast<uint32_t*>(ws + pl.off_max_c);
     NormPartial* part_b = reinterpret_cast<NormPartial*>(ws + pl.off_part_b);
     NormPartial* part_d = reinterpret_cast<NormPartial*>(ws + pl.off_part_d);
+    wide::WidePartial* part_w = reinterpret_cast<wide::WidePartial*>(ws + pl.off_wide);
+    const dim3 gw(uint32_t(wide::grid(n)));
     hipStream_t s = (hipStream_t)stream;
     const dim3 g1(uint32_t(pl.grid1)), g2(uint32_t(pl.grid2));
     const uint32_t cap = lds_reservation(kOneShotCap);
     const uint32_t cap_ac = cap > 256 ? cap - 256 : 0;     // room for block_max's static LDS
-    hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, grad16, n, dev_state,
-                       max_a);
-    int rc = launch_status();
+    // a warm-up step: the ordinary update (it returns at once in the compression stage)
+    int rc = adam_step_gated(p16, p32, m32, v32, grad16, n, dev_state, stream, warmup);
     if (rc != ZERO_OK)
         return rc;
+    hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, grad16, n, dev_state,
+                       warmup, max_a);
+    if ((rc = launch_status()) != ZERO_OK)
+        return rc;
     hipLaunchKernelGGL(onebit_sum_worker_kernel, g2, dim3(kNormBlock), 0, s, m32, err_w, n, max_a, pl.grid1,
-                       dev_state, dev_onebit, part_b);
+                       dev_state, warmup, dev_onebit, part_b);
+    if ((rc = launch_status()) != ZERO_OK)
+        return rc;
+    hipLaunchKernelGGL((wide::wide_sum_kernel<WorkerValues, ScaleFinish<kWorker>>), gw, dim3(wide::kBlock), 0, s,
+                       WorkerValues{m32, err_w}, n, ScaleFinish<kWorker>{dev_onebit, n}, part_w);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
     hipLaunchKernelGGL(onebit_compress_worker_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, err_s, bits_w, n,
-                       dev_state, dev_onebit, max_c);
+                       dev_state, warmup, dev_onebit, max_c);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
     hipLaunchKernelGGL(onebit_sum_server_kernel, g2, dim3(kNormBlock), 0, s, bits_w, err_s, n, max_c, pl.grid1,
-                       dev_state, dev_onebit, part_d);
+                       dev_state, warmup, dev_onebit, part_d);
+    if ((rc = launch_status()) != ZERO_OK)
+        return rc;
+    hipLaunchKernelGGL((wide::wide_sum_kernel<ServerValues, ScaleFinish<kServer>>), gw, dim3(wide::kBlock), 0, s,
+                       ServerValues{bits_w, err_s, dev_onebit}, n, ScaleFinish<kServer>{dev_onebit, n}, part_w);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
     hipLaunchKernelGGL(onebit_update_kernel, g1, dim3(kBlock), cap, s, p16, p32, m32, v32, err_s,
-                       bits_w, bits_s, n, dev_state, dev_onebit);
+                       bits_w, bits_s, n, dev_state, warmup, dev_onebit);
     return launch_status();
 }

@@ -75,6 +75,11 @@ static_assert(sizeof(NormPartial) == 32, "partial layout");
 
 uint64_t norm_grid(uint64_t n);
 
+// zero_shard_adam_step that runs only while dev_state->step <= gate (the
+// warm-up steps of zero_onebit_step); the same checks and errors.
+int adam_step_gated(uint16_t* p16, float* p32, float* m32, float* v32, const uint16_t* grad16, uint64_t n,
+                    const zero_step_state_t* dev_state, void* stream, int64_t gate);
+
 // Partials folded by the decide-only pass (the fused flatten writes one per
 // workgroup); stored partials are carried, so 2^30 of them fit in int64 sums.
 constexpr uint64_t kMaxPartials = uint64_t(1) << 30;

@@ -278,7 +278,8 @@ class AccumStep:
         Z.zero_shard_norm_overflow_f32(self.grad32, self.n, hp, self.state, self.workspace)
 
     def decide(self, hp: Z.HParams) -> None:
-        Z.zero_shard_decide(self.partials, self.partial_count, hp, self.state, self.decide_ws)
+        Z.zero_shard_decide_f32(self.partials, self.partial_count, self.grad32, self.n, hp, self.state,
+                                self.decide_ws)
 
     def adam(self) -> None:
         Z.zero_shard_adam_step_f32(self.p16, self.p32, self.m32, self.v32, self.grad32, self.n, self.state)
@@ -308,11 +309,13 @@ class AccumStep:
 
 class OneBitStep(ShardStep):
     """1-bit Adam on the shard (the DeepSpeed article; Tang et al. 2021,
-    Algorithm 1): the first `warmup` applied steps are the ordinary fused step,
+    Algorithm 1): the first `warmup` applied steps are the ordinary update,
     which also builds the variance; after them the variance is frozen and each
-    step runs the compression stage (zero_onebit_step) instead of the Adam
-    update.  The flatten with exact-norm partials and the decision are the same
-    in both stages."""
+    step runs the compression stage.  The flatten with exact-norm partials and
+    the decision are the same in both stages, and the device picks the stage
+    from its own applied-step count (zero_onebit_step), so a step never reads
+    the state back and a captured step replays correctly on both sides of the
+    hand-over."""
 
     def __init__(self, n: int, warmup: int, device="cuda"):
         import torch
@@ -324,29 +327,26 @@ class OneBitStep(ShardStep):
         self.onebit = torch.zeros(Z.ONEBIT_STATE_BYTES, dtype=torch.uint8, device=self.device)
         self.onebit_ws = torch.empty(max(256, Z.zero_onebit_workspace_bytes(self.n)), dtype=torch.uint8,
                                      device=self.device)
-        self.applied = 0                 # applied steps, counted on the host from the device state
 
     def init_state(self, initial_scale: float) -> None:
         super().init_state(initial_scale)
         Z.zero_onebit_state_init(self.onebit)
 
     def compressing(self) -> bool:
-        return self.applied >= self.warmup
+        """Whether the next step runs the compression stage (reads the state
+        back: a synchronisation, for callers outside the step)."""
+        return int(self.read_state().step) >= self.warmup
 
-    def compress(self) -> None:
+    def update(self) -> None:
+        """The update of a decided step: the ordinary one during the warm-up,
+        the compression stage after it (the device chooses)."""
         Z.zero_onebit_step(self.p16, self.p32, self.m32, self.v32, self.err_w, self.err_s, self.grad16, self.n,
-                           self.bits_w, self.bits_s, self.state, self.onebit, self.onebit_ws)
+                           self.bits_w, self.bits_s, self.state, self.onebit, self.warmup, self.onebit_ws)
 
     def step(self, hp: Z.HParams) -> None:
-        """One step; reads the applied-step count back (a 128-byte copy) to know
-        when the warm-up ends."""
         self.flatten_norm()
         self.decide(hp)
-        if self.compressing():
-            self.compress()
-        else:
-            self.adam()
-        self.applied = int(self.read_state().step)
+        self.update()
 
     def read_onebit(self) -> Z.OneBitState:
         return Z.read_onebit_state(self.onebit)
