@@ -84,6 +84,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        # torch first: the library then binds to the HIP runtime torch has
+        # already loaded (the same soname), so one runtime serves both;
+        # loaded the other way round, torch's tensors and this library's
+        # launches would live in two runtimes and the device calls fail.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         vp, u64, u32, i32 = C.c_void_p, C.c_uint64, C.c_uint32, C.c_int
         L.zero_status_string.argtypes = [i32]

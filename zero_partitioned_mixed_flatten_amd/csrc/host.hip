@@ -56,11 +56,11 @@ uint64_t decide_grid(uint64_t count)
 {
     // Up to 2^15 partials (1 MiB, L2-resident after the flatten) one workgroup
     // folds faster than several that must meet at an agent-scope arrival
-    // counter; beyond that, at least 32 partials per thread and at most one
-    // workgroup per CU.
+    // counter; beyond that, two partials per thread (a workgroup's loads are
+    // then all in flight at once) and at most one workgroup per CU.
     if (count <= (uint64_t(1) << 15))
         return 1;
-    const uint64_t per_block = uint64_t(kNormBlock) * 32;
+    const uint64_t per_block = uint64_t(kNormBlock) * 2;
     uint64_t g = (count + per_block - 1) / per_block;
     if (g < 2) g = 2;
     if (g > kNormMaxBlocks) g = kNormMaxBlocks;
