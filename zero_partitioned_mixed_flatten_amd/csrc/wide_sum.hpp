@@ -50,8 +50,14 @@ __host__ __device__ inline uint64_t grid(uint64_t n)
     return g;
 }
 
-// Adds x^2 (x finite) into the workgroup's LDS digits.
-__device__ __forceinline__ void add_square(uint64_t* acc, float x)
+// x^2 (x finite) as three base-2^32 digits d0, d1, d2 of weights 2^(32k),
+// 2^(32(k+1)), 2^(32(k+2)) units; k = -1 for x = 0.
+struct SquareDigits {
+    int k;
+    uint64_t d0, d1, d2;
+};
+
+__host__ __device__ inline SquareDigits square_digits(float x)
 {
     const uint32_t b = __builtin_bit_cast(uint32_t, x);
     const uint32_t field = (b >> 23) & 0xFFu;
@@ -62,19 +68,27 @@ __device__ __forceinline__ void add_square(uint64_t* acc, float x)
         e = int(field) - 150;
     }
     if (M == 0)
-        return;
+        return SquareDigits{-1, 0, 0, 0};
     const int pos = 2 * e - kUnitExp;               // x^2 = M^2 * 2^pos units, 0 <= pos <= 508
-    const int k = pos >> 5, sh = pos & 31;
+    const int sh = pos & 31;
     const uint64_t sq = M * M;                      // below 2^48
     const uint64_t lo = sq << sh;                   // bits 0..63 of sq * 2^sh
     const uint64_t hi = sh ? (sq >> (64 - sh)) : 0; // bits 64..79
-    const uint64_t d0 = lo & 0xFFFFFFFFull, d1 = lo >> 32;
-    if (d0)
-        atomicAdd(reinterpret_cast<unsigned long long*>(acc + k), (unsigned long long)d0);
-    if (d1)
-        atomicAdd(reinterpret_cast<unsigned long long*>(acc + k + 1), (unsigned long long)d1);
-    if (hi)
-        atomicAdd(reinterpret_cast<unsigned long long*>(acc + k + 2), (unsigned long long)hi);
+    return SquareDigits{pos >> 5, lo & 0xFFFFFFFFull, lo >> 32, hi};
+}
+
+// Adds x^2 (x finite) into the workgroup's LDS digits.
+__device__ __forceinline__ void add_square(uint64_t* acc, float x)
+{
+    const SquareDigits s = square_digits(x);
+    if (s.k < 0)
+        return;
+    if (s.d0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(acc + s.k), (unsigned long long)s.d0);
+    if (s.d1)
+        atomicAdd(reinterpret_cast<unsigned long long*>(acc + s.k + 1), (unsigned long long)s.d1);
+    if (s.d2)
+        atomicAdd(reinterpret_cast<unsigned long long*>(acc + s.k + 2), (unsigned long long)s.d2);
 }
 
 // Brings every digit below 2^32 (the top one keeps the rest).
