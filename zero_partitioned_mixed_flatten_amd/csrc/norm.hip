@@ -11,7 +11,11 @@
 // under a per-thread element bound, integer limbs across the grid, one
 // round-to-nearest-even at the end.  The result is the exactly rounded sum,
 // independent of grid shape and schedule, so the clip factor derived from it
-// is bitwise reproducible.
+// is bitwise reproducible.  An fp32 partition holding a value the fast sum
+// cannot take exactly (off the 2^-24 grid, or 2^24 or more in magnitude)
+// leaves the decision pending, and the wide pass launched right after
+// (wide_sum.hpp) sums it exactly and decides; otherwise that pass returns at
+// once.
 //
 // Two kernels share the tail:
 //   norm_overflow_kernel  reads the partition itself: 1024-thread workgroups,
@@ -22,7 +26,8 @@
 //   decide_kernel         folds the per-workgroup partials a fused flatten
 //                         (flatten.hip) already computed while copying; up
 //                         to 2^15 partials in a single workgroup, which then
-//                         decides without an arrival counter or fence.
+//                         decides without an arrival counter or fence, and
+//                         more two per thread over up to 256 workgroups.
 // In both, every workgroup stores its carried partial, bumps an agent-scope
 // acq_rel arrival counter once, and the last one to arrive folds all
 // partials, takes the decision in binary64 on one thread, writes it into the

@@ -6,11 +6,17 @@
 //   u = cw + es;  m = s_s*sgn(u);  es = u - m      (one rank is its own server)
 //   p = p - lr*(m/(sqrt(v)+eps) + wd*p),  p16 = fp16(p)
 // with sgn(x) = +1 for x >= 0, -1 otherwise, and s = ||x||_2/sqrt(d) in fp32
-// from an EXACT sum of squares: with E the binary exponent of max|x|, each
-// square is rounded to the nearest multiple of 2^(2E-80) (never a tie), the
-// integers are summed exactly and the total is rounded once to binary64.
+// from the EXACT sum of squares rounded once to binary64.  The fast sum
+// works in a window: with E the binary exponent of max|x|, each square is
+// rounded to the nearest multiple of 2^(2E-80) (never a tie) and the
+// integers are summed exactly; the exact sum then lies within n/2 units of
+// that integer W, and when W - n/2 and W + n/2 round to the same binary64
+// value that value is the exactly rounded sum.  When they do not, the wide
+// pass (wide_sum.hpp) sums the squares with no window and sets the scale.
 // The sign bits (one byte per 8 elements, element 8j+k in bit k of byte j)
-// are what a multi-rank run would exchange.
+// are what a multi-rank run would exchange.  The device picks the stage:
+// while the applied-step count is at most the warm-up length, these kernels
+// return before any load and the ordinary update runs instead.
 //
 // Five kernels, because two global scales sit on the data path:
 //   A  momentum + per-block max|x|           one-shot, 8 elements per thread
@@ -21,7 +27,8 @@
 //   C  worker compression: sign byte, ew, u = cw + es, per-block max|u|
 //   D  exact sum of u^2, s_s                  as B (u is recomputed from the bits)
 //   E  server compression + update: m, es, bits, p, p16
-// Per-block maxima go to memory (no same-address atomics, which serialise).
+// (a wide pass follows B and D; it returns at once unless the window could
+// not vouch for its sum).  Per-block maxima go to memory (no same-address atomics, which serialise).
 // Element layout of the one-shot kernels: the whole bytes of the sign payload
 // cover groups of 4 elements, g < 2*floor(n/8); thread t of workgroup b owns
 // groups 512b+t and 512b+t+256, so every vector load and store of a wave is
