@@ -301,6 +301,7 @@ def run_onebit(args, w, p32, grads_host, dev_sets, hp):
     n = w.n
     stream = torch.cuda.current_stream()
     dev = Z.OneBitStep(n, warmup=2)
+    dev.any_order = args.bucket_launch == "any-order"
     dev.p32.copy_(torch.from_numpy(p32))
     dev.p16.copy_(dev.p32.half())
     dev.init_state(w.scale0)
@@ -427,6 +428,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=30.0,
                     help="CPU-baseline budget; at least 3 whole oracle steps run whatever it is")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bucket-launch", default="any-order", choices=["any-order", "ordered"],
+                    help="a bucketed partition's flattens: one call for all buckets, consecutive buckets "
+                         "overlapping (any-order), or one ordered call per bucket")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only the streaming-copy reference (for counter calibration)")
     args = ap.parse_args()
@@ -482,10 +486,10 @@ def main():
     if accum:
         if not 1 <= K <= nsets:
             sys.exit(f"--micro-batches must be 1..{nsets}")
-        dev = Z.AccumStep(n, fused=True)
+        dev = Z.AccumStep(n, fused=True, any_order=(args.bucket_launch == "any-order"))
         plans = [dev.plan(d, w.layout.segments, w.bucket_elems)[1] for d in dev_sets[:K]]
     else:
-        dev = Z.ShardStep(n, fused=fused)
+        dev = Z.ShardStep(n, fused=fused, any_order=(args.bucket_launch == "any-order"))
         plans = []
         for d in dev_sets:
             dev.set_segments(d, w.layout.segments, w.bucket_elems)
@@ -648,7 +652,7 @@ def main():
                    "state": "fp16 p,g + fp32 p,m,v (16 B/param)" if not accum else
                             "fp16 p + fp32 g,p,m,v (18 B/param)", "loss_scale0": w.scale0,
                    "path": args.path, "micro_batches": K, "step_bytes_per_param": step_bpp,
-                   "hip_graph": bool(graphs)},
+                   "hip_graph": bool(graphs), "bucket_launch": args.bucket_launch},
         "roofline": {"bound": "hbm", "kernel": names[-1], "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": adam_bpp * n},

@@ -204,7 +204,7 @@ int zero_flatten_bucket(const zero_segment_t* segs, uint32_t nsegs, void* dst, u
 /* ---- fused flatten + norm (the norm without a second pass) ----------- */
 
 /* Bytes of one per-workgroup partial of the exact sum (opaque contents). */
-#define ZERO_NORM_PARTIAL_BYTES 32
+#define ZERO_NORM_PARTIAL_BYTES 16
 
 /* Number of partials zero_flatten_norm_bucket writes for this segment list
  * (one per workgroup it launches; host only, no device work).  0 for NULL. */
@@ -237,6 +237,34 @@ int zero_flatten_norm_bucket(const zero_segment_t* segs, uint32_t nsegs, uint16_
  * zero_flatten_norm_bucket.  Errors: as zero_flatten_norm_bucket. */
 int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t nsegs, float* dst, uint64_t dst_len,
                                  int accumulate, void* partials, uint64_t partials_capacity, void* stream);
+
+/* Several buckets of one step in one call: the same stores (and, with
+ * partials, the same partials) as calling zero_flatten_bucket -- or
+ * zero_flatten_norm_bucket / zero_flatten_norm_bucket_f32 when partials is
+ * not NULL -- once per bucket, in order, each bucket's partials right after
+ * the previous bucket's (paper card, "Method": the partition is one
+ * contiguous buffer; the buckets are windows of it).  The first launch waits
+ * for the work queued earlier on the stream, like any launch; the launches
+ * after it are issued without the dispatch barrier, so consecutive buckets
+ * overlap on the GPU instead of draining it between them.  Work queued on
+ * the stream after the call waits for all of them.  That is only safe
+ * because no two buckets touch a common element: every segment's
+ * destination range must be disjoint from every other's, and the call
+ * checks it.
+ * segs: HOST array of the buckets' segment lists, one after another;
+ * bucket_nsegs: HOST array of nbuckets counts; dst: device, binary16 or
+ * binary32 (dst_dtype), dst_len elements, 16-byte aligned; partials: NULL
+ * (no norm) or device, 16-byte aligned, partials_capacity entries of
+ * ZERO_NORM_PARTIAL_BYTES, at least zero_flatten_norm_partials(segs, total
+ * segments) of them.  dst_dtype and accumulate as for zero_flatten_bucket.
+ * Errors: those of zero_flatten_bucket and zero_flatten_norm_bucket;
+ *         ZERO_EINVAL also for NULL bucket_nsegs with nbuckets > 0 and for
+ *         two segments whose destination ranges overlap; ZERO_ERANGE for
+ *         more than 2^32 - 1 segments in all.  No device work is queued
+ *         when an error is returned. */
+int zero_flatten_buckets(const zero_segment_t* segs, const uint32_t* bucket_nsegs, uint32_t nbuckets, void* dst,
+                         uint64_t dst_len, int dst_dtype, int accumulate, void* partials,
+                         uint64_t partials_capacity, void* stream);
 
 /* Bytes of device workspace zero_shard_decide needs to fold `count` partials. */
 size_t zero_decide_workspace_bytes(uint64_t count);
@@ -301,7 +329,7 @@ int zero_shard_norm_overflow(const uint16_t* grad16, uint64_t n, const zero_hpar
  * loops, harnesses that forbid hipMalloc).  Same reduction, same kernels,
  * same result bits and errors, except:
  *   - the per-workgroup partials live in a fixed device array inside the
- *     library (256 partials, 8 KiB), which each GPU the library runs on holds
+ *     library (256 partials, 4 KiB), which each GPU the library runs on holds
  *     from the first call on that GPU until the process ends; its device
  *     address is looked up once per GPU, on that call, with that GPU current;
  *   - hence n <= 2^30 (ZERO_ERANGE above; the largest n whose grid of at

@@ -120,8 +120,11 @@ class Run:
         return np.arange(self.n) if self.sample is None else self.sample
 
 
-def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77, fused: bool = False) -> Run:
-    """fused: run the step as flatten-with-norm-partials + decide + Adam."""
+def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77, fused: bool = False,
+          any_order: bool = True) -> Run:
+    """fused: run the step as flatten-with-norm-partials + decide + Adam;
+    any_order: all buckets in one zero_flatten_buckets call (else one ordered
+    call per bucket)."""
     r = Run(w)
     n = w.n
     if sample is not None and sample < n:
@@ -132,7 +135,7 @@ def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77, fu
         edges += list(range(min(n, 64))) + list(range(max(0, n - 64), n))
         r.sample = np.unique(np.clip(np.concatenate([rng.integers(0, n, sample), np.array(edges)]), 0, n - 1))
     p32 = shardgen.master_params(w)
-    r.dev = Z.ShardStep(n, fused=fused)
+    r.dev = Z.ShardStep(n, fused=fused, any_order=any_order)
     if n:
         r.dev.p32.copy_(torch.from_numpy(p32))
         r.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
@@ -242,7 +245,7 @@ class AccumRun:
 
 
 def start_accum(w: shardgen.Workload, micro: int, sample: Optional[int] = None, seed: int = 78,
-                fused: bool = True) -> AccumRun:
+                fused: bool = True, any_order: bool = True) -> AccumRun:
     r = AccumRun(w, micro)
     n = w.n
     if sample is not None and sample < n:
@@ -253,7 +256,7 @@ def start_accum(w: shardgen.Workload, micro: int, sample: Optional[int] = None, 
         edges += list(range(min(n, 64))) + list(range(max(0, n - 64), n))
         r.sample = np.unique(np.clip(np.concatenate([rng.integers(0, n, sample), np.array(edges)]), 0, n - 1))
     p32 = shardgen.master_params(w)
-    r.dev = Z.AccumStep(n, fused=fused)
+    r.dev = Z.AccumStep(n, fused=fused, any_order=any_order)
     if n:
         r.dev.p32.copy_(torch.from_numpy(p32))
         r.dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))

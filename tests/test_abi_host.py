@@ -47,6 +47,12 @@ def test_struct_sizes(Z):
     assert C.sizeof(Z.StepState) == 128 and C.sizeof(Z.Segment) == 32 and C.sizeof(Z.HParams) == 80
 
 
+def test_partial_bytes_match_header(Z):
+    # the binding sizes partial buffers with its own copy of the header's constant
+    m = re.search(r"#define\s+ZERO_NORM_PARTIAL_BYTES\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == Z.NORM_PARTIAL_BYTES == 16
+
+
 def test_state_bytes_matches_oracle(Z, oracle):
     rng = np.random.default_rng(5)
     for _ in range(2000):
@@ -212,6 +218,34 @@ def test_fused_validation(Z, fn):
     assert f(arr, k, FAKE + 2, 5000, 0, FAKE, need, None) == E.ZERO_EALIGN
     assert f(arr, k, FAKE + 8, 5000, 1, FAKE, need, None) == E.ZERO_EALIGN
     assert f(None, 0, 0, 0, 0, 0, 0, None) == E.ZERO_OK
+
+
+def test_buckets_validation(Z):
+    """zero_flatten_buckets rejects, before any device work, what the
+    per-bucket calls reject and also destination ranges that overlap across
+    (or within) buckets, since its later launches are not ordered."""
+    L, E = Z.lib(), Z._lib
+    plan = Z.BucketPlan([Z.make_segments([(FAKE, 0, 0, 3000), (FAKE, 0, 3000, 1000)]),
+                         Z.make_segments([(FAKE, 0, 4000, 1000)])])
+    need = plan.partials()
+    assert need == sum(Z.zero_flatten_norm_partials(a, k) for a, k in plan) == 3
+    f = L.zero_flatten_buckets
+    call = lambda p=plan, nb=None, dst=FAKE, n=5000, dt=Z.ZERO_F16, acc=0, part=FAKE, cap=need: f(
+        p.segs, p.counts, len(p) if nb is None else nb, dst, n, dt, acc, part, cap, None)
+    assert call(dt=7) == E.ZERO_EINVAL
+    assert f(plan.segs, None, 2, FAKE, 5000, Z.ZERO_F16, 0, 0, 0, None) == E.ZERO_EINVAL
+    assert call(n=4999) == E.ZERO_ERANGE
+    assert call(dst=FAKE + 2) == E.ZERO_EALIGN
+    assert call(part=FAKE + 8) == E.ZERO_EALIGN
+    assert call(cap=need - 1) == E.ZERO_ERANGE
+    assert call(dt=Z.ZERO_F32, cap=need - 1) == E.ZERO_ERANGE
+    for a, b in [((0, 3000), (2999, 10)), ((100, 10), (100, 1)), ((0, 5000), (4000, 1000))]:
+        bad = Z.BucketPlan([Z.make_segments([(FAKE, 0, a[0], a[1])]), Z.make_segments([(FAKE, 0, b[0], b[1])])])
+        assert f(bad.segs, bad.counts, 2, FAKE, 5000, Z.ZERO_F16, 0, 0, 0, None) == E.ZERO_EINVAL, (a, b)
+        assert f(bad.segs, bad.counts, 2, FAKE, 5000, Z.ZERO_F16, 0, FAKE, 1 << 20, None) == E.ZERO_EINVAL
+    touching = Z.BucketPlan([Z.make_segments([(FAKE, 0, 0, 3000), (FAKE, 0, 3000, 0), (FAKE, 0, 1000, 0)])])
+    assert L.zero_flatten_norm_partials(touching.segs, touching.nsegs) == 1     # empty segments are skipped
+    assert f(None, None, 0, 0, 0, Z.ZERO_F16, 0, 0, 0, None) == E.ZERO_OK        # nothing to do
 
 
 def test_decide_validation(Z):

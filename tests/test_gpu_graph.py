@@ -23,8 +23,11 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.float16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("onebit", [False, True])
-def test_fused_step_graph_replays_match_eager(onebit):
+@pytest.mark.parametrize("onebit,bucket", [(False, 0), (True, 0), (False, 100_000)])
+def test_fused_step_graph_replays_match_eager(onebit, bucket):
+    """bucket > 0: the partition is flattened in buckets, which the eager twin
+    issues without dispatch barriers between them and the capture records as
+    ordinary graph nodes."""
     rng = np.random.default_rng(61)
     n = 600_011
     numels, segs = shardgen.random_segments(rng, n, 90_000)
@@ -43,8 +46,9 @@ def test_fused_step_graph_replays_match_eager(onebit):
     eager, graphed = make(), make()
     src_e = [torch.zeros(k, dtype=torch.float16, device="cuda") for k in numels]
     src_g = [torch.zeros(k, dtype=torch.float16, device="cuda") for k in numels]
-    eager.set_segments(src_e, segs)
-    graphed.set_segments(src_g, segs)
+    eager.set_segments(src_e, segs, bucket)
+    graphed.set_segments(src_g, segs, bucket)
+    assert len(eager.buckets) == (7 if bucket else 1)
 
     def load(k):
         gpart = shardgen.grad_partition(w, k, 2.0 ** 16)

@@ -51,12 +51,13 @@ def test_ragged_sizes_misaligned_segments(n, fused):
     assert r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
+@pytest.mark.parametrize("any_order", [False, True])
 @pytest.mark.parametrize("fused", [False, True])
-def test_many_segments_over_launch_limit(fused):
+def test_many_segments_over_launch_limit(fused, any_order):
     # > 64 segments forces several flatten launches in one call
     w = _small("many", 300_000, seed=3, max_seg=2000, misalign=False)
     assert len(w.layout.segments) > 64
-    r = H.start(w, fused=fused)
+    r = H.start(w, fused=fused, any_order=any_order)
     for _ in range(2):
         H.step(r)
 

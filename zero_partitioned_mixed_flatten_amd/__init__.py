@@ -6,12 +6,12 @@ ctypes binding with the same entry-point names plus a small helper that wires
 them to torch-owned device buffers.  Importing it loads the library and fails
 loudly if it has not been built -- there is no CPU fallback.
 """
-from ._lib import (EXPORTS, NORM_PARTIAL_BYTES, ONEBIT_STATE_BYTES, STATE_BYTES, ZERO_F16, ZERO_F32, HParams,
-                   OneBitState, Segment, StepState, read_onebit_state, zero_onebit_state_init,
+from ._lib import (EXPORTS, NORM_PARTIAL_BYTES, ONEBIT_STATE_BYTES, STATE_BYTES, ZERO_F16, ZERO_F32, BucketPlan,
+                   HParams, OneBitState, Segment, StepState, read_onebit_state, zero_onebit_state_init,
                    zero_onebit_step, zero_onebit_workspace_bytes,
                    ZeroError, lib, make_segments, read_state, zero_bucket_segments, zero_decide_workspace_bytes,
-                   zero_flatten_bucket, zero_flatten_norm_bucket, zero_flatten_norm_bucket_f32,
-                   zero_flatten_norm_partials, zero_norm_workspace_bytes, zero_shard_adam_step,
+                   zero_flatten_bucket, zero_flatten_buckets, zero_flatten_norm_bucket,
+                   zero_flatten_norm_bucket_f32, zero_flatten_norm_partials, zero_norm_workspace_bytes, zero_shard_adam_step,
                    zero_shard_adam_step_f32, zero_shard_decide, zero_shard_decide_f32, zero_shard_norm_overflow,
                    zero_shard_norm_overflow_f32, zero_shard_norm_overflow_noalloc, zero_state_bytes,
                    zero_status_string, zero_step_state_init,
@@ -21,9 +21,9 @@ from .stepper import AccumStep, HostContext, OffloadStep, OneBitStep, ShardStep,
 
 lib()
 
-__all__ = ["EXPORTS", "NORM_PARTIAL_BYTES", "STATE_BYTES", "ZERO_F16", "ZERO_F32", "AccumStep", "HParams",
+__all__ = ["EXPORTS", "NORM_PARTIAL_BYTES", "STATE_BYTES", "ZERO_F16", "ZERO_F32", "AccumStep", "BucketPlan", "HParams",
            "Segment", "ShardStep", "StepState", "ZeroError", "hparams", "lib", "make_segments", "read_state",
-           "zero_bucket_segments", "zero_decide_workspace_bytes", "zero_flatten_bucket",
+           "zero_bucket_segments", "zero_decide_workspace_bytes", "zero_flatten_bucket", "zero_flatten_buckets",
            "zero_flatten_norm_bucket", "zero_flatten_norm_bucket_f32", "zero_flatten_norm_partials",
            "zero_norm_workspace_bytes", "zero_shard_adam_step", "zero_shard_adam_step_f32", "zero_shard_decide", "zero_shard_decide_f32",
            "zero_shard_norm_overflow", "zero_shard_norm_overflow_f32", "zero_shard_norm_overflow_noalloc",

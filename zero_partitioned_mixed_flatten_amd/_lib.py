@@ -19,12 +19,12 @@ ZERO_F16, ZERO_F32 = 1, 2
 EXPORTS = ("zero_status_string", "zero_state_bytes", "zero_bucket_segments", "zero_step_state_init",
            "zero_flatten_bucket", "zero_norm_workspace_bytes", "zero_shard_norm_overflow",
            "zero_shard_adam_step", "zero_stream_copy", "zero_flatten_norm_partials", "zero_flatten_norm_bucket",
-           "zero_decide_workspace_bytes", "zero_shard_decide", "zero_flatten_norm_bucket_f32",
+           "zero_decide_workspace_bytes", "zero_shard_decide", "zero_flatten_norm_bucket_f32", "zero_flatten_buckets",
            "zero_shard_norm_overflow_f32", "zero_shard_adam_step_f32", "zero_host_create", "zero_host_destroy",
            "zero_host_threads", "zero_host_state_init", "zero_host_norm_overflow", "zero_host_adam_step",
            "zero_offload_step", "zero_host_stream_copy", "zero_onebit_state_init", "zero_onebit_workspace_bytes",
            "zero_onebit_step", "zero_shard_norm_overflow_noalloc", "zero_shard_decide_f32")
-NORM_PARTIAL_BYTES = 32
+NORM_PARTIAL_BYTES = 16
 
 
 class ZeroError(RuntimeError):
@@ -110,6 +110,7 @@ def lib():
         L.zero_flatten_norm_partials.restype = u64
         L.zero_flatten_norm_bucket.argtypes = [C.POINTER(Segment), u32, vp, u64, i32, vp, u64, vp]
         L.zero_flatten_norm_bucket_f32.argtypes = [C.POINTER(Segment), u32, vp, u64, i32, vp, u64, vp]
+        L.zero_flatten_buckets.argtypes = [C.POINTER(Segment), C.POINTER(u32), u32, vp, u64, i32, i32, vp, u64, vp]
         L.zero_decide_workspace_bytes.argtypes = [u64]
         L.zero_decide_workspace_bytes.restype = C.c_size_t
         L.zero_shard_decide.argtypes = [vp, u64, C.POINTER(HParams), vp, vp, C.c_size_t, vp]
@@ -206,6 +207,36 @@ def zero_bucket_segments(segs, nsegs: int, begin: int, end: int):
     return out, got.value
 
 
+class BucketPlan:
+    """The buckets of one step as zero_flatten_buckets takes them: every
+    bucket's segments in one host array and the per-bucket counts, built once.
+    Iterates as the (segments, count) pairs it was made from."""
+
+    def __init__(self, buckets):
+        self.parts = [(segs, int(k)) for segs, k in buckets]
+        self.nsegs = sum(k for _, k in self.parts)
+        self.segs = (Segment * max(1, self.nsegs))()
+        size, pos = C.sizeof(Segment), 0
+        for segs, k in self.parts:
+            if k:
+                C.memmove(C.addressof(self.segs) + pos * size, C.addressof(segs), k * size)
+            pos += k
+        self.counts = (C.c_uint32 * max(1, len(self.parts)))(*[k for _, k in self.parts])
+
+    def __len__(self):
+        return len(self.parts)
+
+    def __iter__(self):
+        return iter(self.parts)
+
+    def __getitem__(self, i):
+        return self.parts[i]
+
+    def partials(self) -> int:
+        """Partials the fused form writes for the whole plan."""
+        return int(lib().zero_flatten_norm_partials(self.segs, self.nsegs))
+
+
 def zero_norm_workspace_bytes(n: int) -> int:
     return int(lib().zero_norm_workspace_bytes(n))
 
@@ -291,6 +322,25 @@ def zero_flatten_norm_bucket(segs, nsegs: int, dst, partials, dst_len: Optional[
     _check("zero_flatten_norm_bucket",
            lib().zero_flatten_norm_bucket(segs, nsegs, _ptr(dst), dst_len, int(bool(accumulate)), ptr, cap,
                                           _stream(stream)))
+
+
+def zero_flatten_buckets(plan, dst, dst_len: Optional[int] = None, dst_dtype: int = ZERO_F16,
+                         accumulate: bool = False, partials=None, partials_offset: int = 0, stream=None) -> None:
+    """Every bucket of `plan` (a BucketPlan, or (segments, count) pairs) in one
+    call, consecutive buckets overlapping on the GPU; with `partials` (a
+    uint8 device buffer) the fused form, writing from entry `partials_offset`."""
+    if not isinstance(plan, BucketPlan):
+        plan = BucketPlan(plan)
+    if dst_len is None:
+        dst_len = dst.numel()
+    _need("zero_flatten_buckets", dst, dst_len * (4 if dst_dtype == ZERO_F32 else 2))
+    ptr, cap = 0, 0
+    if partials is not None:
+        cap = partials.numel() // NORM_PARTIAL_BYTES - partials_offset
+        ptr = _ptr(partials) + partials_offset * NORM_PARTIAL_BYTES
+    _check("zero_flatten_buckets",
+           lib().zero_flatten_buckets(plan.segs, plan.counts, len(plan), _ptr(dst), dst_len, dst_dtype,
+                                      int(bool(accumulate)), ptr, cap, _stream(stream)))
 
 
 def zero_flatten_norm_bucket_f32(segs, nsegs: int, dst, partials, dst_len: Optional[int] = None,

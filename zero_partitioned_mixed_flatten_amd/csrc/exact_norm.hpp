@@ -30,7 +30,8 @@
 
 // The sums become signed base-2^32 limbs that threads, workgroups and the
 // grid add without carries.  A workgroup's partial is stored carried (each
-// limb below 2^32), so any number of partials up to 2^30 adds inside int64.
+// limb below 2^32, the top one below 2^30), so any number of partials up to
+// 2^30 adds inside int64.
 // At the end one thread carries the total into 128 bits and converts it to
 // binary64 with a single round-to-nearest-even: the exactly rounded sum,
 // independent of grid shape and schedule.  A total of 2^128 units or more
@@ -173,14 +174,14 @@ __device__ __forceinline__ Limbs carry(Limbs s)
     return s;
 }
 
-// Adds a stored partial (two carried 64-bit words) as four 32-bit limbs.
+// Adds a stored partial as four 32-bit limbs and ORs in its status bits.
 __device__ __forceinline__ void fold_partial(Limbs& s, uint32_t& flag, const NormPartial& p)
 {
     s.l0 += int64_t(p.w0 & 0xFFFFFFFFull);
     s.l1 += int64_t(p.w0 >> 32);
     s.l2 += int64_t(p.w1 & 0xFFFFFFFFull);
-    s.l3 += int64_t(p.w1 >> 32);
-    flag |= p.flag;
+    s.l3 += int64_t((p.w1 >> 32) & 0x3FFFFFFFull);
+    flag |= uint32_t(p.w1 >> kPartialStatusShift);
 }
 
 // The total as an unsigned 128-bit value; false if it is 2^128 or more.
@@ -231,16 +232,18 @@ __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
     }
 }
 
-// A workgroup's partial: the carried sum in two words and the status bits; a
-// sum of 2^128 units or more asks for the wide pass.
+// A workgroup's partial: the carried sum and the status bits (kOvf, kWide
+// fit the two bits); a sum of 2^126 units or more asks for the wide pass,
+// and then its value is not used.
 __device__ __forceinline__ NormPartial make_partial(Limbs s, uint32_t status)
 {
+    static_assert((kOvf | kWide) < 4u, "status bits");
     s = carry(s);
+    if (s.l3 >> 30)
+        status |= kWide;
     NormPartial p;
     p.w0 = uint64_t(s.l0) | (uint64_t(s.l1) << 32);
-    p.w1 = uint64_t(s.l2) | (uint64_t(s.l3) << 32);
-    p.flag = status | ((s.l3 >> 32) != 0 ? kWide : 0u);
-    p.pad[0] = p.pad[1] = p.pad[2] = 0;
+    p.w1 = uint64_t(s.l2) | (uint64_t(s.l3 & 0x3FFFFFFFll) << 32) | (uint64_t(status) << kPartialStatusShift);
     return p;
 }
 

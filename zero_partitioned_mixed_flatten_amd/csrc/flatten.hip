@@ -28,7 +28,12 @@
 // It takes four vectors per thread (the workgroup fold is amortised over
 // 8192 elements) and nontemporal stores (nothing reads the partition before
 // the Adam pass, and draining dirty cache lines during it costs more).
+#include <hip/hip_ext.h>
+
+#include <algorithm>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "exact_norm.hpp"
 
@@ -292,14 +297,28 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     }
 }
 
+// One launch.  ordered = false clears the barrier bit of the dispatch packet
+// (hipExtAnyOrderLaunch): the packet processor may then start this kernel's
+// workgroups while earlier kernels of the stream are still running, so
+// back-to-back flattens of disjoint buckets overlap their ramp and drain.
+template <int MODE, bool NORM>
+void launch_one(const FlatArgs& a, uint32_t blocks, void* dst, hipStream_t s, bool ordered)
+{
+    if (ordered)
+        hipLaunchKernelGGL((flatten_kernel<MODE, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst);
+    else
+        hipExtLaunchKernelGGL((flatten_kernel<MODE, NORM>), dim3(blocks), dim3(kBlock), 0, s, nullptr, nullptr,
+                              uint32_t(hipExtAnyOrderLaunch), a, dst);
+}
+
 template <bool NORM>
-int launch(const FlatArgs& a, uint32_t blocks, int mode, void* dst, hipStream_t s)
+int launch(const FlatArgs& a, uint32_t blocks, int mode, void* dst, hipStream_t s, bool ordered = true)
 {
     switch (mode) {
-    case kCopy16: hipLaunchKernelGGL((flatten_kernel<kCopy16, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    case kAcc16: hipLaunchKernelGGL((flatten_kernel<kAcc16, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    case kTo32: hipLaunchKernelGGL((flatten_kernel<kTo32, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
-    default: hipLaunchKernelGGL((flatten_kernel<kAcc32, NORM>), dim3(blocks), dim3(kBlock), 0, s, a, dst); break;
+    case kCopy16: launch_one<kCopy16, NORM>(a, blocks, dst, s, ordered); break;
+    case kAcc16: launch_one<kAcc16, NORM>(a, blocks, dst, s, ordered); break;
+    case kTo32: launch_one<kTo32, NORM>(a, blocks, dst, s, ordered); break;
+    default: launch_one<kAcc32, NORM>(a, blocks, dst, s, ordered); break;
     }
     return launch_status();
 }
@@ -441,4 +460,91 @@ extern "C" int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t
 {
     return flatten_norm(segs, nsegs, dst, dst_len, accumulate ? kAcc32 : kTo32, partials, partials_capacity,
                         stream);
+}
+
+namespace zero {
+namespace {
+
+// ZERO_EINVAL if two nonempty segments write a common destination element.
+int check_disjoint(const zero_segment_t* segs, uint64_t nsegs)
+{
+    std::vector<std::pair<uint64_t, uint64_t>> r;
+    r.reserve(nsegs);
+    for (uint64_t i = 0; i < nsegs; ++i)
+        if (segs[i].count)
+            r.emplace_back(segs[i].dst_off, segs[i].count);
+    std::sort(r.begin(), r.end());
+    for (size_t i = 1; i < r.size(); ++i)
+        if (r[i].first - r[i - 1].first < r[i - 1].second)     // sorted: r[i].first >= r[i-1].first
+            return ZERO_EINVAL;
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zero
+
+extern "C" int zero_flatten_buckets(const zero_segment_t* segs, const uint32_t* bucket_nsegs, uint32_t nbuckets,
+                                    void* dst, uint64_t dst_len, int dst_dtype, int accumulate, void* partials,
+                                    uint64_t partials_capacity, void* stream)
+{
+    if (dst_dtype != ZERO_F16 && dst_dtype != ZERO_F32)
+        return ZERO_EINVAL;
+    if (nbuckets && !bucket_nsegs)
+        return ZERO_EINVAL;
+    uint64_t total = 0;
+    for (uint32_t b = 0; b < nbuckets; ++b)
+        total += bucket_nsegs[b];
+    if (total > 0xFFFFFFFFull)
+        return ZERO_ERANGE;
+    int rc = validate(segs, uint32_t(total), dst, dst_len);
+    if (rc != ZERO_OK)
+        return rc;
+    rc = check_disjoint(segs, total);
+    if (rc != ZERO_OK)
+        return rc;
+    const bool norm = partials != nullptr;
+    if (norm) {
+        if (!is_aligned(partials, 16))
+            return ZERO_EALIGN;
+        if (zero_flatten_norm_partials(segs, uint32_t(total)) > partials_capacity)
+            return ZERO_ERANGE;
+    }
+    const int mode = (dst_dtype == ZERO_F16 ? kCopy16 : kTo32) + (accumulate ? 1 : 0);
+    hipStream_t s = (hipStream_t)stream;
+    NormPartial* next = static_cast<NormPartial*>(partials);
+    bool ordered = true;          // the first launch waits for the stream's earlier work
+    int capturing = -1;           // looked up after the first launch
+    // After a launch: whether the next one keeps the dispatch barrier.  Under
+    // stream capture the launches become graph nodes, ordered by the graph's
+    // edges, so they are captured as ordinary launches.
+    auto after_launch = [&](int rc_launch) {
+        if (rc_launch != ZERO_OK)
+            return rc_launch;
+        if (capturing < 0) {
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            const hipError_t e = hipStreamIsCapturing(s, &cap);
+            if (e != hipSuccess)
+                return hip_fail(e);
+            capturing = cap != hipStreamCaptureStatusNone ? 1 : 0;
+        }
+        ordered = capturing != 0;
+        return int(ZERO_OK);
+    };
+    const zero_segment_t* b = segs;
+    for (uint32_t k = 0; k < nbuckets; ++k) {
+        if (norm)
+            rc = for_each_launch<true>(b, bucket_nsegs[k], [&](FlatArgs& a, uint32_t blocks) {
+                a.partials = next;
+                next += blocks;
+                return after_launch(launch<true>(a, blocks, mode, dst, s, ordered));
+            });
+        else
+            rc = for_each_launch<false>(b, bucket_nsegs[k], [&](FlatArgs& a, uint32_t blocks) {
+                return after_launch(launch<false>(a, blocks, mode, dst, s, ordered));
+            });
+        if (rc != ZERO_OK)
+            return rc;
+        b += bucket_nsegs[k];
+    }
+    return ZERO_OK;
 }

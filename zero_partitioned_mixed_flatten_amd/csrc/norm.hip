@@ -72,17 +72,21 @@ __device__ __forceinline__ void publish_and_decide(Limbs s, uint32_t flag, zero_
     __shared__ uint32_t s_last;
     if (threadIdx.x == 0) {
         ws[blockIdx.x] = exact::make_partial(s, flag);
-        // release this block's partial / acquire everyone else's
-        const uint32_t prev = __hip_atomic_fetch_add(&st->done_blocks, 1u, __ATOMIC_ACQ_REL,
+        // Release this workgroup's partial.  Only the last workgroup acquires
+        // the others' (its increment ends the release sequence of every
+        // earlier one), so the rest skip the acquire's cache invalidation.
+        const uint32_t prev = __hip_atomic_fetch_add(&st->done_blocks, 1u, __ATOMIC_RELEASE,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+        const bool last = prev == gridDim.x - 1;
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last ? 1u : 0u;
     }
     __syncthreads();
     if (!s_last)
         return;
 
     // Last workgroup: fold every partial (integer limbs: order is irrelevant).
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     Limbs t{0, 0, 0, 0};
     uint32_t tflag = 0;
     for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock)
@@ -187,12 +191,14 @@ __global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* _
     uint32_t flag = 0;
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
     uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
-    for (; i + 3 * stride < count; i += 4 * stride) {          // four partials' loads in flight
-        const NormPartial a = in[i], b = in[i + stride], c = in[i + 2 * stride], e = in[i + 3 * stride];
-        exact::fold_partial(s, flag, a);
-        exact::fold_partial(s, flag, b);
-        exact::fold_partial(s, flag, c);
-        exact::fold_partial(s, flag, e);
+    for (; i + 7 * stride < count; i += 8 * stride) {          // eight partials' loads in flight
+        NormPartial q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            q[k] = in[i + k * stride];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            exact::fold_partial(s, flag, q[k]);
     }
     for (; i < count; i += stride)
         exact::fold_partial(s, flag, in[i]);

@@ -351,14 +351,17 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
     __shared__ uint32_t s_last;
     if (threadIdx.x == 0) {
         ws[blockIdx.x] = exact::make_partial(s, 0);
-        const uint32_t prev = __hip_atomic_fetch_add(&ob->done_blocks, 1u, __ATOMIC_ACQ_REL,
+        // release this partial; the last workgroup acquires everyone's
+        const uint32_t prev = __hip_atomic_fetch_add(&ob->done_blocks, 1u, __ATOMIC_RELEASE,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+        const bool last = prev == gridDim.x - 1;
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last ? 1u : 0u;
     }
     __syncthreads();
     if (!s_last)
         return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     exact::Limbs t{0, 0, 0, 0};
     uint32_t tflag = 0;
     for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock)

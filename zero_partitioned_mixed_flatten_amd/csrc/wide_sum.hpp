@@ -175,14 +175,16 @@ __global__ __launch_bounds__(kBlock) void wide_sum_kernel(Src src, uint64_t n, F
             p.d[j] = acc[j];
         carry(p.d);
         ws[blockIdx.x] = p;
-        // release this workgroup's partial / acquire everyone else's
-        const uint32_t prev = __hip_atomic_fetch_add(fin.counter(), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+        // release this workgroup's partial; the last workgroup acquires everyone's
+        const uint32_t prev = __hip_atomic_fetch_add(fin.counter(), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == gridDim.x - 1;
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last ? 1u : 0u;
     }
     __syncthreads();
     if (!s_last)
         return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __shared__ uint64_t tot[kDigits];
     if (threadIdx.x < kDigits) {
         uint64_t t = 0;                             // at most 512 digits below 2^32

@@ -63,15 +63,16 @@ constexpr uint64_t kNormMaxBlocks = 256;                    // one per CU of an 
 constexpr uint64_t kNormMaxPerThread = uint64_t(1) << 12;   // keeps the binary64 partial sums exact
 constexpr uint64_t kNormMaxElems = uint64_t(1) << 40;       // keeps the grid within 2^18 workgroups
 
-// One workgroup's exact partial: the sum of squares in 2^-48 units as a
-// carried 128-bit value (w0 low word, w1 high word), plus the OR-ed overflow
-// test bits.
+// One workgroup's exact partial in 16 bytes, one vector load: the sum of
+// squares in 2^-48 units, below 2^126, as w0 + 2^64 * (w1 mod 2^62), and the
+// OR-ed status bits in the top two bits of w1.  No partial of a valid fast
+// reduction comes near 2^126 units: a workgroup adds at most 2^22 squares,
+// each below 2^96 units; a larger sum is marked for the wide pass.
 struct alignas(16) NormPartial {
     uint64_t w0, w1;
-    uint32_t flag;
-    uint32_t pad[3];
 };
-static_assert(sizeof(NormPartial) == 32, "partial layout");
+static_assert(sizeof(NormPartial) == 16 && sizeof(NormPartial) == ZERO_NORM_PARTIAL_BYTES, "partial layout");
+constexpr int kPartialStatusShift = 62;
 
 uint64_t norm_grid(uint64_t n);
 

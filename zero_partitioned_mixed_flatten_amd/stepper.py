@@ -109,9 +109,11 @@ class ShardStep:
     """fused=False: flatten, then the standalone exact-norm pass over the
     partition.  fused=True: the flatten computes the exact-norm partials while
     it copies and a decide-only pass folds them (no second read of the
-    partition).  Both take bit-identical decisions."""
+    partition).  Both take bit-identical decisions.  any_order=True flattens
+    all buckets of a step in one zero_flatten_buckets call (consecutive
+    buckets overlap on the GPU); False issues one ordered call per bucket."""
 
-    def __init__(self, n: int, device="cuda", fused: bool = False, extra=()):
+    def __init__(self, n: int, device="cuda", fused: bool = False, extra=(), any_order: bool = True):
         """extra: further (name, numel, dtype) arrays placed in the same arena
         after the five of the step (attributes of the same names)."""
         import torch
@@ -126,15 +128,26 @@ class ShardStep:
         self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
         ws = Z.zero_norm_workspace_bytes(self.n)
         self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
-        self.buckets: List[Tuple[object, int]] = []
+        self._buckets = Z.BucketPlan([])
         self._sources: Sequence = ()
         self.fused = bool(fused)
-        self.partials = None            # fused form: one 32-byte partial per flatten workgroup
+        self.any_order = bool(any_order)
+        self.partials = None            # fused form: one 16-byte partial per flatten workgroup
         self.partial_offsets: List[int] = []
         self.partial_count = 0
         self.decide_ws = None
 
     # ---- set-up ----------------------------------------------------------------
+    @property
+    def buckets(self) -> "Z.BucketPlan":
+        """The step's buckets: a BucketPlan (assign one, or (segments, count)
+        pairs, which are turned into one)."""
+        return self._buckets
+
+    @buckets.setter
+    def buckets(self, plan) -> None:
+        self._buckets = plan if isinstance(plan, Z.BucketPlan) else Z.BucketPlan(plan)
+
     def init_state(self, initial_scale: float) -> None:
         Z.zero_step_state_init(self.state, initial_scale)
 
@@ -142,7 +155,7 @@ class ShardStep:
                      bucket_elems: int = 0) -> None:
         """sources: device fp16 tensors; segments: (tensor index, src_off,
         dst_off, count).  With bucket_elems > 0 the partition is flattened in
-        windows of that many destination elements, one call each."""
+        windows of that many destination elements."""
         self._sources = list(sources)                  # keep the tensors alive
         segs, nsegs = _segments(self._sources, segments, "ShardStep.set_segments")
         if bucket_elems and bucket_elems < self.n:
@@ -169,6 +182,9 @@ class ShardStep:
 
     # ---- the step ---------------------------------------------------------------
     def flatten(self) -> None:
+        if self.any_order:
+            Z.zero_flatten_buckets(self.buckets, self.grad16, self.n, Z.ZERO_F16, False)
+            return
         for segs, nsegs in self.buckets:
             Z.zero_flatten_bucket(segs, nsegs, self.grad16, self.n, Z.ZERO_F16, False)
 
@@ -179,6 +195,9 @@ class ShardStep:
         Z.zero_shard_adam_step(self.p16, self.p32, self.m32, self.v32, self.grad16, self.n, self.state)
 
     def flatten_norm(self) -> None:
+        if self.any_order:
+            Z.zero_flatten_buckets(self.buckets, self.grad16, self.n, Z.ZERO_F16, False, self.partials)
+            return
         for (segs, nsegs), off in zip(self.buckets, self.partial_offsets):
             Z.zero_flatten_norm_bucket(segs, nsegs, self.grad16, self.partials, self.n, False, off)
 
@@ -212,7 +231,7 @@ class AccumStep:
     the decide-only pass; fused=False runs the standalone fp32 reduction.
     Both take bit-identical decisions."""
 
-    def __init__(self, n: int, device="cuda", fused: bool = True):
+    def __init__(self, n: int, device="cuda", fused: bool = True, any_order: bool = True):
         import torch
         self.n = int(n)
         alloc = max(1, self.n)
@@ -226,6 +245,7 @@ class AccumStep:
         ws = Z.zero_norm_workspace_bytes(self.n)
         self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
         self.fused = bool(fused)
+        self.any_order = bool(any_order)
         self.partials = None
         self.decide_ws = None
         self.partial_count = 0
@@ -235,7 +255,7 @@ class AccumStep:
         Z.zero_step_state_init(self.state, initial_scale)
 
     def plan(self, sources: Sequence, segments: Sequence[Tuple[int, int, int, int]], bucket_elems: int = 0):
-        """One micro-batch's segment plan: (kept sources, [(segs, nsegs), ...])."""
+        """One micro-batch's segment plan: (kept sources, BucketPlan)."""
         sources = list(sources)
         segs, nsegs = _segments(sources, segments, "AccumStep.plan")
         if bucket_elems and bucket_elems < self.n:
@@ -243,6 +263,7 @@ class AccumStep:
                        for b in range(0, self.n, bucket_elems)]
         else:
             buckets = [(segs, nsegs)]
+        buckets = Z.BucketPlan(buckets)
         if self.fused:
             self._size_partials(buckets)
         return sources, buckets
@@ -263,6 +284,9 @@ class AccumStep:
 
     def accumulate(self, buckets, first: bool) -> None:
         """Widen (first micro-batch) or add one micro-batch into grad32."""
+        if self.any_order:
+            Z.zero_flatten_buckets(buckets, self.grad32, self.n, Z.ZERO_F32, not first)
+            return
         for segs, nsegs in buckets:
             Z.zero_flatten_bucket(segs, nsegs, self.grad32, self.n, Z.ZERO_F32, not first)
 
@@ -271,6 +295,9 @@ class AccumStep:
         the finished fp32 partition (requires fused=True)."""
         if self.partial_count != sum(Z.zero_flatten_norm_partials(s, k) for s, k in buckets):
             self._size_partials(buckets)
+        if self.any_order:
+            Z.zero_flatten_buckets(buckets, self.grad32, self.n, Z.ZERO_F32, not first, self.partials)
+            return
         for (segs, nsegs), off in zip(buckets, self.partial_offsets):
             Z.zero_flatten_norm_bucket_f32(segs, nsegs, self.grad32, self.partials, self.n, not first, off)
 
