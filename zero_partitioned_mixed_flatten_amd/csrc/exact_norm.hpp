@@ -11,7 +11,8 @@
 //     h = x^2 rounded to a multiple of 2^-8   (fma(x, x, C) - C, C = 1.5*2^44)
 //     l = x^2 - h, exactly                     (fma(x, x, -h), |l| <= 2^-9)
 //     sum(h) stays a multiple of 2^-8 below 2^44, sum(l) a multiple of 2^-48
-//     below 2^3.
+//     below 2^3.  An inf or NaN input leaves h or l non-finite, and finite
+//     inputs cannot: that is the overflow test (no look at exponent fields).
 //
 //   binary32 gradients (the accumulation form): on the fast path every value
 //   is a multiple of 2^-24 below 2^24 in magnitude (any binary32 sum of at
@@ -53,16 +54,6 @@ constexpr uint32_t kWide = 2u;      // the fast sum does not hold: the wide pass
 
 constexpr double kSplit16 = 0x1.8p44;          // 1.5 * 2^44: its ulp is 2^-8
 
-// The exponent test adds 0x0400 to each masked exponent field of a word that
-// holds two binary16 values: only an all-ones field carries into bit 15
-// (resp. 31), and the low half never carries into the high half.
-__device__ __forceinline__ uint32_t exp_test(uint32_t w) { return (w & 0x7C007C00u) + 0x04000400u; }
-
-__device__ __forceinline__ uint32_t exp_test(u32x4 v)
-{
-    return exp_test(v.x) | exp_test(v.y) | exp_test(v.z) | exp_test(v.w);
-}
-
 // Signed base-2^32 limbs of an integer count of 2^-48 units:
 // l0 + l1*2^32 + l2*2^64 + l3*2^96.
 struct Limbs {
@@ -71,7 +62,6 @@ struct Limbs {
 
 struct Acc16 {
     double h = 0.0, l = 0.0;
-    uint32_t flag = 0;           // bit 15 or 31 set: an all-ones exponent was seen
 
     __device__ __forceinline__ void square(_Float16 v)
     {
@@ -83,19 +73,21 @@ struct Acc16 {
     // Eight binary16 values in one 16-byte vector.
     __device__ __forceinline__ void vec(u32x4 v)
     {
-        flag |= exp_test(v);
         const f16x8 e = __builtin_bit_cast(f16x8, v);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             square(e[k]);
     }
     // One element given as its bit pattern.
-    __device__ __forceinline__ void bits(uint16_t b)
+    __device__ __forceinline__ void bits(uint16_t b) { square(__builtin_bit_cast(_Float16, b)); }
+    // An inf or NaN among the values leaves a non-finite h or l (x = +-inf:
+    // hh = inf, l gets inf - inf; NaN propagates), and finite values keep
+    // both finite (h < 2^44, |l| < 2^3): the overflow test needs no
+    // separate look at the exponent fields.
+    __device__ __forceinline__ uint32_t status() const
     {
-        flag |= (uint32_t(b) & 0x7C00u) + 0x0400u;
-        square(__builtin_bit_cast(_Float16, b));
+        return (__builtin_isfinite(h) && __builtin_isfinite(l)) ? 0u : kOvf;
     }
-    __device__ __forceinline__ uint32_t status() const { return (flag & 0x80008000u) ? kOvf : 0u; }
     // The thread's sum as limbs; an inf/NaN seen by the thread voids it
     // (the overflow flag makes the sum irrelevant anyway).
     __device__ __forceinline__ Limbs limbs() const
