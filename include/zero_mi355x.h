@@ -260,8 +260,9 @@ int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t nsegs, flo
  * Errors: those of zero_flatten_bucket and zero_flatten_norm_bucket;
  *         ZERO_EINVAL also for NULL bucket_nsegs with nbuckets > 0 and for
  *         two segments whose destination ranges overlap; ZERO_ERANGE for
- *         more than 2^32 - 1 segments in all.  No device work is queued
- *         when an error is returned. */
+ *         more than 2^32 - 1 segments in all; ZERO_ENOMEM if the host
+ *         cannot allocate the overlap check's list.  No device work is
+ *         queued when an argument error is returned. */
 int zero_flatten_buckets(const zero_segment_t* segs, const uint32_t* bucket_nsegs, uint32_t nbuckets, void* dst,
                          uint64_t dst_len, int dst_dtype, int accumulate, void* partials,
                          uint64_t partials_capacity, void* stream);

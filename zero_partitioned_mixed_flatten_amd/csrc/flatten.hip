@@ -465,19 +465,24 @@ extern "C" int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t
 namespace zero {
 namespace {
 
-// ZERO_EINVAL if two nonempty segments write a common destination element.
+// ZERO_EINVAL if two nonempty segments write a common destination element
+// (ZERO_ENOMEM if the host cannot hold the sorted list).
 int check_disjoint(const zero_segment_t* segs, uint64_t nsegs)
 {
-    std::vector<std::pair<uint64_t, uint64_t>> r;
-    r.reserve(nsegs);
-    for (uint64_t i = 0; i < nsegs; ++i)
-        if (segs[i].count)
-            r.emplace_back(segs[i].dst_off, segs[i].count);
-    std::sort(r.begin(), r.end());
-    for (size_t i = 1; i < r.size(); ++i)
-        if (r[i].first - r[i - 1].first < r[i - 1].second)     // sorted: r[i].first >= r[i-1].first
-            return ZERO_EINVAL;
-    return ZERO_OK;
+    try {
+        std::vector<std::pair<uint64_t, uint64_t>> r;
+        r.reserve(nsegs);
+        for (uint64_t i = 0; i < nsegs; ++i)
+            if (segs[i].count)
+                r.emplace_back(segs[i].dst_off, segs[i].count);
+        std::sort(r.begin(), r.end());
+        for (size_t i = 1; i < r.size(); ++i)
+            if (r[i].first - r[i - 1].first < r[i - 1].second)     // sorted: r[i].first >= r[i-1].first
+                return ZERO_EINVAL;
+        return ZERO_OK;
+    } catch (...) {
+        return ZERO_ENOMEM;
+    }
 }
 
 }  // namespace
