@@ -453,6 +453,7 @@ def main():
     if args.copy_only:
         nbytes = (ADAM_BYTES // 2) * n // 16 * 16
         src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        src.view(torch.int32).random_()
         dst = torch.empty_like(src)
         for _ in range(args.warmup + args.steps):
             Z.zero_stream_copy(dst, src, nbytes)
@@ -603,9 +604,11 @@ def main():
     log(f"step {1e3 * el / args.steps:.3f} ms; " + ", ".join(f"{k} {v:.1f} us" for k, v in kernels_us.items())
         + f"; adam {achieved:.0f} GB/s; skipped={st.skipped_total} scale={st.loss_scale:g}")
 
-    # streaming-copy reference on the same byte count as one Adam launch
+    # streaming-copy reference on the same byte count as one Adam launch; it
+    # copies random bits (a copy of zero pages measured 1.3-2% faster)
     nbytes = (ADAM_BYTES // 2) * n // 16 * 16
     csrc = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    csrc.view(torch.int32).random_()
     cdst = torch.empty_like(csrc)
     for _ in range(3):
         Z.zero_stream_copy(cdst, csrc, nbytes)
