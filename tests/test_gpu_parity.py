@@ -291,6 +291,41 @@ def test_standalone_norm_multi_workgroup_fold(dtype):
         H.compare_state(s, ost, None)
 
 
+def test_standalone_norm_beyond_256_workgroups():
+    """Above 2^30 elements the standalone norm's grid grows past one
+    workgroup per CU (no thread sums more than 4096 values): 513 workgroups
+    here, whose partials the last workgroup folds in three batches.  The
+    partition is one value everywhere but at planted positions, so its exact
+    sum is a closed form; the 128-bit sum, its rounding and the decision must
+    match it bit for bit."""
+    from fractions import Fraction
+    n = (1 << 31) + 12345
+    rng = np.random.default_rng(92)
+    pos = np.unique(rng.integers(0, n, 64))
+    bits = rng.integers(0, 0x7C00, pos.size, dtype=np.uint16) | (rng.integers(0, 2, pos.size, dtype=np.uint16) << 15)
+    dev = torch.full((n,), 0.5, dtype=torch.float16, device="cuda")
+    dev[torch.from_numpy(pos).cuda()] = H.to_dev16(bits)
+
+    def units(b):                                   # x^2 in units of 2^-48 from the binary16 fields
+        f, m = (int(b) >> 10) & 31, int(b) & 1023
+        e = f - 25 if f else -24
+        return (m | (1024 if f else 0)) ** 2 << (2 * e + 48)
+    exact = (n - pos.size) * (1 << 46) + sum(units(b) for b in bits)
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    assert Z.zero_norm_workspace_bytes(n) >= 513 * Z.NORM_PARTIAL_BYTES
+    st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st, 65536.0)
+    ost = O.new_state(65536.0)
+    for k in range(2):
+        H.log(f"standalone norm n={n} (513 workgroups) call {k}")
+        Z.zero_shard_norm_overflow(dev, n, Z.hparams(), st, ws)
+        O.decide(ost, O.hparams(), float(Fraction(exact, 1 << 48)), 0)
+        s = Z.read_state(st)
+        assert (int(s.sumsq_units[1]) << 64 | int(s.sumsq_units[0])) == exact and s.overflow == 0
+        assert s.sumsq == float(Fraction(exact, 1 << 48))
+        H.compare_state(s, ost, None)
+
+
 def test_determinism_two_runs():
     w = _small("det", 777_777, seed=12)
     outs = []

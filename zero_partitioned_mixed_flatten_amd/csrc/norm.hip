@@ -83,15 +83,27 @@ __device__ __forceinline__ void publish_and_decide(Limbs s, uint32_t flag, zero_
         s_last = last ? 1u : 0u;
     }
     __syncthreads();
-    if (!s_last)
+    if (!s_last || threadIdx.x >= 64)
         return;
 
-    // Last workgroup: fold every partial (integer limbs: order is irrelevant).
+    // Last workgroup: its first wave folds every partial (integer limbs:
+    // order is irrelevant), four per lane per batch with the loads in
+    // flight together (one batch for up to 256 workgroups, the usual grid),
+    // then a shuffle fold with no barrier.
     Limbs t{0, 0, 0, 0};
     uint32_t tflag = 0;
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock)
-        exact::fold_partial(t, tflag, ws[b]);
-    exact::block_fold<kNormBlock>(t, tflag);
+    for (uint32_t b0 = 0; b0 < gridDim.x; b0 += 256) {
+        NormPartial q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t b = b0 + threadIdx.x + 64 * k;
+            q[k] = b < gridDim.x ? ws[b] : NormPartial{0, 0};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            exact::fold_partial(t, tflag, q[k]);
+    }
+    exact::block_fold<64>(t, tflag);
     if (threadIdx.x == 0) {
         conclude(st, d, t, tflag);
         st->done_blocks = 0;                                 // re-arm for the next call
@@ -160,19 +172,23 @@ __global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const T* __re
     const uint64_t nvec = n / E::kPerVec;
     const u32x4* __restrict__ gv = reinterpret_cast<const u32x4*>(g);
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-    uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
-    for (; j + 3 * stride < nvec; j += 4 * stride) {      // four 16-byte loads in flight
+    // a round: each wave reads one contiguous 4 KiB block (its four load
+    // instructions 1 KiB apart), the grid 4 * stride vectors
+    const uint64_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t j = (uint64_t(blockIdx.x) * (kNormBlock / 64) + wave) * 256 + lane;
+    for (; j + 192 < nvec; j += 4 * stride) {             // four 16-byte loads in flight
         const u32x4 a = __builtin_nontemporal_load(gv + j);
-        const u32x4 b = __builtin_nontemporal_load(gv + j + stride);
-        const u32x4 c = __builtin_nontemporal_load(gv + j + 2 * stride);
-        const u32x4 e = __builtin_nontemporal_load(gv + j + 3 * stride);
+        const u32x4 b = __builtin_nontemporal_load(gv + j + 64);
+        const u32x4 c = __builtin_nontemporal_load(gv + j + 128);
+        const u32x4 e = __builtin_nontemporal_load(gv + j + 192);
         acc_vec(acc, a);
         acc_vec(acc, b);
         acc_vec(acc, c);
         acc_vec(acc, e);
     }
-    for (; j < nvec; j += stride)
-        acc_vec(acc, __builtin_nontemporal_load(gv + j));
+    for (int k = 0; k < 4; ++k, j += 64)                  // the grid's last, partial round
+        if (j < nvec)
+            acc_vec(acc, __builtin_nontemporal_load(gv + j));
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * E::kPerVec)   // the last n % kPerVec elements
         E::one(acc, g, nvec * E::kPerVec + threadIdx.x);
 
