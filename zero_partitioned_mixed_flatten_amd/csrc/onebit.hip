@@ -322,24 +322,29 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
     if (mx) {
         const uint64_t ng = (n >> 3) * 2;                     // groups of 4 in whole payload bytes
         const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-        uint64_t j = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
-        for (; j + 7 * stride < ng; j += 8 * stride) {        // eight groups' loads in flight
+        // a round: each wave reads 512 consecutive groups (its eight loads
+        // 64 groups apart), the grid 8 * stride groups
+        const uint64_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        uint64_t j = (uint64_t(blockIdx.x) * (kNormBlock / 64) + wave) * 512 + lane;
+        for (; j + 448 < ng; j += 8 * stride) {               // eight groups' loads in flight
             float x[8][4];
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                vsrc.vec(j + q * stride, x[q]);
+                vsrc.vec(j + 64 * q, x[q]);
 #pragma unroll
             for (int q = 0; q < 8; ++q)
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     acc.add(x[q][k], w);
         }
-        for (; j < ng; j += stride) {
-            float x[4];
-            vsrc.vec(j, x);
+        for (int q = 0; q < 8; ++q, j += 64) {                // the grid's last, partial round
+            if (j < ng) {
+                float x[4];
+                vsrc.vec(j, x);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                acc.add(x[k], w);
+                for (int k = 0; k < 4; ++k)
+                    acc.add(x[k], w);
+            }
         }
         if (blockIdx.x == 0 && threadIdx.x < (n & 7))
             acc.add(vsrc.at(4 * ng + threadIdx.x), w);   // elements past the last whole byte
@@ -360,13 +365,24 @@ __device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restr
         s_last = last ? 1u : 0u;
     }
     __syncthreads();
-    if (!s_last)
+    if (!s_last || threadIdx.x >= 64)
         return;
+    // the last workgroup's first wave folds the partials, four loads per lane
+    // in flight per batch of 256, then a shuffle fold with no barrier
     exact::Limbs t{0, 0, 0, 0};
     uint32_t tflag = 0;
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += kNormBlock)
-        exact::fold_partial(t, tflag, ws[b]);
-    exact::block_fold<kNormBlock>(t, tflag);
+    for (uint32_t b0 = 0; b0 < gridDim.x; b0 += 256) {
+        NormPartial q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t b = b0 + threadIdx.x + 64 * k;
+            q[k] = b < gridDim.x ? ws[b] : NormPartial{0, 0};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            exact::fold_partial(t, tflag, q[k]);
+    }
+    exact::block_fold<64>(t, tflag);
     if (threadIdx.x == 0) {
         uint64_t hi = 0, lo = 0;
         exact::limbs_to_u128(t, hi, lo);                        // < n * 2^82: always fits
