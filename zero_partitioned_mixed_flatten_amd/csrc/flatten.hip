@@ -288,7 +288,40 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
             put_scalar<MODE, NORM>(dst, doff + t0 + t, src[t0 + t], acc);
     }
 
-    if (NORM) {                                 // every thread reaches this point
+    if constexpr (NORM && MODE < kTo32) {       // every thread reaches this point
+        // A lane has added at most 46 binary16 squares (its vectors, one head
+        // and one tail element each), so the wave's h is a multiple of 2^-8
+        // below 2^44 and its |l| a multiple of 2^-48 below 2^3: both fold
+        // across the wave in binary64 without rounding, and become limbs once
+        // per wave.
+        static_assert(kVecsPerThread * 8 + 14 <= 64, "the binary64 wave fold needs at most 64 squares per lane");
+        exact::Acc16 w = acc;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            w.h += __shfl_xor(w.h, off, 64);
+            w.l += __shfl_xor(w.l, off, 64);
+        }
+        __shared__ exact::Limbs s_w[kBlock / 64];
+        __shared__ uint32_t s_f[kBlock / 64];
+        if ((threadIdx.x & 63) == 0) {
+            s_w[threadIdx.x >> 6] = w.limbs();
+            s_f[threadIdx.x >> 6] = w.status();
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            exact::Limbs s{0, 0, 0, 0};
+            uint32_t flag = 0;
+#pragma unroll
+            for (int k = 0; k < kBlock / 64; ++k) {
+                s.l0 += s_w[k].l0;
+                s.l1 += s_w[k].l1;
+                s.l2 += s_w[k].l2;
+                s.l3 += s_w[k].l3;
+                flag |= s_f[k];
+            }
+            a.partials[blockIdx.x] = exact::make_partial(s, flag);
+        }
+    } else if constexpr (NORM) {
         uint32_t flag = acc.status();
         exact::Limbs s = acc.limbs();
         exact::block_fold<kBlock>(s, flag);
