@@ -197,10 +197,10 @@ def test_flatten_norm_partial_count(Z):
     numels, segs = shardgen.random_segments(rng, 50_000, 9000)
     arr, k = Z.make_segments([(FAKE, so, do, c) for _, so, do, c in segs] + [(FAKE, 0, 0, 0)])
     want = 0
-    for _, _, do, c in segs:                      # one workgroup per 1024 aligned 8-vectors, at least one
+    for _, _, do, c in segs:                      # one workgroup per 768 aligned 8-vectors, at least one
         head = min((8 - do % 8) % 8, c)
         nv = (c - head) // 8
-        want += -(-nv // 1024) if nv else 1
+        want += -(-nv // 768) if nv else 1
     assert Z.zero_flatten_norm_partials(arr, k) == want          # the empty segment needs none
     assert Z.lib().zero_flatten_norm_partials(None, 3) == 0
 

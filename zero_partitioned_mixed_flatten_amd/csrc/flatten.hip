@@ -25,8 +25,10 @@
 // inf/NaN test of every value it stores (exact_norm.hpp) and writes one
 // partial per workgroup, so the norm needs no second pass over the
 // partition: zero_shard_decide folds the partials and takes the decision.
-// It takes four vectors per thread (the workgroup fold is amortised over
-// 8192 elements) and nontemporal stores (nothing reads the partition before
+// It takes three vectors per thread (the fold is amortised over 6144
+// elements, and a 25M-element bucket is 4069 workgroups, two full
+// generations of 2048 resident ones, where four vectors left a half-empty
+// second generation) and nontemporal stores (nothing reads the partition before
 // the Adam pass, and draining dirty cache lines during it costs more).
 #include <hip/hip_ext.h>
 
@@ -43,10 +45,10 @@ namespace {
 constexpr uint32_t kMaxSegs = 64;
 constexpr int kBlock = 256;
 
-// 16-byte vectors per thread: 1 for the plain flatten, 4 for the fused one.
+// 16-byte vectors per thread: 1 for the plain flatten, 3 for the fused one.
 template <bool NORM>
 struct Geometry {
-    static constexpr int kVecsPerThread = NORM ? 4 : 1;
+    static constexpr int kVecsPerThread = NORM ? 3 : 1;
     static constexpr uint64_t kVecsPerBlock = uint64_t(kBlock) * kVecsPerThread;
 };
 
