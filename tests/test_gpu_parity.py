@@ -326,6 +326,47 @@ def test_standalone_norm_beyond_256_workgroups():
         H.compare_state(s, ost, None)
 
 
+def test_fused_flatten_sum_at_the_magnitude_bound():
+    """The fused flatten folds each wave's squares in binary64, which stays
+    exact while a lane adds at most 46 of them: here every value is +-65504
+    (the largest finite binary16, square just below 2^32) over several full
+    workgroups and misaligned segments, so the first workgroup of each
+    segment adds head and tail elements on top of its vectors, plus a few
+    2^-24 subnormals whose 2^-48 squares any rounding at that magnitude would
+    lose.  The 128-bit sum equals the closed form, bit for bit, through the
+    plain and the bucketed call."""
+    rng = np.random.default_rng(93)
+    n = 5 * 6144 + 6 * 8 + 5
+    numels, segs = shardgen.random_segments(rng, n, 4000, True)
+    assert any(do % 8 for _, _, do, _ in segs)                  # some segment heads and tails
+    vals = np.where(rng.integers(0, 2, n) == 1, np.uint16(0x7BFF), np.uint16(0xFBFF))
+    tiny = rng.choice(n, 9, replace=False)
+    vals[tiny] = np.uint16(0x0001)                             # 2^-24: square 2^-48, one unit
+    srcs, k = [], 0
+    for (t, so, do, c), m in zip(segs, numels):
+        buf = rng.integers(0, 0x7C00, m, dtype=np.uint16)      # padding around the segment: not summed
+        buf[so:so + c] = vals[do:do + c]
+        srcs.append(H.to_dev16(buf))
+    arr, kk = Z.make_segments([(srcs[t].data_ptr(), so, do, c) for t, so, do, c in segs])
+    exact = (n - tiny.size) * (65504 ** 2 << 48) + tiny.size
+    for bucket in (0, 7000):
+        plan = [(arr, kk)] if not bucket else [Z.zero_bucket_segments(arr, kk, b, min(n, b + bucket))
+                                               for b in range(0, n, bucket)]
+        plan = Z.BucketPlan(plan)
+        count = plan.partials()
+        dst = torch.zeros(n, dtype=torch.float16, device="cuda")
+        parts = torch.empty(count * Z.NORM_PARTIAL_BYTES, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(16, Z.zero_decide_workspace_bytes(count)), dtype=torch.uint8, device="cuda")
+        st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+        Z.zero_step_state_init(st, 1.0)
+        H.log(f"fused flatten at the magnitude bound: n={n} buckets={len(plan)}")
+        Z.zero_flatten_buckets(plan, dst, n, Z.ZERO_F16, False, parts)
+        Z.zero_shard_decide(parts, count, Z.hparams(), st, ws)
+        s = Z.read_state(st)
+        assert s.overflow == 0 and (int(s.sumsq_units[1]) << 64 | int(s.sumsq_units[0])) == exact
+        assert np.array_equal(H.bits16(dst), vals)
+
+
 def test_determinism_two_runs():
     w = _small("det", 777_777, seed=12)
     outs = []

@@ -291,12 +291,13 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(FlatArgs a, void* __res
     }
 
     if constexpr (NORM && MODE < kTo32) {       // every thread reaches this point
-        // A lane has added at most 46 binary16 squares (its vectors, one head
-        // and one tail element each), so the wave's h is a multiple of 2^-8
-        // below 2^44 and its |l| a multiple of 2^-48 below 2^3: both fold
-        // across the wave in binary64 without rounding, and become limbs once
-        // per wave.
-        static_assert(kVecsPerThread * 8 + 14 <= 64, "the binary64 wave fold needs at most 64 squares per lane");
+        // A lane has added at most 8 * kVecsPerThread + 2 binary16 squares
+        // (its vectors, at most one head and one tail element), each below
+        // 2^32, so the wave's h is a multiple of 2^-8 below 2^44 and its |l| a
+        // multiple of 2^-48 below 2^3 while that count is at most 64: both
+        // fold across the wave in binary64 without rounding, and become limbs
+        // once per wave.
+        static_assert(kVecsPerThread * 8 + 2 <= 64, "the binary64 wave fold needs at most 64 squares per lane");
         exact::Acc16 w = acc;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
