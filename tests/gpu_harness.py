@@ -30,6 +30,7 @@ import torch
 
 import oracle as O
 import shardgen
+from floatcmp import same_floats32
 import zero_partitioned_mixed_flatten_amd as Z
 
 FP32_REL_TOL = 1e-6
@@ -300,8 +301,7 @@ def step_accum(r: AccumRun, check: bool = True, exact: bool = True) -> None:
     if not check:
         return
     compare_state(r.dev.read_state(), r.st, exact_units32(grad) if (exact and not ovf) else None)
-    assert np.array_equal(r.dev.grad32[:w.n].cpu().numpy().view(np.uint32), grad.view(np.uint32)), \
-        "accumulated gradient differs"
+    assert same_floats32(r.dev.grad32[:w.n].cpu().numpy(), grad), "accumulated gradient differs"
     it = torch.from_numpy(i).cuda()
     d16 = bits16(r.dev.p16[it])
     assert np.array_equal(d16, r.p16), f"p16 differs at {int(np.sum(d16 != r.p16))} elements"

@@ -226,3 +226,21 @@ def test_huge_finite_fp32_gradient_is_clipped_not_skipped(oracle):
     assert st.skip == 0 and st.overflow == 0 and st.step == 1 and st.loss_scale == S16
     assert st.sumsq == math.fsum(gd * gd) and st.grad_norm == math.sqrt(st.sumsq) / S16
     assert st.gmul == np.float32(1.0 / st.grad_norm / S16)
+
+
+def test_nan_tolerant_comparison_of_accumulated_gradients():
+    """The GPU harness compares accumulated binary32 gradients bit for bit but
+    lets an element that is NaN on both sides carry any NaN bits (IEEE 754
+    leaves a NaN result's sign and payload unspecified); a NaN on one side
+    only, or any other bit difference, still fails."""
+    from floatcmp import same_floats32 as same
+    a = np.array([1.0, -0.0, np.inf, np.nan], np.float32)
+    b = a.copy()
+    b.view(np.uint32)[3] = 0xFFC00000                       # another NaN: matches
+    assert same(a, b)
+    c = a.copy(); c[1] = 0.0                                 # -0.0 vs +0.0: differs
+    assert not same(a, c)
+    d = a.copy(); d[0] = np.nan                              # NaN on one side only
+    assert not same(a, d)
+    e = a.copy(); e.view(np.uint32)[0] += 1                  # one ulp
+    assert not same(a, e)
