@@ -245,9 +245,11 @@ int zero_flatten_norm_bucket_f32(const zero_segment_t* segs, uint32_t nsegs, flo
  * the previous bucket's (paper card, "Method": the partition is one
  * contiguous buffer; the buckets are windows of it).  The first launch waits
  * for the work queued earlier on the stream, like any launch; the launches
- * after it are issued without the dispatch barrier, so consecutive buckets
- * overlap on the GPU instead of draining it between them.  Work queued on
- * the stream after the call waits for all of them.  That is only safe
+ * between the first and the last are issued without the dispatch barrier,
+ * so consecutive buckets overlap on the GPU instead of draining it between
+ * them; the last keeps the barrier, so its completion implies every
+ * earlier one's and anything queued or waiting on the stream after the call
+ * (kernels, copies, events, synchronisation) sees all of them.  That is only safe
  * because no two buckets touch a common element: every segment's
  * destination range must be disjoint from every other's, and the call
  * checks it.

@@ -397,8 +397,7 @@ int validate(const zero_segment_t* segs, uint32_t nsegs, const void* dst, uint64
 template <bool NORM, typename F>
 int for_each_launch(const zero_segment_t* segs, uint32_t nsegs, F&& fn)
 {
-    FlatArgs a;
-    a.partials = nullptr;
+    FlatArgs a{};
     uint32_t k = 0;
     uint64_t blocks = 0;
     for (uint32_t i = 0; i <= nsegs; ++i) {
@@ -571,21 +570,41 @@ extern "C" int zero_flatten_buckets(const zero_segment_t* segs, const uint32_t* 
         ordered = capturing != 0;
         return int(ZERO_OK);
     };
+    // Each launch is issued once the next one is known, so that the call's
+    // last launch keeps the dispatch barrier too: its completion then implies
+    // that of every launch before it, for whatever waits on the stream's last
+    // packet afterwards (a synchronisation, an event, a copy engine).
+    FlatArgs pend{};
+    uint32_t pend_blocks = 0;
+    bool have = false;
+    auto flush = [&](bool last) {
+        if (!have)
+            return int(ZERO_OK);
+        have = false;
+        const bool ord = ordered || last;
+        return after_launch(norm ? launch<true>(pend, pend_blocks, mode, dst, s, ord)
+                                 : launch<false>(pend, pend_blocks, mode, dst, s, ord));
+    };
+    auto defer = [&](FlatArgs& a, uint32_t blocks) {
+        const int r = flush(false);
+        pend = a;
+        pend_blocks = blocks;
+        have = true;
+        return r;
+    };
     const zero_segment_t* b = segs;
     for (uint32_t k = 0; k < nbuckets; ++k) {
         if (norm)
             rc = for_each_launch<true>(b, bucket_nsegs[k], [&](FlatArgs& a, uint32_t blocks) {
                 a.partials = next;
                 next += blocks;
-                return after_launch(launch<true>(a, blocks, mode, dst, s, ordered));
+                return defer(a, blocks);
             });
         else
-            rc = for_each_launch<false>(b, bucket_nsegs[k], [&](FlatArgs& a, uint32_t blocks) {
-                return after_launch(launch<false>(a, blocks, mode, dst, s, ordered));
-            });
+            rc = for_each_launch<false>(b, bucket_nsegs[k], defer);
         if (rc != ZERO_OK)
             return rc;
         b += bucket_nsegs[k];
     }
-    return ZERO_OK;
+    return flush(true);
 }
