@@ -185,9 +185,11 @@ __device__ __forceinline__ bool limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& l
     return (s.l3 >> 32) == 0;
 }
 
-// Sums limbs and ORs flags over a workgroup of BLOCK threads (every thread
-// must call it); the result is valid in thread 0.  Ends with a barrier, so
-// the LDS it uses may be reused right after.
+// Sums limbs and ORs flags over BLOCK threads (every one of them must call
+// it); the result is valid in thread 0.  BLOCK = 64 is one wave: lane
+// shuffles only, no LDS and no barrier, so the other waves of the workgroup
+// may have exited.  A larger BLOCK is the whole workgroup and ends with a
+// barrier, so the LDS it uses may be reused right after.
 template <int BLOCK>
 __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
 {

@@ -24,14 +24,16 @@
 //                         flight; about 8 VALU operations per fp16 element,
 //                         about 12 binary64 operations per fp32 element;
 //   decide_kernel         folds the per-workgroup partials a fused flatten
-//                         (flatten.hip) already computed while copying; up
-//                         to 2^15 partials in a single workgroup, which then
-//                         decides without an arrival counter or fence, and
-//                         more two per thread over up to 256 workgroups.
-// In both, every workgroup stores its carried partial, bumps an agent-scope
-// acq_rel arrival counter once, and the last one to arrive folds all
-// partials, takes the decision in binary64 on one thread, writes it into the
-// step state and re-arms the counter.  No MFMA: 2 or 4 bytes per element.
+//                         (flatten.hip) already computed while copying
+//                         (decide_grid: a single workgroup, which then
+//                         decides without an arrival counter or fence, up
+//                         to 2^15 partials; more take two per thread over
+//                         up to 256 workgroups).
+// With several workgroups, each stores its carried partial and bumps an
+// agent-scope arrival counter once with release order; the last one to
+// arrive acquires, and its first wave folds all partials, takes the decision
+// in binary64 on one thread, writes it into the step state and re-arms the
+// counter.  No MFMA: 2 or 4 bytes per element.
 #include <math.h>
 
 #include <mutex>
