@@ -142,10 +142,24 @@ def _check(fn: str, rc: int) -> None:
         raise ZeroError(fn, rc, zero_status_string(rc))
 
 
+_raw_stream = None
+
+
 def _stream(stream) -> int:
+    """The HIP stream handle of `stream`, or of torch's current stream on the
+    current device.  The current one is read through torch's raw-handle
+    getter where it exists (the same handle as
+    torch.cuda.current_stream().cuda_stream, without building a Stream object:
+    0.07 against 2.7 us per call, which the launch-bound small shards feel)."""
+    global _raw_stream
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return int(s.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    if _raw_stream is None:
+        get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        dev = getattr(torch._C, "_cuda_getDevice", None)
+        _raw_stream = (lambda: get(dev())) if get and dev else (lambda: torch.cuda.current_stream().cuda_stream)
+    return int(_raw_stream())
 
 
 def _need(fn: str, t, nbytes: int) -> None:
