@@ -126,6 +126,11 @@ class ShardStep:
         for name, t in self.arena.arrays.items():
             setattr(self, name, t)
         self.state = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device=self.device)
+        # The arrays never move: their addresses, taken once (the binding
+        # passes integer addresses through without checking a tensor again,
+        # which is most of a call's host time on a small shard).
+        self._addr = {name: t.data_ptr() for name, t in self.arena.arrays.items()}
+        self._addr["state"] = self.state.data_ptr()
         ws = Z.zero_norm_workspace_bytes(self.n)
         self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=self.device)
         self._buckets = Z.BucketPlan([])
@@ -183,26 +188,27 @@ class ShardStep:
     # ---- the step ---------------------------------------------------------------
     def flatten(self) -> None:
         if self.any_order:
-            Z.zero_flatten_buckets(self.buckets, self.grad16, self.n, Z.ZERO_F16, False)
+            Z.zero_flatten_buckets(self.buckets, self._addr["grad16"], self.n, Z.ZERO_F16, False)
             return
         for segs, nsegs in self.buckets:
-            Z.zero_flatten_bucket(segs, nsegs, self.grad16, self.n, Z.ZERO_F16, False)
+            Z.zero_flatten_bucket(segs, nsegs, self._addr["grad16"], self.n, Z.ZERO_F16, False)
 
     def norm_overflow(self, hp: Z.HParams) -> None:
-        Z.zero_shard_norm_overflow(self.grad16, self.n, hp, self.state, self.workspace)
+        Z.zero_shard_norm_overflow(self._addr["grad16"], self.n, hp, self._addr["state"], self.workspace)
 
     def adam(self) -> None:
-        Z.zero_shard_adam_step(self.p16, self.p32, self.m32, self.v32, self.grad16, self.n, self.state)
+        a = self._addr
+        Z.zero_shard_adam_step(a["p16"], a["p32"], a["m32"], a["v32"], a["grad16"], self.n, a["state"])
 
     def flatten_norm(self) -> None:
         if self.any_order:
-            Z.zero_flatten_buckets(self.buckets, self.grad16, self.n, Z.ZERO_F16, False, self.partials)
+            Z.zero_flatten_buckets(self.buckets, self._addr["grad16"], self.n, Z.ZERO_F16, False, self.partials)
             return
         for (segs, nsegs), off in zip(self.buckets, self.partial_offsets):
-            Z.zero_flatten_norm_bucket(segs, nsegs, self.grad16, self.partials, self.n, False, off)
+            Z.zero_flatten_norm_bucket(segs, nsegs, self._addr["grad16"], self.partials, self.n, False, off)
 
     def decide(self, hp: Z.HParams) -> None:
-        Z.zero_shard_decide(self.partials, self.partial_count, hp, self.state, self.decide_ws)
+        Z.zero_shard_decide(self.partials, self.partial_count, hp, self._addr["state"], self.decide_ws)
 
     def step(self, hp: Z.HParams) -> None:
         if self.fused:
