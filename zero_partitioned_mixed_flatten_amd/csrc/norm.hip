@@ -209,17 +209,17 @@ __global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* _
     uint32_t flag = 0;
     const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
     uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
-    for (; i + 7 * stride < count; i += 8 * stride) {          // eight partials' loads in flight
+    // eight partials' loads in flight per round, the last round guarded (so a
+    // thread's few left-over partials cost one load latency, not one each)
+    for (; i < count; i += 8 * stride) {
         NormPartial q[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            q[k] = in[i + k * stride];
+            q[k] = i + k * stride < count ? in[i + k * stride] : NormPartial{0, 0};
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             exact::fold_partial(s, flag, q[k]);
     }
-    for (; i < count; i += stride)
-        exact::fold_partial(s, flag, in[i]);
     exact::block_fold<kNormBlock>(s, flag);
     publish_and_decide(s, flag, st, ws, d);
 }
