@@ -25,10 +25,11 @@
 //                         about 12 binary64 operations per fp32 element;
 //   decide_kernel         folds the per-workgroup partials a fused flatten
 //                         (flatten.hip) already computed while copying
-//                         (decide_grid: a single workgroup, which then
-//                         decides without an arrival counter or fence, up
-//                         to 2^15 partials; more take two per thread over
-//                         up to 256 workgroups).
+//                         (one wave up to 512 partials; decide_grid: a
+//                         single workgroup, which then decides without an
+//                         arrival counter or fence, up to 2^15 partials;
+//                         more take two per thread over up to 256
+//                         workgroups).
 // With several workgroups, each stores its carried partial and bumps an
 // agent-scope arrival counter once with release order; the last one to
 // arrive acquires, and its first wave folds all partials, takes the decision
@@ -200,15 +201,20 @@ __global__ __launch_bounds__(kNormBlock) void norm_overflow_kernel(const T* __re
     publish_and_decide(s, flag, st, ws, d);
 }
 
-// Folds `count` carried partials (from a fused flatten) and decides.
-__global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* __restrict__ in, uint64_t count,
-                                                            zero_step_state_t* __restrict__ st,
-                                                            NormPartial* __restrict__ ws, DecideArgs d)
+// Folds `count` carried partials (from a fused flatten) and decides.  BLOCK
+// = 64 for a few partials: one wave (eight per lane, loads in flight
+// together) folds them with lane shuffles, no LDS and no barrier.
+constexpr uint64_t kOneWavePartials = 512;
+
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void decide_kernel(const NormPartial* __restrict__ in, uint64_t count,
+                                                       zero_step_state_t* __restrict__ st,
+                                                       NormPartial* __restrict__ ws, DecideArgs d)
 {
     Limbs s{0, 0, 0, 0};
     uint32_t flag = 0;
-    const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-    uint64_t i = uint64_t(blockIdx.x) * kNormBlock + threadIdx.x;
+    const uint64_t stride = uint64_t(gridDim.x) * BLOCK;
+    uint64_t i = uint64_t(blockIdx.x) * BLOCK + threadIdx.x;
     // eight partials' loads in flight per round, the last round guarded (so a
     // thread's few left-over partials cost one load latency, not one each)
     for (; i < count; i += 8 * stride) {
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(kNormBlock) void decide_kernel(const NormPartial* _
         for (int k = 0; k < 8; ++k)
             exact::fold_partial(s, flag, q[k]);
     }
-    exact::block_fold<kNormBlock>(s, flag);
+    exact::block_fold<BLOCK>(s, flag);
     publish_and_decide(s, flag, st, ws, d);
 }
 
@@ -358,9 +364,14 @@ int decide(const void* partials, uint64_t count, const float* grad32, uint64_t n
         return ZERO_ERANGE;
     const uint64_t grid = decide_grid(count);
     const DecideArgs d = decide_args(hp);
-    hipLaunchKernelGGL(decide_kernel, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
-                       static_cast<const NormPartial*>(partials), count, dev_state,
-                       static_cast<NormPartial*>(workspace), d);
+    if (count <= kOneWavePartials)              // one wave, one round of loads, a shuffle fold
+        hipLaunchKernelGGL(decide_kernel<64>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           static_cast<const NormPartial*>(partials), count, dev_state,
+                           static_cast<NormPartial*>(workspace), d);
+    else
+        hipLaunchKernelGGL(decide_kernel<kNormBlock>, dim3(uint32_t(grid)), dim3(kNormBlock), 0, (hipStream_t)stream,
+                           static_cast<const NormPartial*>(partials), count, dev_state,
+                           static_cast<NormPartial*>(workspace), d);
     int rc = launch_status();
     if (rc == ZERO_OK && grad32)
         rc = launch_wide(grad32, n, dev_state, d, workspace, (hipStream_t)stream);
