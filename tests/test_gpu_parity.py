@@ -51,6 +51,23 @@ def test_ragged_sizes_misaligned_segments(n, fused):
     assert r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
+@pytest.mark.parametrize("blocks", [1, 511, 512, 513, 1024])
+def test_decide_around_the_one_wave_fold(blocks):
+    """The decide folds up to 512 partials in one wave and more in a
+    workgroup: one aligned segment of exactly `blocks` fused-flatten
+    workgroups (6144 elements each), stepped against the oracle, with an
+    overflow on the third step (the skip path through the same fold)."""
+    n = blocks * 6144
+    w = _small(f"decide{blocks}", n, seed=blocks)
+    w.layout = shardgen.single_tensor_layout(n)
+    w.inject = {3: shardgen.F16_POS_INF}
+    r = H.start(w, fused=True)
+    for _ in range(4):
+        H.step(r)
+    assert r.dev.partial_count == blocks
+    assert r.st.skipped_total == 1 and r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
 @pytest.mark.parametrize("any_order", [False, True])
 @pytest.mark.parametrize("fused", [False, True])
 def test_many_segments_over_launch_limit(fused, any_order):
