@@ -49,9 +49,10 @@ NORM_BYTES = 2           # read fp16 g
 FLATTEN_BYTES = 4        # read fp16 source, write fp16 partition
 WIDEN_BYTES = 6          # read fp16 source, write fp32 partition
 ACCUM_BYTES = 10         # read fp16 source and fp32 partition, write fp32 partition
-# 1-bit Adam compression stage, per parameter: momentum 14, worker sum 8, worker
-# compression 16 + 1/8, server sum 4 + 1/8, server compression + update 26 + 1/4
-ONEBIT_BYTES = 14 + 8 + 16.125 + 4.125 + 26.25
+# 1-bit Adam compression stage, per parameter: momentum (with the worker window
+# sums) 14, worker compression (with the server window sums) 16 + 1/8, server
+# compression + update 26 + 1/4; the two folds read a few bytes per 2048
+ONEBIT_BYTES = 14 + 16.125 + 26.25
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc")
 
@@ -294,8 +295,8 @@ def run_onebit(args, w, p32, grads_host, dev_sets, hp):
     """1-bit Adam: two untimed warm-up steps of the ordinary fused step, then
     the timed steps of the compression stage (flatten with exact-norm
     partials, decide, zero_onebit_step).  The roofline object is the whole
-    compression stage (five kernels, 68.5 algorithmic bytes per parameter);
-    rocprofv3 gives the split."""
+    compression stage (three streaming kernels and two folds, 56.375
+    algorithmic bytes per parameter); rocprofv3 gives the split."""
     import torch
     import zero_partitioned_mixed_flatten_amd as Z
     n = w.n

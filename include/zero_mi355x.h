@@ -410,12 +410,12 @@ typedef struct {
     float    scale_w, scale_s;  /* worker and server scales of the last step */
     double   sumsq_w, sumsq_s;  /* the exact sums of squares, rounded once to binary64 */
     int32_t  qexp_w, qexp_s;    /* diagnostics of the fast windowed sums: the */
-    uint32_t done_blocks;       /*   window's unit 2^qexp; internal arrival
-                                     counter (0 between calls) */
+    uint32_t done_blocks;       /*   final window's unit 2^qexp; internal
+                                     arrival counter (0 between calls) */
     uint32_t wide_pending;      /* internal: bit 0 / bit 1 while the worker /
                                    server scale waits for its wide pass */
     uint64_t units_w[2];        /* the windowed sums as integers of 2^qexp */
-    uint64_t units_s[2];        /* units (low, high), each square rounded */
+    uint64_t units_s[2];        /* units (low, high), before the wide pass */
 } zero_onebit_state_t;
 
 /* Enqueue the zeroing of a compression-stage state.
@@ -446,10 +446,12 @@ size_t zero_onebit_workspace_bytes(uint64_t n);
  * sgn(x) = +1 for x >= 0 (zeros too), -1 otherwise; bit k of byte j of a
  * bits array is element 8j+k, 1 for +1.  S(x) = fp32(sqrt(sum/n)) with the
  * sum of squares exact and rounded once to binary64.  The fast sum works in
- * a window set by max|x| (each square rounded to a multiple of 2^(2E-80),
- * 2^E <= max|x| < 2^(E+1)); it keeps its result when the binary64 rounding
- * is the same at both ends of the window's error interval, and otherwise
- * hands the sum to a wide pass that is exact for any binary32 values.
+ * windows: each workgroup of 2048 elements rounds its squares to multiples
+ * of 2^(2E_b-80), 2^E_b <= its max|x| < 2^(E_b+1), and a fold moves those
+ * integer sums onto the window of the largest E_b, rounding each to the
+ * nearest unit; it keeps the result when the binary64 rounding is the same
+ * at both ends of the error interval this leaves, and otherwise hands the
+ * sum to a wide pass that is exact for any binary32 values.
  * Every elementwise operation is one binary32 operation in the order
  * above.  Results do not depend on the launch configuration.
  * p16, p32, m32, v32, err_w, err_s, grad16: device, n elements, 16-byte

@@ -6,29 +6,34 @@
 //   u = cw + es;  m = s_s*sgn(u);  es = u - m      (one rank is its own server)
 //   p = p - lr*(m/(sqrt(v)+eps) + wd*p),  p16 = fp16(p)
 // with sgn(x) = +1 for x >= 0, -1 otherwise, and s = ||x||_2/sqrt(d) in fp32
-// from the EXACT sum of squares rounded once to binary64.  The fast sum
-// works in a window: with E the binary exponent of max|x|, each square is
-// rounded to the nearest multiple of 2^(2E-80) (never a tie) and the
-// integers are summed exactly; the exact sum then lies within n/2 units of
-// that integer W, and when W - n/2 and W + n/2 round to the same binary64
-// value that value is the exactly rounded sum.  When they do not, the wide
-// pass (wide_sum.hpp) sums the squares with no window and sets the scale.
+// from the EXACT sum of squares rounded once to binary64.  The fast sum works in
+// windows: the kernel that produces x (or u) sums, per workgroup b, its squares
+// rounded to the nearest multiple of 2^(2E_b-80), E_b the binary exponent of
+// that workgroup's max|x| (never a tie), as an exact integer W_b.  A fold
+// kernel takes E, the largest E_b, and adds every W_b moved onto the window of
+// E and rounded to the nearest unit: W.  Each square is then off by at most
+// half a unit of 2^(2E-80) and each moved W_b by half a unit more, so the
+// exact sum lies within (n + blocks)/2 units of W (the fold's own two levels
+// add half a unit per group), and when the ends of that interval round to
+// the same binary64 value, that value is the exactly rounded sum.  When they
+// do not, the wide pass (wide_sum.hpp) sums the squares with no window and
+// sets the scale.
 // The sign bits (one byte per 8 elements, element 8j+k in bit k of byte j)
 // are what a multi-rank run would exchange.  The device picks the stage:
 // while the applied-step count is at most the warm-up length, these kernels
 // return before any load and the ordinary update runs instead.
 //
 // Five kernels, because two global scales sit on the data path:
-//   A  momentum + per-block max|x|           one-shot, 8 elements per thread
-//   B  exact sum of x^2 in the window, s_w   <= 256 workgroups x 1024, grid-stride
-//      with eight 4-element groups' loads in flight; every workgroup first folds A's
-//      block maxima (L2-resident), the last one to arrive folds the limbs and
-//      writes s_w
-//   C  worker compression: sign byte, ew, u = cw + es, per-block max|u|
-//   D  exact sum of u^2, s_s                  as B (u is recomputed from the bits)
+//   A  momentum; per workgroup max|x| and window sum of x^2     one-shot, 8 elements per thread
+//   B  fold of A's window sums: s_w                             a few workgroups, one round of loads
+//   C  worker compression: sign byte, ew, u = cw + es; per workgroup max|u| and window sum of u^2
+//   D  fold of C's window sums: s_s                             as B
 //   E  server compression + update: m, es, bits, p, p16
 // (a wide pass follows B and D; it returns at once unless the window could
-// not vouch for its sum).  Per-block maxima go to memory (no same-address atomics, which serialise).
+// not vouch for its sum).  Per-block maxima go to memory (no same-address
+// atomics, which serialise).  Summing in A and C, from the values already in
+// registers, saves the two passes that read x and u back (12.125 bytes per
+// element).
 // Element layout of the one-shot kernels: the whole bytes of the sign payload
 // cover groups of 4 elements, g < 2*floor(n/8); thread t of workgroup b owns
 // groups 512b+t and 512b+t+256, so every vector load and store of a wave is
@@ -36,11 +41,12 @@
 // two lanes of an even/odd pair hold the two nibbles of one byte and join
 // them with a lane shuffle.  The elements past the last whole byte (fewer
 // than 8) are done one by one.
-// The exact windowed square: z = x * 2^(40-E) (exact, |z| < 2^41),
+// The exact windowed square: z = x * 2^(40-E_b) (exact, |z| < 2^41),
 //   a = fma(z, z, C1) - C1       z^2 to a multiple of 2^41 (C1 = 1.5*2^93)
 //   b = (fma(z, z, -a) + C2) - C2   the rest, to the nearest integer (C2 = 1.5*2^52)
-// so z^2 rounded to an integer is a + b; with at most 2^11 elements per
-// thread, sum(a) <= 2^93 in steps of 2^41 and |sum(b)| <= 2^51 stay exact.
+// so z^2 rounded to an integer is a + b.  A lane adds at most 15 squares, so
+// a wave's sum(a) < 2^92 in steps of 2^41 and |sum(b)| < 2^50 fold across the
+// wave in binary64 without rounding; each wave's sums then become limbs.
 #include <math.h>
 
 #include "decide.hpp"
@@ -51,12 +57,16 @@ namespace zero {
 namespace {
 
 constexpr int kBlock = 256;                  // one-shot kernels A, C, E
-// The one-shot kernels run at most kOneShotCap workgroups per CU, enforced by
-// a dynamic-LDS reservation they never touch (as the Adam kernel): measured on
-// MI355X, momentum 4.7%, compression 3.2% and the update after it 1.6% faster
-// than at full occupancy.  A and C also hold block_max's few static LDS bytes,
+// The one-shot kernels run at most kOneShotCap (E) or kOneShotCapAC (A, C)
+// workgroups per CU, enforced by a dynamic-LDS reservation they never touch
+// (as the Adam kernel).  Measured on MI355X: E 1.6% faster at 2 than at full
+// occupancy.  A and C were too (4.7% and 3.2%) until they took over the window
+// sums: with the workgroup max and the sum's fold at the end of every
+// workgroup, 4 per CU made the stage 949-952 -> 901-909 us (full occupancy
+// 906-913, 6 per CU 900-903).  A and C also hold a few static LDS bytes,
 // which the reservation leaves room for.
 constexpr int kOneShotCap = 2;
+constexpr int kOneShotCapAC = 4;
 constexpr double kWinHi = 0x1.8p93;          // ulp 2^41
 constexpr double kWinLo = 0x1.8p52;          // ulp 1
 
@@ -121,6 +131,56 @@ struct AccWin {
     }
 };
 
+// Every thread: the max of v over the workgroup (one barrier).
+__device__ __forceinline__ uint32_t block_max_all(uint32_t v)
+{
+    __shared__ uint32_t sm[kBlock / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    if ((threadIdx.x & 63) == 0)
+        sm[threadIdx.x >> 6] = v;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w)
+        v = sm[w] > v ? sm[w] : v;
+    return v;
+}
+
+// The workgroup's window sum as a carried partial, valid in thread 0 (every
+// thread calls it).  A lane holds at most 15 squares, so each wave folds its
+// binary64 sums exactly (header note) before lane 0 turns them into limbs.
+__device__ __forceinline__ NormPartial window_partial(AccWin acc)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        acc.a += __shfl_xor(acc.a, off, 64);
+        acc.b += __shfl_xor(acc.b, off, 64);
+    }
+    __shared__ exact::Limbs s_w[kBlock / 64];
+    if ((threadIdx.x & 63) == 0)
+        s_w[threadIdx.x >> 6] = acc.limbs();
+    __syncthreads();
+    NormPartial p{0, 0};
+    if (threadIdx.x == 0) {
+        exact::Limbs t{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) {
+            t.l0 += s_w[w].l0;
+            t.l1 += s_w[w].l1;
+            t.l2 += s_w[w].l2;
+            t.l3 += s_w[w].l3;
+        }
+        p = exact::make_partial(t, 0);
+    }
+    return p;
+}
+
+// The window of a block maximum given as bits: 2^(40-E).
+__device__ __forceinline__ double window_of(uint32_t mx) { return ldexp(1.0, 40 - exponent_of(mx)); }
+
 // The two groups of 4 elements a thread of a one-shot kernel owns (see the
 // layout note above), out of ng = 2*floor(n/8); ragged0 = 4*ng is the first
 // element done one by one.
@@ -152,14 +212,16 @@ __device__ __forceinline__ uint32_t nibble_of(const uint8_t* bits, uint64_t j)
 
 // ---- A: momentum + block max of |m + ew| ----------------------------------------
 
-__device__ __forceinline__ void momentum4(f16x4 g, f32x4& m, f32x4 e, const Coef& c, uint32_t& mx)
+// m -> beta1*m + (1-beta1)*g*gmul; x = m + ew into x, and the max of |x|.
+__device__ __forceinline__ void momentum4(f16x4 g, f32x4& m, f32x4 e, const Coef& c, f32x4& x, uint32_t& mx)
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
 #pragma clang fp contract(off)
         const float gk = float(g[k]) * c.gmul;
         m[k] = c.b1 * m[k] + c.omb1 * gk;
-        const uint32_t a = abs_bits(m[k] + e[k]);
+        x[k] = m[k] + e[k];
+        const uint32_t a = abs_bits(x[k]);
         mx = a > mx ? a : mx;
     }
 }
@@ -167,7 +229,8 @@ __device__ __forceinline__ void momentum4(f16x4 g, f32x4& m, f32x4 e, const Coef
 __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restrict__ m32, const float* __restrict__ ew,
                                                                  const uint16_t* __restrict__ g16, uint64_t n,
                                                                  const zero_step_state_t* __restrict__ st,
-                                                                 int64_t warmup, uint32_t* __restrict__ blockmax)
+                                                                 int64_t warmup, uint32_t* __restrict__ blockmax,
+                                                                 NormPartial* __restrict__ part)
 {
     if (st->step <= warmup)                      // a warm-up step: the Adam update runs instead
         return;
@@ -179,6 +242,8 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
     const f32x4* __restrict__ EW = reinterpret_cast<const f32x4*>(ew);
     const u32x2* __restrict__ G = reinterpret_cast<const u32x2*>(g16);
     uint32_t mx = 0;
+    f32x4 xa{}, xb{};
+    float xr = 0.0f;
     if (gr.both()) {
         // Every stream here is read once and m is written back in place:
         // nontemporal loads and stores throughout (the gradient alone: 5%
@@ -194,8 +259,8 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
             return;
         }
         const Coef c = coef_of(st);
-        momentum4(__builtin_bit_cast(f16x4, ga), ma, ea, c, mx);
-        momentum4(__builtin_bit_cast(f16x4, gb), mb, eb, c, mx);
+        momentum4(__builtin_bit_cast(f16x4, ga), ma, ea, c, xa, mx);
+        momentum4(__builtin_bit_cast(f16x4, gb), mb, eb, c, xb, mx);
         __builtin_nontemporal_store(ma, M + gr.ja);
         __builtin_nontemporal_store(mb, M + gr.jb);
     } else {
@@ -203,63 +268,46 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
             return;
         if (gr.first()) {
             f32x4 ma = M[gr.ja];
-            momentum4(__builtin_bit_cast(f16x4, G[gr.ja]), ma, EW[gr.ja], coef_of(st), mx);
+            momentum4(__builtin_bit_cast(f16x4, G[gr.ja]), ma, EW[gr.ja], coef_of(st), xa, mx);
             M[gr.ja] = ma;
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const bool ragged = blockIdx.x == 0 && threadIdx.x < (n & 7);
+    if (ragged) {
 #pragma clang fp contract(off)
         const Coef c = coef_of(st);
         const uint64_t i = gr.ragged0 + threadIdx.x;
         const float gk = float(__builtin_bit_cast(_Float16, g16[i])) * c.gmul;
         const float mi = c.b1 * m32[i] + c.omb1 * gk;
         m32[i] = mi;
-        const uint32_t a = abs_bits(mi + ew[i]);
+        xr = mi + ew[i];
+        const uint32_t a = abs_bits(xr);
         mx = a > mx ? a : mx;
     }
-    mx = block_max<kBlock>(mx);
-    if (threadIdx.x == 0)
+    // the workgroup's window (E_b from its max |x|) and its exact window sum
+    mx = block_max_all(mx);
+    AccWin acc;
+    if (mx) {
+        const double w = window_of(mx);
+        if (gr.first())
+            for (int k = 0; k < 4; ++k)
+                acc.add(xa[k], w);
+        if (gr.both())
+            for (int k = 0; k < 4; ++k)
+                acc.add(xb[k], w);
+        if (ragged)
+            acc.add(xr, w);
+    }
+    const NormPartial p = window_partial(acc);
+    if (threadIdx.x == 0) {
         blockmax[blockIdx.x] = mx;
+        part[blockIdx.x] = p;
+    }
 }
 
-// ---- B / D: the exact windowed sum and the scale ------------------------------------
+// ---- B / D: the fold of the window sums, and the scale ------------------------------------
 
-// The vector whose scale is taken: x = m + ew (worker), or u = s_w*sgn + es (server).
-struct WorkerX {
-    const float* m;
-    const float* ew;
-    __device__ __forceinline__ float at(uint64_t i) const { return m[i] + ew[i]; }
-    // group j: elements 4j..4j+3
-    __device__ __forceinline__ void vec(uint64_t j, float (&x)[4]) const
-    {
-        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m) + j);
-        const f32x4 c = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ew) + j);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            x[k] = a[k] + c[k];
-    }
-};
-
-struct ServerU {
-    const uint8_t* bits;
-    const float* es;
-    float sw;
-    __device__ __forceinline__ float at(uint64_t i) const
-    {
-        const float c = ((bits[i >> 3] >> (i & 7)) & 1) ? sw : -sw;
-        return c + es[i];
-    }
-    __device__ __forceinline__ void vec(uint64_t j, float (&x)[4]) const
-    {
-        const uint32_t nib = nibble_of(bits, j);
-        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(es) + j);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            x[k] = (((nib >> k) & 1) ? sw : -sw) + a[k];
-    }
-};
-
-// Which scale a sum kernel writes.
+// Which scale a fold writes.
 enum Which { kWorker = 0, kServer = 1 };
 
 // The scale from the exactly rounded sum of squares S of n values.
@@ -276,168 +324,150 @@ __device__ __forceinline__ void set_scale(zero_onebit_state_t* ob, double S, uin
     }
 }
 
-// The window rounds each of the n squares to a whole number of units (off by
-// at most half a unit each), so the exact sum lies within n/2 units of the
-// window's integer W.  Rounding to binary64 is monotonic: when W - n/2 and
-// W + n/2 round to the same value, every sum between them does, and RNE(W)
-// is the exactly rounded sum.  (W >= 2^80 whenever a value is nonzero, so
-// 2W - n > 0.)  Otherwise the wide pass decides.
-__device__ __forceinline__ bool window_decides(uint64_t hi, uint64_t lo, uint64_t n)
+// W lies within `half`/2 units of the exact sum (header note).  Rounding to
+// binary64 is monotonic: when W - half/2 and W + half/2 round to the same
+// value, every sum between them does, and that is the exactly rounded sum.
+// (W >= 2^79 whenever a value is nonzero, so 2W - half > 0.)  Otherwise the
+// wide pass decides.
+__device__ __forceinline__ bool window_decides(uint64_t hi, uint64_t lo, uint64_t half)
 {
     const unsigned __int128 w2 = ((unsigned __int128)hi << 65) | ((unsigned __int128)lo << 1);   // 2W < 2^124
-    const unsigned __int128 a = w2 - n, b = w2 + n;
+    const unsigned __int128 a = w2 - half, b = w2 + half;
     return u128_to_f64(uint64_t(a >> 64), uint64_t(a)) == u128_to_f64(uint64_t(b >> 64), uint64_t(b));
 }
 
-template <int WHICH, typename V>
-__device__ void sum_and_scale(const V& vsrc, uint64_t n, const uint32_t* __restrict__ blockmax, uint64_t nmax,
-                              const zero_step_state_t* __restrict__ st, zero_onebit_state_t* __restrict__ ob,
-                              NormPartial* __restrict__ ws)
+// A carried partial as a 128-bit integer (its status bits are zero here).
+__device__ __forceinline__ unsigned __int128 partial_value(const NormPartial& p)
 {
-    // the window: max over the previous kernel's block maxima (L2-resident;
-    // eight loads in flight per thread, or the fold is a chain of latencies)
+    return ((unsigned __int128)(p.w1 & ((uint64_t(1) << kPartialStatusShift) - 1)) << 64) | p.w0;
+}
+
+// Adds v * 2^-d rounded to the nearest integer (ties up) to the limbs.
+__device__ __forceinline__ void add_moved(exact::Limbs& s, unsigned __int128 v, int d)
+{
+    if (d >= 127)
+        return;                                               // v < 2^126: below half a unit
+    if (d > 0)
+        v = (v + ((unsigned __int128)1 << (d - 1))) >> d;
+    s.l0 += int64_t(uint64_t(v) & 0xFFFFFFFFull);
+    s.l1 += int64_t(uint64_t(v) >> 32);
+    s.l2 += int64_t(uint64_t(v >> 64) & 0xFFFFFFFFull);
+    s.l3 += int64_t(uint64_t(v >> 96));
+}
+
+// Window sums moved onto the window of the largest of their maxima: every
+// thread takes its entries j = first, first + stride, ... (of count), eight
+// loads in flight per round; returns the workgroup max in every thread and
+// the moved sum (exact limbs of rounded moves) in thread 0.
+__device__ __forceinline__ uint32_t fold_windows(const uint32_t* __restrict__ mxs, const NormPartial* __restrict__ parts,
+                                                 uint64_t count, uint64_t first, uint64_t stride, exact::Limbs& t)
+{
+    // the largest maximum of this workgroup's entries
     uint32_t mx = 0;
-    uint64_t b = threadIdx.x;
-    for (; b + 7 * kNormBlock < nmax; b += 8 * kNormBlock) {
+    for (uint64_t j = first; j < count; j += 8 * stride) {
         uint32_t v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            v[q] = blockmax[b + q * kNormBlock];
+            v[q] = j + q * stride < count ? mxs[j + q * stride] : 0u;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             mx = v[q] > mx ? v[q] : mx;
     }
-    for (; b < nmax; b += kNormBlock)
-        mx = blockmax[b] > mx ? blockmax[b] : mx;
     __shared__ uint32_t s_mx;
     mx = block_max<kNormBlock>(mx);
     if (threadIdx.x == 0)
         s_mx = mx;
     __syncthreads();
     mx = s_mx;
-    const int E = mx ? exponent_of(mx) : 0;
-    const double w = ldexp(1.0, 40 - E);
-
-    AccWin acc;
+    t = exact::Limbs{0, 0, 0, 0};
     if (mx) {
-        const uint64_t ng = (n >> 3) * 2;                     // groups of 4 in whole payload bytes
-        const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
-        // a round: each wave reads 512 consecutive groups (its eight loads
-        // 64 groups apart), the grid 8 * stride groups
-        const uint64_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        uint64_t j = (uint64_t(blockIdx.x) * (kNormBlock / 64) + wave) * 512 + lane;
-        for (; j + 448 < ng; j += 8 * stride) {               // eight groups' loads in flight
-            float x[8][4];
+        const int E = exponent_of(mx);
+        for (uint64_t j = first; j < count; j += 8 * stride) {
+            uint32_t v[8];
+            NormPartial q8[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                vsrc.vec(j + 64 * q, x[q]);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    acc.add(x[q][k], w);
-        }
-        for (int q = 0; q < 8; ++q, j += 64) {                // the grid's last, partial round
-            if (j < ng) {
-                float x[4];
-                vsrc.vec(j, x);
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    acc.add(x[k], w);
+            for (int q = 0; q < 8; ++q) {
+                const bool in = j + q * stride < count;
+                v[q] = in ? mxs[j + q * stride] : 0u;
+                q8[q] = in ? parts[j + q * stride] : NormPartial{0, 0};
             }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (v[q])
+                    add_moved(t, partial_value(q8[q]), 2 * (E - exponent_of(v[q])));
         }
-        if (blockIdx.x == 0 && threadIdx.x < (n & 7))
-            acc.add(vsrc.at(4 * ng + threadIdx.x), w);   // elements past the last whole byte
     }
-    exact::Limbs s = acc.limbs();
     uint32_t flag = 0;
-    exact::block_fold<kNormBlock>(s, flag);
+    exact::block_fold<kNormBlock>(t, flag);
+    return mx;
+}
 
-    __shared__ uint32_t s_last;
-    if (threadIdx.x == 0) {
-        ws[blockIdx.x] = exact::make_partial(s, 0);
-        // release this partial; the last workgroup acquires everyone's
-        const uint32_t prev = __hip_atomic_fetch_add(&ob->done_blocks, 1u, __ATOMIC_RELEASE,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == gridDim.x - 1;
-        if (last)
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_last = last ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!s_last || threadIdx.x >= 64)
+// B (WHICH = kWorker) and D (kServer): the scale from the nb window sums of
+// A or C.  Each workgroup moves its share onto the window of its own largest
+// maximum; with several workgroups the last to arrive moves their sums onto
+// the window of the largest of all (half a unit each).
+template <int WHICH>
+__global__ __launch_bounds__(kNormBlock) void onebit_scale_kernel(const uint32_t* __restrict__ blockmax,
+                                                                  const NormPartial* __restrict__ part, uint64_t nb,
+                                                                  uint64_t n, const zero_step_state_t* __restrict__ st,
+                                                                  int64_t warmup,
+                                                                  zero_onebit_state_t* __restrict__ ob,
+                                                                  uint32_t* __restrict__ gmax,
+                                                                  NormPartial* __restrict__ gpart)
+{
+    if (st->skip || st->step <= warmup)
         return;
-    // the last workgroup's first wave folds the partials, four loads per lane
-    // in flight per batch of 256, then a shuffle fold with no barrier
-    exact::Limbs t{0, 0, 0, 0};
-    uint32_t tflag = 0;
-    for (uint32_t b0 = 0; b0 < gridDim.x; b0 += 256) {
-        NormPartial q[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t b = b0 + threadIdx.x + 64 * k;
-            q[k] = b < gridDim.x ? ws[b] : NormPartial{0, 0};
+    const uint64_t stride = uint64_t(gridDim.x) * kNormBlock;
+    exact::Limbs t;
+    uint32_t mx = fold_windows(blockmax, part, nb, uint64_t(blockIdx.x) * kNormBlock + threadIdx.x, stride, t);
+    uint64_t half = n + nb;                                   // twice the error bound, in units of the window
+    if (gridDim.x > 1) {
+        __shared__ uint32_t s_last;
+        if (threadIdx.x == 0) {
+            gmax[blockIdx.x] = mx;
+            gpart[blockIdx.x] = exact::make_partial(t, 0);
+            // release this workgroup's sum; the last one acquires everyone's
+            const uint32_t prev = __hip_atomic_fetch_add(&ob->done_blocks, 1u, __ATOMIC_RELEASE,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = prev == gridDim.x - 1;
+            if (last)
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_last = last ? 1u : 0u;
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            exact::fold_partial(t, tflag, q[k]);
+        __syncthreads();
+        if (!s_last)
+            return;
+        mx = fold_windows(gmax, gpart, gridDim.x, threadIdx.x, kNormBlock, t);
+        half += gridDim.x;
     }
-    exact::block_fold<64>(t, tflag);
     if (threadIdx.x == 0) {
         uint64_t hi = 0, lo = 0;
-        exact::limbs_to_u128(t, hi, lo);                        // < n * 2^82: always fits
-        const int qexp = 2 * E - 80;
+        exact::limbs_to_u128(t, hi, lo);                        // < (n + nb) * 2^82: always fits
+        const int qexp = mx ? 2 * exponent_of(mx) - 80 : 0;
         if (WHICH == kWorker) {
-            ob->qexp_w = mx ? qexp : 0;
+            ob->qexp_w = qexp;
             ob->units_w[0] = lo;
             ob->units_w[1] = hi;
         } else {
-            ob->qexp_s = mx ? qexp : 0;
+            ob->qexp_s = qexp;
             ob->units_s[0] = lo;
             ob->units_s[1] = hi;
         }
-        if (!mx || window_decides(hi, lo, n)) {
+        if (!mx || window_decides(hi, lo, half)) {
             const double S = mx ? ldexp(u128_to_f64(hi, lo), qexp) : 0.0;
             set_scale<WHICH>(ob, S, n);
         } else {
             ob->wide_pending |= 1u << WHICH;                    // the wide pass sets the scale
         }
-        ob->done_blocks = 0;                                    // re-arm for the next sum
+        ob->done_blocks = 0;                                    // re-arm for the next fold
     }
-}
-
-__global__ __launch_bounds__(kNormBlock) void onebit_sum_worker_kernel(const float* __restrict__ m32,
-                                                                       const float* __restrict__ ew, uint64_t n,
-                                                                       const uint32_t* __restrict__ blockmax,
-                                                                       uint64_t nmax,
-                                                                       const zero_step_state_t* __restrict__ st,
-                                                                       int64_t warmup,
-                                                                       zero_onebit_state_t* __restrict__ ob,
-                                                                       NormPartial* __restrict__ ws)
-{
-    if (st->skip || st->step <= warmup)
-        return;
-    sum_and_scale<kWorker>(WorkerX{m32, ew}, n, blockmax, nmax, st, ob, ws);
-}
-
-__global__ __launch_bounds__(kNormBlock) void onebit_sum_server_kernel(const uint8_t* __restrict__ bits_w,
-                                                                       const float* __restrict__ es, uint64_t n,
-                                                                       const uint32_t* __restrict__ blockmax,
-                                                                       uint64_t nmax,
-                                                                       const zero_step_state_t* __restrict__ st,
-                                                                       int64_t warmup,
-                                                                       zero_onebit_state_t* __restrict__ ob,
-                                                                       NormPartial* __restrict__ ws)
-{
-    if (st->skip || st->step <= warmup)
-        return;
-    sum_and_scale<kServer>(ServerU{bits_w, es, ob->scale_w}, n, blockmax, nmax, st, ob, ws);
 }
 
 // ---- C: worker compression ----------------------------------------------------------
 
-// x = m + ew -> sign nibble, ew = x - s_w*sgn(x), and the max of |s_w*sgn(x) + es|.
-__device__ __forceinline__ uint32_t compress4(f32x4 m, f32x4& e, f32x4 s, float sw, uint32_t& mx)
+// x = m + ew -> sign nibble, ew = x - s_w*sgn(x), u = s_w*sgn(x) + es into u,
+// and the max of |u|.
+__device__ __forceinline__ uint32_t compress4(f32x4 m, f32x4& e, f32x4 s, float sw, f32x4& u, uint32_t& mx)
 {
     uint32_t nib = 0;
 #pragma unroll
@@ -446,7 +476,8 @@ __device__ __forceinline__ uint32_t compress4(f32x4 m, f32x4& e, f32x4 s, float 
         const float cw = sgn_scale(x, sw);
         nib |= (x < 0.0f ? 0u : 1u) << k;
         e[k] = x - cw;
-        const uint32_t a = abs_bits(cw + s[k]);
+        u[k] = cw + s[k];
+        const uint32_t a = abs_bits(u[k]);
         mx = a > mx ? a : mx;
     }
     return nib;
@@ -459,7 +490,8 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
                                                                         const zero_step_state_t* __restrict__ st,
                                                                         int64_t warmup,
                                                                         const zero_onebit_state_t* __restrict__ ob,
-                                                                        uint32_t* __restrict__ blockmax)
+                                                                        uint32_t* __restrict__ blockmax,
+                                                                        NormPartial* __restrict__ part)
 {
     if (st->step <= warmup)
         return;
@@ -471,6 +503,7 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
     f32x4* __restrict__ EW = reinterpret_cast<f32x4*>(ew);
     const f32x4* __restrict__ ES = reinterpret_cast<const f32x4*>(es);
     uint32_t mx = 0, nib_a = 0, nib_b = 0;
+    f32x4 ua{}, ub{};
     if (gr.both()) {
         // nontemporal throughout: e_w is rewritten in place, and a plain load
         // ahead of an in-place nontemporal store is the slow pattern
@@ -484,8 +517,8 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
             return;
         }
         const float sw = ob->scale_w;
-        nib_a = compress4(ma, ea, sa, sw, mx);
-        nib_b = compress4(mb, eb, sb, sw, mx);
+        nib_a = compress4(ma, ea, sa, sw, ua, mx);
+        nib_b = compress4(mb, eb, sb, sw, ub, mx);
         __builtin_nontemporal_store(ea, EW + gr.ja);
         __builtin_nontemporal_store(eb, EW + gr.jb);
     } else {
@@ -493,29 +526,56 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
             return;
         if (gr.first()) {
             f32x4 ea = EW[gr.ja];
-            nib_a = compress4(M[gr.ja], ea, ES[gr.ja], ob->scale_w, mx);
+            nib_a = compress4(M[gr.ja], ea, ES[gr.ja], ob->scale_w, ua, mx);
             EW[gr.ja] = ea;
         }
     }
     store_byte_pair(bits_w, gr.ja, nib_a, gr.first());
     store_byte_pair(bits_w, gr.jb, nib_b, gr.both());
-    if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {     // the ragged last byte
+    // the ragged last byte (fewer than 8 elements, one thread)
+    const bool ragged = blockIdx.x == 0 && threadIdx.x == 0 && (n & 7);
+    float ur[7] = {};
+    if (ragged) {
         const uint64_t nvec = n >> 3;
         const float sw = ob->scale_w;
         uint32_t byte = 0;
-        for (uint64_t i = nvec << 3; i < n; ++i) {
-            const float x = m32[i] + ew[i];
-            const float cw = sgn_scale(x, sw);
-            byte |= (x < 0.0f ? 0u : 1u) << (i & 7);
-            ew[i] = x - cw;
-            const uint32_t a = abs_bits(cw + es[i]);
-            mx = a > mx ? a : mx;
+#pragma unroll
+        for (int k = 0; k < 7; ++k) {                     // fixed indices: ur stays in registers
+            const uint64_t i = (nvec << 3) + k;
+            if (i < n) {
+                const float x = m32[i] + ew[i];
+                const float cw = sgn_scale(x, sw);
+                byte |= (x < 0.0f ? 0u : 1u) << k;
+                ew[i] = x - cw;
+                ur[k] = cw + es[i];
+                const uint32_t a = abs_bits(ur[k]);
+                mx = a > mx ? a : mx;
+            }
         }
         bits_w[nvec] = uint8_t(byte);
     }
-    mx = block_max<kBlock>(mx);
-    if (threadIdx.x == 0)
+    // the workgroup's window (from its max |u|) and its exact window sum
+    mx = block_max_all(mx);
+    AccWin acc;
+    if (mx) {
+        const double w = window_of(mx);
+        if (gr.first())
+            for (int k = 0; k < 4; ++k)
+                acc.add(ua[k], w);
+        if (gr.both())
+            for (int k = 0; k < 4; ++k)
+                acc.add(ub[k], w);
+        if (ragged)
+#pragma unroll
+            for (int k = 0; k < 7; ++k)
+                if (uint64_t(k) < (n & 7))
+                    acc.add(ur[k], w);
+    }
+    const NormPartial p = window_partial(acc);
+    if (threadIdx.x == 0) {
         blockmax[blockIdx.x] = mx;
+        part[blockIdx.x] = p;
+    }
 }
 
 // ---- E: server compression + update ----------------------------------------------------
@@ -679,11 +739,12 @@ __global__ void onebit_state_init_kernel(zero_onebit_state_t* ob)
     *ob = s;
 }
 
-// Workspace: block maxima of A and C, then the partials of B and D.
+// Workspace: the per-workgroup maxima and window sums of A and of C, the
+// fold's per-workgroup maxima and sums, and the wide pass's partials.
 struct Plan {
     uint64_t grid1;                 // one-shot kernels (A, C, E)
-    uint64_t grid2;                 // sums (B, D)
-    uint64_t off_max_a, off_max_c, off_part_b, off_part_d, off_wide, bytes;
+    uint64_t gridf;                 // the folds (B, D)
+    uint64_t off_max_a, off_part_a, off_max_c, off_part_c, off_fmax, off_fpart, off_wide, bytes;
 };
 
 Plan plan(uint64_t n)
@@ -692,17 +753,19 @@ Plan plan(uint64_t n)
     const uint64_t nvec = n >> 3;
     p.grid1 = (nvec + kBlock - 1) / kBlock;
     if (p.grid1 < 1) p.grid1 = 1;
-    // at most 2^11 elements per thread, so the binary64 window sums stay exact
-    p.grid2 = norm_grid(n);
-    const uint64_t per = uint64_t(kNormBlock) * 2048;
-    if ((n + p.grid2 * kNormBlock - 1) / (p.grid2 * kNormBlock) > 2048)
-        p.grid2 = (n + per - 1) / per;
+    // two window sums per thread (one round of loads) where that takes at most
+    // 256 workgroups; eight per thread measured 1 us slower on the gpt2 shard
+    const uint64_t per = uint64_t(kNormBlock) * 2;
+    p.gridf = (p.grid1 + per - 1) / per;
+    if (p.gridf > kNormMaxBlocks) p.gridf = kNormMaxBlocks;
     auto up = [](uint64_t b) { return (b + 255) / 256 * 256; };
     p.off_max_a = 0;
-    p.off_max_c = up(p.grid1 * 4);
-    p.off_part_b = p.off_max_c + up(p.grid1 * 4);
-    p.off_part_d = p.off_part_b + up(p.grid2 * sizeof(NormPartial));
-    p.off_wide = p.off_part_d + up(p.grid2 * sizeof(NormPartial));
+    p.off_part_a = p.off_max_a + up(p.grid1 * 4);
+    p.off_max_c = p.off_part_a + up(p.grid1 * sizeof(NormPartial));
+    p.off_part_c = p.off_max_c + up(p.grid1 * 4);
+    p.off_fmax = p.off_part_c + up(p.grid1 * sizeof(NormPartial));
+    p.off_fpart = p.off_fmax + up(p.gridf * 4);
+    p.off_wide = p.off_fpart + up(p.gridf * sizeof(NormPartial));
     p.bytes = p.off_wide + up(wide::grid(n) * sizeof(wide::WidePartial));
     return p;
 }
@@ -746,25 +809,28 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v3
         return ZERO_ERANGE;
     char* ws = static_cast<char*>(workspace);
     uint32_t* max_a = reinterpret_cast<uint32_t*>(ws + pl.off_max_a);
+    NormPartial* part_a = reinterpret_cast<NormPartial*>(ws + pl.off_part_a);
     uint32_t* max_c = reinterpret_cast<uint32_t*>(ws + pl.off_max_c);
-    NormPartial* part_b = reinterpret_cast<NormPartial*>(ws + pl.off_part_b);
-    NormPartial* part_d = reinterpret_cast<NormPartial*>(ws + pl.off_part_d);
+    NormPartial* part_c = reinterpret_cast<NormPartial*>(ws + pl.off_part_c);
+    uint32_t* fmax = reinterpret_cast<uint32_t*>(ws + pl.off_fmax);
+    NormPartial* fpart = reinterpret_cast<NormPartial*>(ws + pl.off_fpart);
     wide::WidePartial* part_w = reinterpret_cast<wide::WidePartial*>(ws + pl.off_wide);
     const dim3 gw(uint32_t(wide::grid(n)));
     hipStream_t s = (hipStream_t)stream;
-    const dim3 g1(uint32_t(pl.grid1)), g2(uint32_t(pl.grid2));
+    const dim3 g1(uint32_t(pl.grid1)), gf(uint32_t(pl.gridf));
     const uint32_t cap = lds_reservation(kOneShotCap);
-    const uint32_t cap_ac = cap > 256 ? cap - 256 : 0;     // room for block_max's static LDS
+    const uint32_t cap_ac0 = lds_reservation(kOneShotCapAC);
+    const uint32_t cap_ac = cap_ac0 > 512 ? cap_ac0 - 512 : 0;   // room for A's and C's static LDS
     // a warm-up step: the ordinary update (it returns at once in the compression stage)
     int rc = adam_step_gated(p16, p32, m32, v32, grad16, n, dev_state, stream, warmup);
     if (rc != ZERO_OK)
         return rc;
     hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, grad16, n, dev_state,
-                       warmup, max_a);
+                       warmup, max_a, part_a);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_sum_worker_kernel, g2, dim3(kNormBlock), 0, s, m32, err_w, n, max_a, pl.grid1,
-                       dev_state, warmup, dev_onebit, part_b);
+    hipLaunchKernelGGL(onebit_scale_kernel<kWorker>, gf, dim3(kNormBlock), 0, s, max_a, part_a, pl.grid1, n,
+                       dev_state, warmup, dev_onebit, fmax, fpart);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
     hipLaunchKernelGGL((wide::wide_sum_kernel<WorkerValues, ScaleFinish<kWorker>>), gw, dim3(wide::kBlock), 0, s,
@@ -772,11 +838,11 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v3
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
     hipLaunchKernelGGL(onebit_compress_worker_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, err_s, bits_w, n,
-                       dev_state, warmup, dev_onebit, max_c);
+                       dev_state, warmup, dev_onebit, max_c, part_c);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_sum_server_kernel, g2, dim3(kNormBlock), 0, s, bits_w, err_s, n, max_c, pl.grid1,
-                       dev_state, warmup, dev_onebit, part_d);
+    hipLaunchKernelGGL(onebit_scale_kernel<kServer>, gf, dim3(kNormBlock), 0, s, max_c, part_c, pl.grid1, n,
+                       dev_state, warmup, dev_onebit, fmax, fpart);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
     hipLaunchKernelGGL((wide::wide_sum_kernel<ServerValues, ScaleFinish<kServer>>), gw, dim3(wide::kBlock), 0, s,
