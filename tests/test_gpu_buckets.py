@@ -129,3 +129,21 @@ def test_bucketed_steps_against_oracle(any_order):
     for _ in range(4):
         H.step(r)
     assert len(r.dev.buckets) > 1 and r.stats["fp32_not_bitwise"] == 0, r.stats
+
+
+def test_copy_right_after_the_call_sees_every_bucket():
+    """The call's last launch keeps the dispatch barrier, so whatever waits on
+    the stream's last packet -- here a copy to the host queued straight after
+    the call, with no synchronisation in between -- sees every bucket's
+    stores, including those of the unordered launches before it."""
+    n, bucket = 3_000_017, 50_000
+    rng, srcs, buckets = _case(91, n, 30_000, True, bucket)
+    plan = Z.BucketPlan(buckets)
+    assert len(plan) == 61
+    ref = torch.zeros(n, dtype=torch.float16, device="cuda")
+    _per_bucket(plan, ref, n, Z.ZERO_F16, False, None)
+    ref_host = ref.view(torch.int16).cpu()
+    for k in range(3):
+        dst = torch.full((n,), float(k + 1), dtype=torch.float16, device="cuda")
+        Z.zero_flatten_buckets(plan, dst, n, Z.ZERO_F16, False)
+        assert torch.equal(dst.view(torch.int16).cpu(), ref_host), k
