@@ -509,11 +509,20 @@ void oracle_step(const oracle_hparams_t* hp, oracle_state_t* st,
 /* ------------------------------------------------------------------ */
 float oracle_onebit_scale(const float* x, uint64_t n, double* sumsq_out)
 {
+    /* A non-finite element (possible only when the stage's own binary32
+     * arithmetic overflows) makes the sum of squares what IEEE arithmetic
+     * over the squares gives: NaN if some element is NaN, else +inf. */
+    int inf = 0, nan = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        nan |= isnan(x[i]);
+        inf |= isinf(x[i]);
+    }
     wide_t w;
     memset(&w, 0, sizeof w);
-    for (uint64_t i = 0; i < n; ++i)
-        wide_add_square(&w, x[i]);
-    double S = wide_to_double(&w);
+    if (!inf && !nan)
+        for (uint64_t i = 0; i < n; ++i)
+            wide_add_square(&w, x[i]);
+    double S = nan ? (double)NAN : inf ? INFINITY : wide_to_double(&w);
     if (sumsq_out)
         *sumsq_out = S;
     return n ? (float)sqrt(S / (double)n) : 0.0f;

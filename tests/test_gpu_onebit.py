@@ -202,3 +202,51 @@ def test_onebit_window_extremes(case):
     for t, ref in ((dev.p32, refs[1]), (dev.m32, refs[2]), (dev.err_w, refs[4]), (dev.err_s, refs[5])):
         assert np.array_equal(_f32(t), ref.view(np.uint32))
     assert np.array_equal(H.bits16(dev.p16), refs[0])
+
+
+@pytest.mark.parametrize("case", ["inf", "nan"])
+def test_onebit_non_finite_vector(case):
+    """A worker vector holding an inf (or also a NaN), as binary32 overflow
+    in the stage's own adds would leave it: both scales are what IEEE
+    arithmetic over the squares gives (+inf, or NaN), and everything after
+    follows the same binary32 operations as the oracle's.  NaN results may
+    differ in their bits (sign and payload are unspecified), so arrays are
+    compared with NaN matching NaN."""
+    from floatcmp import same_floats32
+    n = 10_007
+    rng = np.random.default_rng(77)
+    m = np.zeros(n, np.float32)
+    ew = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    ew[1234] = np.inf
+    if case == "nan":
+        ew[9000] = np.nan
+    es = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    p32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    v32 = (np.abs(rng.standard_normal(n)) * 1e-6).astype(np.float32)
+    g16 = np.zeros(n, np.uint16)
+    dev = Z.OneBitStep(n, warmup=0)
+    for t, a in ((dev.p32, p32), (dev.m32, m), (dev.v32, v32), (dev.err_w, ew), (dev.err_s, es)):
+        t.copy_(torch.from_numpy(a))
+    dev.p16.copy_(torch.from_numpy(shardgen.to_f16_bits(p32).view(np.float16)))
+    dev.grad16.copy_(torch.from_numpy(g16.view(np.float16)))
+    dev.init_state(1.0)
+    Z.zero_shard_norm_overflow(dev.grad16, n, Z.hparams(max_grad_norm=0.0), dev.state, dev.workspace)
+    H.log(f"onebit non-finite vector: {case}")
+    dev.update()
+    st = O.new_state(1.0)
+    O.decide(st, O.hparams(max_grad_norm=0.0), *O.norm_overflow(g16))
+    refs = [shardgen.to_f16_bits(p32), p32.copy(), m.copy(), v32.copy(), ew.copy(), es.copy()]
+    bw, bs, (sw, ss) = O.onebit_step(st, *refs, g16)
+    torch.cuda.synchronize()
+    ob = dev.read_onebit()
+    want = np.array([sw, ss], np.float32)
+    assert same_floats32(np.array([ob.scale_w, ob.scale_s], np.float32), want), (ob.scale_w, ob.scale_s, sw, ss)
+    assert (np.isnan(sw) if case == "nan" else sw == np.inf) and ob.wide_pending == 0
+    assert np.array_equal(dev.bits_w.cpu().numpy(), bw) and np.array_equal(dev.bits_s.cpu().numpy(), bs)
+    for t, ref in ((dev.p32, refs[1]), (dev.m32, refs[2]), (dev.err_w, refs[4]), (dev.err_s, refs[5])):
+        assert same_floats32(t.cpu().numpy(), ref)
+    got16, want16 = H.bits16(dev.p16), refs[0]
+    nan16 = lambda b: ((b & 0x7C00) == 0x7C00) & ((b & 0x3FF) != 0)
+    assert np.array_equal(nan16(got16), nan16(want16))
+    assert np.array_equal(got16[~nan16(got16)], want16[~nan16(want16)])
+

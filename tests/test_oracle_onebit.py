@@ -63,6 +63,22 @@ def test_scale_closed_forms(oracle):
     assert oracle.onebit_scale(np.zeros(0, np.float32)) == (0.0, 0.0)
 
 
+@pytest.mark.parametrize("special", [[np.inf], [-np.inf], [np.nan], [np.inf, np.nan], [-np.inf, 3e38]])
+def test_scale_of_non_finite_vectors(oracle, special):
+    """A vector holding an inf or a NaN (only binary32 overflow in the stage's
+    own adds can put one there): the sum of squares is what IEEE arithmetic
+    over the squares gives -- math.fsum of the Python squares: +inf, or NaN
+    with any NaN -- and the scale fp32(sqrt(S/d)) follows."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(1000) * 1e3).astype(np.float32)
+    x[rng.choice(1000, len(special), replace=False)] = np.array(special, np.float32)
+    s, S = oracle.onebit_scale(x)
+    ref = math.fsum(float(v) * float(v) for v in x)
+    assert (math.isnan(S) and math.isnan(ref)) or S == ref == math.inf
+    want = np.float32(math.sqrt(ref / x.size))
+    assert (np.isnan(s) and np.isnan(want)) or s == want == np.inf
+
+
 @pytest.mark.parametrize("seed", range(3))
 def test_scale_preserves_the_norm(oracle, seed):
     rng = np.random.default_rng(10 + seed)

@@ -124,6 +124,10 @@ struct AccWin {
     }
     __device__ __forceinline__ exact::Limbs limbs() const
     {
+        // an inf or NaN input leaves a or b non-finite; the fold then sets the
+        // scale from the maxima alone, so the sum is not needed
+        if (!__builtin_isfinite(a) || !__builtin_isfinite(b))
+            return exact::Limbs{0, 0, 0, 0};
         const int64_t au = int64_t(a * 0x1p-41);              // < 2^53
         const int64_t bu = int64_t(b);                         // |.| <= 2^52
         const int64_t hs = au << 9;                            // au * 2^41 = hs * 2^32
@@ -453,7 +457,12 @@ __global__ __launch_bounds__(kNormBlock) void onebit_scale_kernel(const uint32_t
             ob->units_s[0] = lo;
             ob->units_s[1] = hi;
         }
-        if (!mx || window_decides(hi, lo, half)) {
+        if (mx >= 0x7F800000u) {
+            // an inf or NaN (binary32 overflow in the stage's own adds): the sum
+            // of squares IEEE arithmetic gives, NaN if any NaN (its bits are the
+            // larger), else +inf
+            set_scale<WHICH>(ob, mx > 0x7F800000u ? double(NAN) : double(INFINITY), n);
+        } else if (!mx || window_decides(hi, lo, half)) {
             const double S = mx ? ldexp(u128_to_f64(hi, lo), qexp) : 0.0;
             set_scale<WHICH>(ob, S, n);
         } else {
