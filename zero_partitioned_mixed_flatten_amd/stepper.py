@@ -111,7 +111,10 @@ class ShardStep:
     it copies and a decide-only pass folds them (no second read of the
     partition).  Both take bit-identical decisions.  any_order=True flattens
     all buckets of a step in one zero_flatten_buckets call (consecutive
-    buckets overlap on the GPU); False issues one ordered call per bucket."""
+    buckets overlap on the GPU); False issues one ordered call per bucket.
+    The arrays (p32, m32, v32, grad16, p16 and state) are fixed for the
+    object's life: write into them in place; the calls use the addresses
+    taken when it was made."""
 
     def __init__(self, n: int, device="cuda", fused: bool = False, extra=(), any_order: bool = True):
         """extra: further (name, numel, dtype) arrays placed in the same arena
