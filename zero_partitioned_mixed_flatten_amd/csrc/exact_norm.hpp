@@ -7,9 +7,11 @@
 // binary64 accumulators that cannot round under a per-thread bound of
 // kNormMaxPerThread = 2^12 elements:
 //
-//   binary16 gradients: every square is a multiple of 2^-48 below 2^32.
-//     h = x^2 rounded to a multiple of 2^-8   (fma(x, x, C) - C, C = 1.5*2^44)
-//     l = x^2 - h, exactly                     (fma(x, x, -h), |l| <= 2^-9)
+//   binary16 gradients: every square is a multiple of 2^-48 below 2^32, and
+//   exact in binary32 (22 significant bits), where one mixed-precision fma
+//   forms it from the binary16 value.
+//     h = x^2 rounded to a multiple of 2^-8   ((x^2 + C) - C, C = 1.5*2^44)
+//     l = x^2 - h, exactly                     (|l| <= 2^-9)
 //     sum(h) stays a multiple of 2^-8 below 2^44, sum(l) a multiple of 2^-48
 //     below 2^3.  An inf or NaN input leaves h or l non-finite, and finite
 //     inputs cannot: that is the overflow test (no look at exponent fields).
@@ -65,10 +67,14 @@ struct Acc16 {
 
     __device__ __forceinline__ void square(_Float16 v)
     {
-        const double x = double(float(v));                         // exact
-        const double hh = __builtin_fma(x, x, kSplit16) - kSplit16;  // x^2 to a multiple of 2^-8
+        // x^2 exact in binary32; written as an fma with a zero addend so that
+        // gfx950 forms it from the binary16 operand in one v_fma_mix_f32
+        // (a plain product keeps a separate binary16 -> binary32 conversion)
+        const float xf = float(v);
+        const double s = double(__builtin_fmaf(xf, xf, 0.0f));
+        const double hh = (s + kSplit16) - kSplit16;               // x^2 to a multiple of 2^-8
         h += hh;
-        l += __builtin_fma(x, x, -hh);                             // x^2 - hh, exact
+        l += s - hh;                                               // x^2 - hh, exact
     }
     // Eight binary16 values in one 16-byte vector.
     __device__ __forceinline__ void vec(u32x4 v)
