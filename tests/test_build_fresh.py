@@ -12,10 +12,20 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _ignore(_dir, names):
-    return [n for n in names
-            if n.endswith((".so", ".tmp", ".pyc")) or n in ("__pycache__", ".git", "gpurun_out", "_work",
-                                                             "profiles", "tests")]
+def _ignored_dirs():
+    """The directories .gitignore lists (caches, build outputs, working
+    folders), plus the repository metadata and the parts build() does not read."""
+    out = {".git", "profiles", "tests"}
+    with open(os.path.join(ROOT, ".gitignore")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and line.endswith("/"):
+                out.add(line.strip("/"))
+    return out
+
+
+def _ignore(_dir, names, _dirs=_ignored_dirs()):
+    return [n for n in names if n.endswith((".so", ".tmp", ".pyc")) or n in _dirs]
 
 
 def test_build_from_a_tree_without_libraries(tmp_path):
