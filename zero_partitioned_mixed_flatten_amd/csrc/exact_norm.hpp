@@ -161,7 +161,7 @@ struct Acc32 {
 
 // Carries l0, l1, l2 into [0, 2^32); the value is unchanged and >= 0, so l3
 // ends up >= 0.
-__device__ __forceinline__ Limbs carry(Limbs s)
+__host__ __device__ __forceinline__ Limbs carry(Limbs s)
 {
     s.l1 += s.l0 >> 32;
     s.l0 &= 0xFFFFFFFFll;
@@ -173,7 +173,7 @@ __device__ __forceinline__ Limbs carry(Limbs s)
 }
 
 // Adds a stored partial as four 32-bit limbs and ORs in its status bits.
-__device__ __forceinline__ void fold_partial(Limbs& s, uint32_t& flag, const NormPartial& p)
+__host__ __device__ __forceinline__ void fold_partial(Limbs& s, uint32_t& flag, const NormPartial& p)
 {
     s.l0 += int64_t(p.w0 & 0xFFFFFFFFull);
     s.l1 += int64_t(p.w0 >> 32);
@@ -183,7 +183,7 @@ __device__ __forceinline__ void fold_partial(Limbs& s, uint32_t& flag, const Nor
 }
 
 // The total as an unsigned 128-bit value; false if it is 2^128 or more.
-__device__ __forceinline__ bool limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& lo)
+__host__ __device__ __forceinline__ bool limbs_to_u128(Limbs s, uint64_t& hi, uint64_t& lo)
 {
     s = carry(s);
     lo = uint64_t(s.l0) | (uint64_t(s.l1) << 32);
@@ -235,7 +235,7 @@ __device__ __forceinline__ void block_fold(Limbs& s, uint32_t& flag)
 // A workgroup's partial: the carried sum and the status bits (kOvf, kWide
 // fit the two bits); a sum of 2^126 units or more asks for the wide pass,
 // and then its value is not used.
-__device__ __forceinline__ NormPartial make_partial(Limbs s, uint32_t status)
+__host__ __device__ __forceinline__ NormPartial make_partial(Limbs s, uint32_t status)
 {
     static_assert((kOvf | kWide) < 4u, "status bits");
     s = carry(s);

@@ -52,6 +52,7 @@
 #include "decide.hpp"
 #include "exact_norm.hpp"
 #include "wide_sum.hpp"
+#include "window_fold.hpp"
 
 namespace zero {
 namespace {
@@ -328,37 +329,6 @@ __device__ __forceinline__ void set_scale(zero_onebit_state_t* ob, double S, uin
     }
 }
 
-// W lies within `half`/2 units of the exact sum (header note).  Rounding to
-// binary64 is monotonic: when W - half/2 and W + half/2 round to the same
-// value, every sum between them does, and that is the exactly rounded sum.
-// (W >= 2^79 whenever a value is nonzero, so 2W - half > 0.)  Otherwise the
-// wide pass decides.
-__device__ __forceinline__ bool window_decides(uint64_t hi, uint64_t lo, uint64_t half)
-{
-    const unsigned __int128 w2 = ((unsigned __int128)hi << 65) | ((unsigned __int128)lo << 1);   // 2W < 2^124
-    const unsigned __int128 a = w2 - half, b = w2 + half;
-    return u128_to_f64(uint64_t(a >> 64), uint64_t(a)) == u128_to_f64(uint64_t(b >> 64), uint64_t(b));
-}
-
-// A carried partial as a 128-bit integer (its status bits are zero here).
-__device__ __forceinline__ unsigned __int128 partial_value(const NormPartial& p)
-{
-    return ((unsigned __int128)(p.w1 & ((uint64_t(1) << kPartialStatusShift) - 1)) << 64) | p.w0;
-}
-
-// Adds v * 2^-d rounded to the nearest integer (ties up) to the limbs.
-__device__ __forceinline__ void add_moved(exact::Limbs& s, unsigned __int128 v, int d)
-{
-    if (d >= 127)
-        return;                                               // v < 2^126: below half a unit
-    if (d > 0)
-        v = (v + ((unsigned __int128)1 << (d - 1))) >> d;
-    s.l0 += int64_t(uint64_t(v) & 0xFFFFFFFFull);
-    s.l1 += int64_t(uint64_t(v) >> 32);
-    s.l2 += int64_t(uint64_t(v >> 64) & 0xFFFFFFFFull);
-    s.l3 += int64_t(uint64_t(v >> 96));
-}
-
 // Window sums moved onto the window of the largest of their maxima: every
 // thread takes its entries j = first, first + stride, ... (of count), eight
 // loads in flight per round; returns the workgroup max in every thread and
@@ -398,7 +368,7 @@ __device__ __forceinline__ uint32_t fold_windows(const uint32_t* __restrict__ mx
 #pragma unroll
             for (int q = 0; q < 8; ++q)
                 if (v[q])
-                    add_moved(t, partial_value(q8[q]), 2 * (E - exponent_of(v[q])));
+                    window::add_moved(t, window::partial_value(q8[q]), 2 * (E - exponent_of(v[q])));
         }
     }
     uint32_t flag = 0;
@@ -462,7 +432,7 @@ __global__ __launch_bounds__(kNormBlock) void onebit_scale_kernel(const uint32_t
             // of squares IEEE arithmetic gives, NaN if any NaN (its bits are the
             // larger), else +inf
             set_scale<WHICH>(ob, mx > 0x7F800000u ? double(NAN) : double(INFINITY), n);
-        } else if (!mx || window_decides(hi, lo, half)) {
+        } else if (!mx || window::decides(hi, lo, half)) {
             const double S = mx ? ldexp(u128_to_f64(hi, lo), qexp) : 0.0;
             set_scale<WHICH>(ob, S, n);
         } else {
