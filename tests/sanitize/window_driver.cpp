@@ -9,6 +9,12 @@
 //                               prints "hi lo fits decides roundtrip" for the
 //                               folded sum
 //   window_driver decides FILE  lines "hi lo half": prints decides per line
+//   window_driver limbs FILE    lines "hi lo status repeat": each value (below
+//                               2^126) becomes a carried partial with those
+//                               status bits (make_partial, as a workgroup
+//                               stores it) and is folded `repeat` times
+//                               (fold_partial, as the decide kernels fold);
+//                               prints "hi lo fits flag" for the total
 #include <stdio.h>
 #include <string.h>
 
@@ -50,6 +56,18 @@ int main(int argc, char** argv)
         const bool fits = exact::limbs_to_u128(t, h, l);
         printf("%llu %llu %d %d %d\n", (unsigned long long)h, (unsigned long long)l, fits ? 1 : 0,
                window::decides(h, l, half) ? 1 : 0, roundtrip);
+    } else if (!strcmp(argv[1], "limbs")) {
+        exact::Limbs t{0, 0, 0, 0};
+        uint32_t flag = 0;
+        unsigned status, repeat;
+        while (fscanf(f, "%llu %llu %u %u", &hi, &lo, &status, &repeat) == 4) {
+            const NormPartial p = exact::make_partial(limbs_of(hi, lo), status);
+            for (unsigned r = 0; r < repeat; ++r)
+                exact::fold_partial(t, flag, p);
+        }
+        uint64_t h = 0, l = 0;
+        const bool fits = exact::limbs_to_u128(t, h, l);
+        printf("%llu %llu %d %u\n", (unsigned long long)h, (unsigned long long)l, fits ? 1 : 0, flag);
     } else if (!strcmp(argv[1], "decides")) {
         while (fscanf(f, "%llu %llu %llu", &hi, &lo, &half) == 3)
             printf("%d\n", window::decides(hi, lo, half) ? 1 : 0);
