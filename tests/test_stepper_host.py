@@ -65,3 +65,23 @@ def test_intact_sees_a_store_just_outside_an_array(where):
            "after_last": last.data_ptr() + last.numel()}[where] - arena.tensor.data_ptr()
     arena.tensor[off] = 0
     assert not arena.intact()
+
+
+def test_step_arrays_cannot_be_rebound():
+    """The step's calls pass the addresses taken when it was made, so its
+    arrays (and those of the 1-bit form) are written in place; rebinding one
+    is an error instead of being silently ignored.  Host only: nothing is
+    launched."""
+    import zero_partitioned_mixed_flatten_amd as Z
+    for step in (Z.ShardStep(1000, device="cpu"), Z.OneBitStep(1000, warmup=2, device="cpu")):
+        names = ["p32", "m32", "v32", "grad16", "p16", "state"]
+        if isinstance(step, Z.OneBitStep):
+            names += ["err_w", "err_s", "bits_w", "bits_s"]
+        for name in names:
+            old = getattr(step, name)
+            with pytest.raises(AttributeError, match="in place"):
+                setattr(step, name, torch.zeros_like(old))
+            assert getattr(step, name) is old
+        step.p32.fill_(1.5)                       # in place is the way
+        assert float(step.arena.arrays["p32"][0]) == 1.5
+        step.fused = True                         # ordinary attributes stay assignable

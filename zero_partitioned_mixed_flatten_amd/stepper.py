@@ -145,6 +145,14 @@ class ShardStep:
         self.partial_count = 0
         self.decide_ws = None
 
+    def __setattr__(self, name, value):
+        # An array whose address the calls hold cannot be rebound: the calls
+        # would go on using the old one.
+        if name in self.__dict__.get("_addr", ()):
+            raise AttributeError(f"{type(self).__name__}.{name} is fixed for the object's life (the calls use "
+                                 f"its address); write into it in place")
+        object.__setattr__(self, name, value)
+
     # ---- set-up ----------------------------------------------------------------
     @property
     def buckets(self) -> "Z.BucketPlan":
