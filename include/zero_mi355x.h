@@ -49,7 +49,12 @@
  *   - pointers named dev_* or documented as device memory are HIP device
  *     pointers; everything else is host memory;
  *   - the caller owns and allocates every buffer; the library allocates
- *     nothing and keeps no pointer after a call returns;
+ *     nothing and keeps no pointer to a caller's buffer after a call
+ *     returns.  Two exceptions, both owned by the library: a host context
+ *     (zero_host_create: its worker threads and, after zero_offload_step,
+ *     HIP events), and the fixed device array of
+ *     zero_shard_norm_overflow_noalloc (4 KiB per GPU, held until the
+ *     process ends);
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
  *     device work is enqueued there and the call returns without waiting;
  *   - return value: ZERO_OK (0) or a negative ZERO_E* code; argument errors
