@@ -448,3 +448,124 @@ def test_fused_flatten_accumulate_norm():
     sumsq, ovf = O.norm_overflow(ref)
     assert s.overflow == ovf == 0 and np.float64(s.sumsq).tobytes() == np.float64(sumsq).tobytes()
     assert s.as_dict()["sumsq_units"] == H.exact_units(ref)
+
+
+
+def _units16(b: int) -> int:
+    """The square of a finite binary16 value, from its fields, in units of 2^-48."""
+    f, m = (b >> 10) & 31, b & 1023
+    e = f - 25 if f else -24
+    return (m | (1024 if f else 0)) ** 2 << (2 * e + 48)
+
+
+def _where_not(t: torch.Tensor, value: int) -> np.ndarray:
+    """Indices of the elements of a 1-D integer tensor that differ from value,
+    in chunks of 2^30 (torch's nonzero is limited to 2^31 - 1 elements)."""
+    out = [np.zeros(0, np.int64)]
+    for lo in range(0, t.numel(), 1 << 30):
+        out.append((torch.nonzero(t[lo:lo + (1 << 30)] != value).flatten() + lo).cpu().numpy())
+    return np.concatenate(out)
+
+
+def test_fused_step_beyond_2_32_elements():
+    """Index arithmetic past 2^32: a 4,294,970,407-element partition (17.2 GB
+    per fp32 array, 69 GB of state in the arena) from three per-layer
+    tensors -- the second starting at an odd destination offset, so its body
+    is gathered, the third read from source offset 5 -- flattened in 17
+    any-order buckets with exact-norm partials, decided from about 700,000
+    partials over 256 workgroups with clipping active, and updated; two
+    steps.  The gradient is 0.5 and the master parameter 0.0123 everywhere
+    but at planted positions (segment and bucket edges, around 2^32, the
+    ragged tail, and random ones), so the exact sum is a closed form.
+    Checked: the state bit for bit; the flattened partition differs from 0.5
+    exactly at the planted positions, with their values; p32/m32/v32/p16 at
+    the planted positions and at 2,000 random others equal the oracle's
+    update; every element of p32, m32 and v32 outside the planted set equals
+    the oracle's update of the common element (so all n were updated);
+    p16 = fp16(p32) everywhere; the arena's guards are intact.  Then the
+    standalone norm over the same partition (1,025 workgroups) gives the
+    same 128-bit sum and decision."""
+    from fractions import Fraction
+    n = (1 << 32) + 4 * 777 + 3
+    a, b = 1_431_656_771, 1_431_655_765               # a odd: the second segment starts misaligned
+    c = n - a - b
+    segs = [(0, 0, 0, a), (1, 0, a, b), (2, 5, a + b, c)]
+    bucket = 1 << 28
+    c16, p_common, S = 0x3800, np.float32(0.0123), 65536.0
+
+    rng = np.random.default_rng(94)
+    edges = [0, 1, 7, 8, a - 1, a, a + 1, a + b - 1, a + b, a + b + 1, (1 << 32) - 1, 1 << 32, (1 << 32) + 1]
+    edges += [k * bucket + d for k in range(1, n // bucket + 1) for d in (-1, 0, 1)]
+    edges += list(range(n - 9, n))
+    planted = np.unique(np.concatenate([np.array(edges, np.int64), rng.integers(0, n, 300)]))
+    g_pl = (rng.integers(0, 0x7C00, planted.size, dtype=np.uint16)
+            | (rng.integers(0, 2, planted.size, dtype=np.uint16) << 15))
+    g_pl[g_pl == c16] ^= 1                               # every planted value differs from the common one
+    p_pl = rng.normal(0.0, 0.05, planted.size).astype(np.float32)
+    others = np.setdiff1d(rng.integers(0, n, 2000), planted)
+    sample = np.concatenate([planted, others])           # the elements the oracle updates
+
+    torch.cuda.empty_cache()
+    srcs = [torch.full((a,), 0.5, dtype=torch.float16, device="cuda"),
+            torch.full((b,), 0.5, dtype=torch.float16, device="cuda"),
+            torch.full((c + 5,), 0.5, dtype=torch.float16, device="cuda")]
+    for t, so, do, cnt in segs:                          # planted through the sources
+        sel = (planted >= do) & (planted < do + cnt)
+        srcs[t][torch.from_numpy(planted[sel] - do + so).cuda()] = H.to_dev16(g_pl[sel])
+    dev = Z.ShardStep(n, fused=True, any_order=True)
+    pl_dev = torch.from_numpy(planted).cuda()
+    dev.p32.fill_(float(p_common))
+    dev.p32[pl_dev] = torch.from_numpy(p_pl).cuda()
+    dev.p16.copy_(dev.p32.half())
+    dev.init_state(S)
+    dev.set_segments(srcs, segs, bucket)
+    assert len(dev.buckets) == 17 and dev.partial_count > 600_000
+
+    # the oracle's side: the sampled elements, and the common element alone
+    g_s = np.full(sample.size, c16, np.uint16)
+    g_s[:planted.size] = g_pl
+    p32_s = np.full(sample.size, p_common, np.float32)
+    p32_s[:planted.size] = p_pl
+    p16_s, m32_s, v32_s = shardgen.to_f16_bits(p32_s), np.zeros_like(p32_s), np.zeros_like(p32_s)
+    c_p32 = np.array([p_common], np.float32)
+    c_p16, c_m32, c_v32, c_g = shardgen.to_f16_bits(c_p32), np.zeros(1, np.float32), np.zeros(1, np.float32), \
+        np.array([c16], np.uint16)
+    exact = (n - planted.size) * _units16(c16) + sum(_units16(int(v)) for v in g_pl)
+    sumsq = float(Fraction(exact, 1 << 48))
+    hp_o, hp_d = O.hparams(max_grad_norm=0.3), Z.hparams(max_grad_norm=0.3)
+    ost = O.new_state(S)
+    it = torch.from_numpy(sample).cuda()
+    for k in range(2):
+        H.log(f"fused step n={n} (17 buckets, {dev.partial_count} partials) step {k + 1}")
+        dev.step(hp_d)
+        O.decide(ost, hp_o, sumsq, 0)
+        assert not ost.skip and ost.gmul < 1.0 / S                         # clipping is active
+        O.adam_update(ost, p16_s, p32_s, m32_s, v32_s, g_s)
+        O.adam_update(ost, c_p16, c_p32, c_m32, c_v32, c_g)
+        torch.cuda.synchronize()
+        H.compare_state(dev.read_state(), ost, exact)
+        assert np.array_equal(H.bits16(dev.p16[it]), p16_s)
+        for name, ref in (("p32", p32_s), ("m32", m32_s), ("v32", v32_s)):
+            got = getattr(dev, name)[it].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name
+        if k == 0:
+            assert np.array_equal(_where_not(dev.grad16.view(torch.int16), c16), planted), \
+                "flattened partition: the positions that differ from the common value are not the planted ones"
+            assert np.array_equal(H.bits16(dev.grad16[pl_dev]), g_pl)
+    for name, ref in (("p32", c_p32), ("m32", c_m32), ("v32", c_v32)):
+        off = _where_not(getattr(dev, name).view(torch.int32), int(ref.view(np.int32)[0]))
+        assert np.isin(off, planted).all(), f"{name}: {int((~np.isin(off, planted)).sum())} unplanted elements differ"
+    assert torch.equal(dev.p16.view(torch.int16), dev.p32.half().view(torch.int16))
+    assert dev.guard_intact()
+
+    st2 = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st2, S)
+    assert Z.zero_norm_workspace_bytes(n) >= 1025 * Z.NORM_PARTIAL_BYTES
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    H.log(f"standalone norm over the same partition, n={n}")
+    Z.zero_shard_norm_overflow(dev.grad16, n, hp_d, st2, ws)
+    ost2 = O.new_state(S)
+    O.decide(ost2, hp_o, sumsq, 0)
+    H.compare_state(Z.read_state(st2), ost2, exact)
+    del srcs, dev, ws, it, pl_dev
+    torch.cuda.empty_cache()
