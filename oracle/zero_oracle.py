@@ -138,8 +138,9 @@ def norm_overflow(g16: np.ndarray):
 
 
 def norm_overflow_f32(g32: np.ndarray):
-    """-> (sumsq, overflow) of a flat fp32 gradient: each square rounded to the
-    2^-48 grid, summed exactly, rounded once; |x| >= 2^24, inf, NaN overflow."""
+    """-> (sumsq, overflow) of a flat fp32 gradient: overflow = some element is
+    inf or NaN; sumsq = the exact sum of the exact squares, rounded once to
+    binary64 (any finite values)."""
     g32 = np.ascontiguousarray(g32, dtype=np.float32)
     s = C.c_double()
     o = C.c_int32()
