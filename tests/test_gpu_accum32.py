@@ -239,3 +239,89 @@ def test_accum_skip_and_resume():
         assert a.cpu().numpy().tobytes() == b.cpu().numpy().tobytes()
     H.step_accum(r)
     assert r.dev.read_state().step == 2
+
+
+def test_accum32_periodic_beyond_2_32_elements():
+    """Index arithmetic of the accumulation form past 2^32, checked over every
+    element: R = 2^20 copies of a K = 4099-element pattern (n = 4,298,113,024,
+    77 GB of state).  Two fp16 micro-batches, each from two sources (the first
+    read from offset 3 and gathered, the second aligned), are accumulated into
+    the fp32 partition in five any-order buckets; the last one's flatten takes
+    the exact-norm partials; decision with clipping off; update; two steps.
+    The exact sum is the pattern's times 2^20 and S/d, clip off, leaves every
+    decision field but the norm the pattern's, so every period of grad32, p32,
+    m32, v32 and p16 must equal the oracle's run on the pattern, bit for bit.
+    Then an off-grid binary32 pattern written into the partition sends the
+    standalone fp32 reduction (1,025 workgroups) to the wide pass over all n
+    values, whose rounded sum must be the pattern's exact sum times 2^20."""
+    K, R = 4099, 1 << 20
+    n = K * R
+    a = K << 18
+    assert n > (1 << 32) and a % 8 == 0
+    segs = [(0, 3, 0, a), (1, 0, a, n - a)]
+    S = 1024.0
+    rng = np.random.default_rng(96)
+    p32 = rng.normal(0.0, 0.02, K).astype(np.float32)
+    p16 = shardgen.to_f16_bits(p32)
+    m32, v32 = np.zeros(K, np.float32), np.zeros(K, np.float32)
+    hp_o, hp_d = O.hparams(max_grad_norm=0.0), Z.hparams(max_grad_norm=0.0)
+    st = O.new_state(S)
+
+    def same_as_pattern(d, ref):
+        for f in H.STATE_FIELDS:
+            assert getattr(d, f) == getattr(ref, f), f
+        for f in H.STEP_FIELDS:
+            if f not in ("sumsq", "grad_norm"):
+                assert np.float64(getattr(d, f)).tobytes() == np.float64(getattr(ref, f)).tobytes(), f
+        assert d.sumsq == ref.sumsq * 2.0 ** 20 and d.grad_norm == ref.grad_norm * 2.0 ** 10
+
+    def every_period(t, ref, tdt, ndt):
+        return torch.equal(t[:n].view(tdt).view(R, K), torch.from_numpy(ref.view(ndt)).cuda().expand(R, K))
+
+    torch.cuda.empty_cache()
+    dev = Z.AccumStep(n, fused=True)
+    dev.p32.view(R, K).copy_(torch.from_numpy(p32).cuda().expand(R, K))
+    dev.p16.copy_(dev.p32.half())
+    dev.init_state(S)
+    srcs = [[torch.empty(a + 3, dtype=torch.float16, device="cuda"),
+             torch.empty(n - a, dtype=torch.float16, device="cuda")] for _ in range(2)]
+    plans = [dev.plan(s, segs, 1 << 30)[1] for s in srcs]
+    assert all(len(p) == 5 for p in plans)
+    for k in range(2):
+        gs = [shardgen.to_f16_bits((rng.normal(0.0, 1e-4, K) * st.loss_scale).astype(np.float32)) for _ in srcs]
+        for (sa, sb), g in zip(srcs, gs):
+            gd = H.to_dev16(g)
+            sa[3:].view(a // K, K).copy_(gd.expand(a // K, K))
+            sb.view((n - a) // K, K).copy_(gd.expand((n - a) // K, K))
+        H.log(f"accum32 n={n} (period {K}) step {k + 1}: 2 micro-batches")
+        dev.step(plans, hp_d)
+        grad = np.zeros(K, np.float32)
+        for j, g in enumerate(gs):
+            O.flatten([g], [(0, 0, 0, K)], grad, accumulate=(j > 0))
+        sumsq, ovf = O.norm_overflow_f32(grad)
+        O.decide(st, hp_o, sumsq, ovf)
+        O.adam_update_f32(st, p16, p32, m32, v32, grad)
+        torch.cuda.synchronize()
+        same_as_pattern(dev.read_state(), st)
+        assert every_period(dev.grad32, grad, torch.int32, np.int32), "grad32"
+        for name, ref in (("p32", p32), ("m32", m32), ("v32", v32)):
+            assert every_period(getattr(dev, name), ref, torch.int32, np.int32), name
+        assert every_period(dev.p16, p16, torch.int16, np.int16), "p16"
+        assert dev.guard_intact()
+
+    off = _crafted_f32(K, 97)                           # most values off the 2^-24 grid
+    dev.grad32.view(R, K).copy_(torch.from_numpy(off).cuda().expand(R, K))
+    st2 = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st2, S)
+    assert Z.zero_norm_workspace_bytes(n) >= 1025 * Z.NORM_PARTIAL_BYTES
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    H.log(f"accum32 n={n}: standalone fp32 reduction of an off-grid pattern (wide pass)")
+    Z.zero_shard_norm_overflow_f32(dev.grad32, n, hp_d, st2, ws)
+    sumsq, ovf = O.norm_overflow_f32(off)
+    ref = O.new_state(S)
+    O.decide(ref, hp_o, sumsq, ovf)
+    d = Z.read_state(st2)
+    assert ovf == 0 and d.wide_pending == 0
+    same_as_pattern(d, ref)
+    del dev, srcs, ws
+    torch.cuda.empty_cache()

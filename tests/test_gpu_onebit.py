@@ -250,3 +250,83 @@ def test_onebit_non_finite_vector(case):
     assert np.array_equal(nan16(got16), nan16(want16))
     assert np.array_equal(got16[~nan16(got16)], want16[~nan16(want16)])
 
+
+
+
+def test_onebit_periodic_beyond_2_32_elements():
+    """Index arithmetic of the 1-bit stage past 2^32, checked over every
+    element: the shard is R = 2^20 copies of a K = 4099-element pattern
+    (n = 4,298,113,024, 104 GB of state), its gradient flattened in five
+    any-order buckets from two sources -- the first read from offset 3, so
+    gathered, the second aligned, so the vector path crosses 2^32.  With
+    clipping off, every decision field but the norm is the pattern's, the
+    exact sums of squares are the pattern's times 2^20 exactly, and S/d is the
+    pattern's quotient, so the scales are the pattern's too: every period of
+    p32, m32, v32, both error buffers, p16 and both sign payloads must equal
+    the oracle's run on the K-element pattern, bit for bit; sumsq and the norm
+    are the pattern's times 2^20 and 2^10.  One warm-up step, then two
+    compression steps."""
+    K, R = 4099, 1 << 20
+    n = K * R
+    a = K << 18                                      # a multiple of 8 and of K
+    assert n > (1 << 32) and n % 8 == 0 and a % 8 == 0
+    segs = [(0, 3, 0, a), (1, 0, a, n - a)]
+    S = 65536.0
+    rng = np.random.default_rng(95)
+    p32 = rng.normal(0.0, 0.02, K).astype(np.float32)
+    p16 = shardgen.to_f16_bits(p32)
+    m32, v32, ew, es = (np.zeros(K, np.float32) for _ in range(4))
+    hp_o, hp_d = O.hparams(max_grad_norm=0.0), Z.hparams(max_grad_norm=0.0)
+    st = O.new_state(S)
+
+    torch.cuda.empty_cache()
+    dev = Z.OneBitStep(n, warmup=1)
+    dev.p32.view(R, K).copy_(torch.from_numpy(p32).cuda().expand(R, K))
+    dev.p16.copy_(dev.p32.half())
+    dev.init_state(S)
+    src_a = torch.empty(a + 3, dtype=torch.float16, device="cuda")
+    src_b = torch.empty(n - a, dtype=torch.float16, device="cuda")
+    shifts = torch.arange(8, dtype=torch.uint8, device="cuda")
+
+    def every_period(t, ref, tdt, ndt):
+        """All R periods of t's first n elements equal ref, bit for bit."""
+        return torch.equal(t[:n].view(tdt).view(R, K), torch.from_numpy(ref.view(ndt)).cuda().expand(R, K))
+
+    for k in range(3):
+        g = shardgen.to_f16_bits((rng.normal(0.0, 1e-4, K) * st.loss_scale).astype(np.float32))
+        gd = H.to_dev16(g)
+        src_a[3:].view(a // K, K).copy_(gd.expand(a // K, K))
+        src_b.view((n - a) // K, K).copy_(gd.expand((n - a) // K, K))
+        if k == 0:
+            dev.set_segments([src_a, src_b], segs, 1 << 30)
+            assert len(dev.buckets) == 5
+        compress = st.step >= 1
+        H.log(f"onebit n={n} (period {K}) step {k + 1} compress={compress}")
+        dev.step(hp_d)
+        s, o = O.norm_overflow(g)
+        O.decide(st, hp_o, s, o)
+        if compress:
+            bw, bs, (sw, ss) = O.onebit_step(st, p16, p32, m32, v32, ew, es, g)
+        else:
+            O.adam_update(st, p16, p32, m32, v32, g)
+        torch.cuda.synchronize()
+        d = dev.read_state()
+        for f in H.STATE_FIELDS:
+            assert getattr(d, f) == getattr(st, f), f
+        for f in H.STEP_FIELDS:
+            if f not in ("sumsq", "grad_norm"):
+                assert np.float64(getattr(d, f)).tobytes() == np.float64(getattr(st, f)).tobytes(), f
+        assert d.sumsq == st.sumsq * 2.0 ** 20 and d.grad_norm == st.grad_norm * 2.0 ** 10
+        for name, ref in (("p32", p32), ("m32", m32), ("v32", v32), ("err_w", ew), ("err_s", es)):
+            assert every_period(getattr(dev, name), ref, torch.int32, np.int32), name
+        assert every_period(dev.p16, p16, torch.int16, np.int16), "p16"
+        if compress:
+            ob = dev.read_onebit()
+            assert (ob.scale_w, ob.scale_s) == (np.float32(sw), np.float32(ss))
+            for name, ref in (("bits_w", bw), ("bits_s", bs)):
+                got = ((getattr(dev, name)[:n // 8].unsqueeze(1) >> shifts) & 1).view(R, K)
+                want = torch.from_numpy(np.unpackbits(ref, bitorder="little")[:K]).cuda().expand(R, K)
+                assert torch.equal(got, want), name
+        assert dev.guard_intact()
+    del dev, src_a, src_b
+    torch.cuda.empty_cache()
