@@ -66,3 +66,40 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
     assert rc == -3                          # ZERO_ERANGE
     rc = Z.lib().zero_shard_norm_overflow_noalloc(g.data_ptr(), 16, None, st.data_ptr(), stream)
     assert rc == -1                          # ZERO_EINVAL
+
+
+def test_noalloc_at_its_largest_size():
+    """n = 2^30, the largest size the scratch array takes: 256 workgroups of
+    1024 threads, each thread summing its full 4096 values.  The partition is
+    0.5 everywhere but at planted positions (the ends, the last vector, and
+    random ones), so the exact sum is a closed form; both entry points give
+    the same state bytes, the 128-bit sum is the closed form, and the
+    decision is the oracle's."""
+    from fractions import Fraction
+    n = 1 << 30
+    rng = np.random.default_rng(71)
+    pos = np.unique(np.concatenate([np.array([0, 1, 7, 8, n - 9, n - 8, n - 1]), rng.integers(0, n, 64)]))
+    bits = rng.integers(0, 0x7C00, pos.size, dtype=np.uint16) | (rng.integers(0, 2, pos.size, dtype=np.uint16) << 15)
+    dg = torch.full((n,), 0.5, dtype=torch.float16, device="cuda")
+    dg[torch.from_numpy(pos).cuda()] = H.to_dev16(bits)
+
+    def units(b):                                   # x^2 in units of 2^-48 from the binary16 fields
+        f, m = (int(b) >> 10) & 31, int(b) & 1023
+        e = f - 25 if f else -24
+        return (m | (1024 if f else 0)) ** 2 << (2 * e + 48)
+    exact = (n - pos.size) * (1 << 46) + sum(units(b) for b in bits)
+    hp = Z.hparams()
+    st_ws = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    st_na = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st_ws, 2.0 ** 16)
+    Z.zero_step_state_init(st_na, 2.0 ** 16)
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    H.log(f"noalloc: n={n} (the largest size), closed-form sum")
+    Z.zero_shard_norm_overflow(dg, n, hp, st_ws, ws)
+    Z.zero_shard_norm_overflow_noalloc(dg, n, hp, st_na)
+    assert _state_bytes(st_ws) == _state_bytes(st_na)
+    ref = O.new_state(2.0 ** 16)
+    O.decide(ref, O.hparams(), float(Fraction(exact, 1 << 48)), 0)
+    H.compare_state(Z.read_state(st_na), ref, exact)
+    del dg, ws
+    torch.cuda.empty_cache()
