@@ -68,6 +68,45 @@ def test_decide_around_the_one_wave_fold(blocks):
     assert r.st.skipped_total == 1 and r.stats["fp32_not_bitwise"] == 0, r.stats
 
 
+
+@pytest.mark.parametrize("blocks", [1 << 15, (1 << 15) + 1])
+def test_decide_around_the_single_workgroup_limit(blocks):
+    """Up to 2^15 partials one workgroup folds them and decides with no
+    arrival counter; one more and the fold spreads over several workgroups
+    that meet at one.  One aligned segment of exactly `blocks` fused-flatten
+    workgroups, 0.5 everywhere but at planted positions (closed-form exact
+    sum); two decisions in a row (the counter re-arms), each against the
+    oracle bit for bit with the 128-bit sum, and equal, byte for byte, to the
+    standalone reduction's over the same partition."""
+    from fractions import Fraction
+    n = blocks * 6144
+    rng = np.random.default_rng(blocks)
+    pos = np.unique(np.concatenate([np.array([0, n - 1]), rng.integers(0, n, 40)]))
+    bits = (rng.integers(0, 0x7C00, pos.size, dtype=np.uint16)
+            | (rng.integers(0, 2, pos.size, dtype=np.uint16) << 15))
+    exact = (n - pos.size) * _units16(0x3800) + sum(_units16(int(b)) for b in bits)
+    src = torch.full((n,), 0.5, dtype=torch.float16, device="cuda")
+    src[torch.from_numpy(pos).cuda()] = H.to_dev16(bits)
+    dev = Z.ShardStep(n, fused=True)
+    dev.set_segments([src], [(0, 0, 0, n)])
+    assert dev.partial_count == blocks
+    st2 = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    hp = Z.hparams()
+    dev.init_state(65536.0)
+    Z.zero_step_state_init(st2, 65536.0)
+    ref = O.new_state(65536.0)
+    for k in range(2):
+        H.log(f"decide over {blocks} partials, call {k + 1}")
+        dev.flatten_norm()
+        dev.decide(hp)
+        Z.zero_shard_norm_overflow(dev.grad16, n, hp, st2, ws)
+        O.decide(ref, O.hparams(), float(Fraction(exact, 1 << 48)), 0)
+        torch.cuda.synchronize()
+        H.compare_state(dev.read_state(), ref, exact)
+        assert bytes(dev.state.cpu().numpy()) == bytes(st2.cpu().numpy())
+
+
 @pytest.mark.parametrize("any_order", [False, True])
 @pytest.mark.parametrize("fused", [False, True])
 def test_many_segments_over_launch_limit(fused, any_order):
