@@ -101,8 +101,10 @@ def test_onebit_tiny_warmup_then_compression():
     assert r.compressed == 5
 
 
-@pytest.mark.parametrize("n", [1, 7, 9, 4099, 65_536 * 3 + 5, (1 << 20) + 3])
+@pytest.mark.parametrize("n", [1, 7, 9, 4099, 65_536 * 3 + 5, (1 << 20) + 3, 1 << 22, (1 << 22) + 1])
 def test_onebit_ragged(n):
+    """Ragged sizes; 2^22 and 2^22 + 1 put the scale folds on either side of
+    one workgroup (2048 and 2049 per-workgroup window sums)."""
     r = OneBitRun(_small(f"onebit{n}", n, seed=500 + n), warmup=1)
     for _ in range(3):
         r.step()
