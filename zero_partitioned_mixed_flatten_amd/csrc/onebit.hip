@@ -24,7 +24,7 @@
 // return before any load and the ordinary update runs instead.
 //
 // Five kernels, because two global scales sit on the data path:
-//   A  momentum; per workgroup max|x| and window sum of x^2     one-shot, 8 elements per thread
+//   A  momentum; per workgroup max|x| and window sum of x^2     one-shot, 16 elements per thread
 //   B  fold of A's window sums: s_w                             a few workgroups, one round of loads
 //   C  worker compression: sign byte, ew, u = cw + es; per workgroup max|u| and window sum of u^2
 //   D  fold of C's window sums: s_s                             as B
@@ -35,18 +35,19 @@
 // registers, saves the two passes that read x and u back (12.125 bytes per
 // element).
 // Element layout of the one-shot kernels: the whole bytes of the sign payload
-// cover groups of 4 elements, g < 2*floor(n/8); thread t of workgroup b owns
-// groups 512b+t and 512b+t+256, so every vector load and store of a wave is
-// one contiguous span.  A thread's 4 sign bits of a group are a nibble; the
+// cover groups of 4 elements, g < 2*floor(n/8); thread t of workgroup b of E
+// owns groups 512b+t and 512b+t+256, of A and C groups 1024b+t+256k (k < 4),
+// so every vector load and store of a wave is one contiguous span.  A thread's 4 sign bits of a group are a nibble; the
 // two lanes of an even/odd pair hold the two nibbles of one byte and join
 // them with a lane shuffle.  The elements past the last whole byte (fewer
 // than 8) are done one by one.
 // The exact windowed square: z = x * 2^(40-E_b) (exact, |z| < 2^41),
 //   a = fma(z, z, C1) - C1       z^2 to a multiple of 2^41 (C1 = 1.5*2^93)
 //   b = (fma(z, z, -a) + C2) - C2   the rest, to the nearest integer (C2 = 1.5*2^52)
-// so z^2 rounded to an integer is a + b.  A lane adds at most 15 squares, so
-// a wave's sum(a) < 2^92 in steps of 2^41 and |sum(b)| < 2^50 fold across the
-// wave in binary64 without rounding; each wave's sums then become limbs.
+// so z^2 rounded to an integer is a + b.  A lane adds at most 23 squares (16,
+// and 7 of the ragged end), so a wave's sum(a) < 2^93 in steps of 2^41 and
+// |sum(b)| < 2^51 fold across the wave in binary64 without rounding; each
+// wave's sums then become limbs.
 #include <math.h>
 
 #include "decide.hpp"
@@ -68,6 +69,13 @@ constexpr int kBlock = 256;                  // one-shot kernels A, C, E
 // which the reservation leaves room for.
 constexpr int kOneShotCap = 2;
 constexpr int kOneShotCapAC = 4;
+// Groups of 4 elements per thread in A and C (E: 2).  Each of their
+// workgroups ends with a max, a window sum and a partial, paid once per
+// kGroupsAC * 1024 elements, and the folds read half as many partials as
+// with 2.  Measured on MI355X (gpt2 shard, one compression step, same box):
+// 2 groups 904 us, 3 908, 4 891-896 (kept), 8 920.
+constexpr int kGroupsAC = 4;
+static_assert(4 * kGroupsAC + 7 <= 64, "the binary64 wave fold of the window sums needs at most 64 squares per lane");
 constexpr double kWinHi = 0x1.8p93;          // ulp 2^41
 constexpr double kWinLo = 0x1.8p52;          // ulp 1
 
@@ -155,8 +163,9 @@ __device__ __forceinline__ uint32_t block_max_all(uint32_t v)
 }
 
 // The workgroup's window sum as a carried partial, valid in thread 0 (every
-// thread calls it).  A lane holds at most 15 squares, so each wave folds its
-// binary64 sums exactly (header note) before lane 0 turns them into limbs.
+// thread calls it).  A lane holds at most 4 * kGroupsAC + 7 squares (at most
+// 64 keep it exact), so each wave folds its binary64 sums exactly (header
+// note) before lane 0 turns them into limbs.
 __device__ __forceinline__ NormPartial window_partial(AccWin acc)
 {
 #pragma unroll
@@ -198,6 +207,18 @@ struct Groups {
     }
     __device__ bool both() const { return jb < ng; }
     __device__ bool first() const { return ja < ng; }
+};
+
+// The G groups of 4 elements a thread of A or C owns: j(k) = j0 + k * kBlock
+// (k < G), out of ng = 2*floor(n/8), so each load and store instruction of a
+// wave covers one contiguous span; the workgroup spans G * kBlock groups.
+template <int G>
+struct GroupsN {
+    uint64_t ng, j0;
+    __device__ explicit GroupsN(uint64_t n) : ng((n >> 3) * 2), j0(uint64_t(blockIdx.x) * (G * kBlock) + threadIdx.x) {}
+    __device__ uint64_t j(int k) const { return j0 + uint64_t(k) * kBlock; }
+    __device__ bool has(int k) const { return j(k) < ng; }
+    __device__ bool all() const { return has(G - 1); }
 };
 
 // Joins the sign nibbles of an even/odd lane pair into the byte of group j
@@ -242,46 +263,62 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
     if (n == UINT64_MAX)
         occupancy_reserve[threadIdx.x] = 0;
-    const Groups gr(n);
+    constexpr int G = kGroupsAC;
+    const GroupsN<G> gr(n);
     f32x4* __restrict__ M = reinterpret_cast<f32x4*>(m32);
     const f32x4* __restrict__ EW = reinterpret_cast<const f32x4*>(ew);
-    const u32x2* __restrict__ G = reinterpret_cast<const u32x2*>(g16);
+    const u32x2* __restrict__ GV = reinterpret_cast<const u32x2*>(g16);
     uint32_t mx = 0;
-    f32x4 xa{}, xb{};
+    f32x4 x[G] = {};
     float xr = 0.0f;
-    if (gr.both()) {
+    if (gr.all()) {
         // Every stream here is read once and m is written back in place:
         // nontemporal loads and stores throughout (the gradient alone: 5%
         // faster; m and e_w as well: the 1-bit stage 2.6% faster).
-        const u32x2 ga = __builtin_nontemporal_load(G + gr.ja), gb = __builtin_nontemporal_load(G + gr.jb);
-        f32x4 ma = __builtin_nontemporal_load(M + gr.ja), mb = __builtin_nontemporal_load(M + gr.jb);
-        const f32x4 ea = __builtin_nontemporal_load(EW + gr.ja), eb = __builtin_nontemporal_load(EW + gr.jb);
+        u32x2 g[G];
+        f32x4 m[G], e[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            g[k] = __builtin_nontemporal_load(GV + gr.j(k));
+            m[k] = __builtin_nontemporal_load(M + gr.j(k));
+            e[k] = __builtin_nontemporal_load(EW + gr.j(k));
+        }
         __builtin_amdgcn_sched_barrier(0);
         // the loads are out before the skip flag is read (see loads_first_use)
         if (st->skip) {
-            if (n == UINT64_MAX)
-                M[gr.ja] = ma + mb + ea + eb + bits_of(ga) + bits_of(gb);
+            if (n == UINT64_MAX) {
+                f32x4 t{};
+#pragma unroll
+                for (int k = 0; k < G; ++k)
+                    t += m[k] + e[k] + bits_of(g[k]);
+                M[gr.j(0)] = t;
+            }
             return;
         }
         const Coef c = coef_of(st);
-        momentum4(__builtin_bit_cast(f16x4, ga), ma, ea, c, xa, mx);
-        momentum4(__builtin_bit_cast(f16x4, gb), mb, eb, c, xb, mx);
-        __builtin_nontemporal_store(ma, M + gr.ja);
-        __builtin_nontemporal_store(mb, M + gr.jb);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            momentum4(__builtin_bit_cast(f16x4, g[k]), m[k], e[k], c, x[k], mx);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            __builtin_nontemporal_store(m[k], M + gr.j(k));
     } else {
         if (st->skip)
             return;
-        if (gr.first()) {
-            f32x4 ma = M[gr.ja];
-            momentum4(__builtin_bit_cast(f16x4, G[gr.ja]), ma, EW[gr.ja], coef_of(st), xa, mx);
-            M[gr.ja] = ma;
-        }
+        const Coef c = coef_of(st);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (gr.has(k)) {
+                f32x4 mk = M[gr.j(k)];
+                momentum4(__builtin_bit_cast(f16x4, GV[gr.j(k)]), mk, EW[gr.j(k)], c, x[k], mx);
+                M[gr.j(k)] = mk;
+            }
     }
     const bool ragged = blockIdx.x == 0 && threadIdx.x < (n & 7);
     if (ragged) {
 #pragma clang fp contract(off)
         const Coef c = coef_of(st);
-        const uint64_t i = gr.ragged0 + threadIdx.x;
+        const uint64_t i = ((n >> 3) << 3) + threadIdx.x;
         const float gk = float(__builtin_bit_cast(_Float16, g16[i])) * c.gmul;
         const float mi = c.b1 * m32[i] + c.omb1 * gk;
         m32[i] = mi;
@@ -294,12 +331,11 @@ __global__ __launch_bounds__(kBlock) void onebit_momentum_kernel(float* __restri
     AccWin acc;
     if (mx) {
         const double w = window_of(mx);
-        if (gr.first())
-            for (int k = 0; k < 4; ++k)
-                acc.add(xa[k], w);
-        if (gr.both())
-            for (int k = 0; k < 4; ++k)
-                acc.add(xb[k], w);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (gr.has(k))
+                for (int q = 0; q < 4; ++q)
+                    acc.add(x[k][q], w);
         if (ragged)
             acc.add(xr, w);
     }
@@ -477,40 +513,56 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
     extern __shared__ char occupancy_reserve[];  // see kOneShotCap
     if (n == UINT64_MAX)
         occupancy_reserve[threadIdx.x] = 0;
-    const Groups gr(n);
+    constexpr int G = kGroupsAC;
+    const GroupsN<G> gr(n);
     const f32x4* __restrict__ M = reinterpret_cast<const f32x4*>(m32);
     f32x4* __restrict__ EW = reinterpret_cast<f32x4*>(ew);
     const f32x4* __restrict__ ES = reinterpret_cast<const f32x4*>(es);
-    uint32_t mx = 0, nib_a = 0, nib_b = 0;
-    f32x4 ua{}, ub{};
-    if (gr.both()) {
+    uint32_t mx = 0, nib[G] = {};
+    f32x4 u[G] = {};
+    if (gr.all()) {
         // nontemporal throughout: e_w is rewritten in place, and a plain load
         // ahead of an in-place nontemporal store is the slow pattern
-        const f32x4 ma = __builtin_nontemporal_load(M + gr.ja), mb = __builtin_nontemporal_load(M + gr.jb);
-        f32x4 ea = __builtin_nontemporal_load(EW + gr.ja), eb = __builtin_nontemporal_load(EW + gr.jb);
-        const f32x4 sa = __builtin_nontemporal_load(ES + gr.ja), sb = __builtin_nontemporal_load(ES + gr.jb);
+        f32x4 m[G], e[G], sv[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            m[k] = __builtin_nontemporal_load(M + gr.j(k));
+            e[k] = __builtin_nontemporal_load(EW + gr.j(k));
+            sv[k] = __builtin_nontemporal_load(ES + gr.j(k));
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (st->skip) {                          // loads first (see loads_first_use)
-            if (n == UINT64_MAX)
-                EW[gr.ja] = ma + mb + ea + eb + sa + sb;
+            if (n == UINT64_MAX) {
+                f32x4 t{};
+#pragma unroll
+                for (int k = 0; k < G; ++k)
+                    t += m[k] + e[k] + sv[k];
+                EW[gr.j(0)] = t;
+            }
             return;
         }
         const float sw = ob->scale_w;
-        nib_a = compress4(ma, ea, sa, sw, ua, mx);
-        nib_b = compress4(mb, eb, sb, sw, ub, mx);
-        __builtin_nontemporal_store(ea, EW + gr.ja);
-        __builtin_nontemporal_store(eb, EW + gr.jb);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            nib[k] = compress4(m[k], e[k], sv[k], sw, u[k], mx);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            __builtin_nontemporal_store(e[k], EW + gr.j(k));
     } else {
         if (st->skip)
             return;
-        if (gr.first()) {
-            f32x4 ea = EW[gr.ja];
-            nib_a = compress4(M[gr.ja], ea, ES[gr.ja], ob->scale_w, ua, mx);
-            EW[gr.ja] = ea;
-        }
+        const float sw = ob->scale_w;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (gr.has(k)) {
+                f32x4 ek = EW[gr.j(k)];
+                nib[k] = compress4(M[gr.j(k)], ek, ES[gr.j(k)], sw, u[k], mx);
+                EW[gr.j(k)] = ek;
+            }
     }
-    store_byte_pair(bits_w, gr.ja, nib_a, gr.first());
-    store_byte_pair(bits_w, gr.jb, nib_b, gr.both());
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+        store_byte_pair(bits_w, gr.j(k), nib[k], gr.has(k));
     // the ragged last byte (fewer than 8 elements, one thread)
     const bool ragged = blockIdx.x == 0 && threadIdx.x == 0 && (n & 7);
     float ur[7] = {};
@@ -538,12 +590,11 @@ __global__ __launch_bounds__(kBlock) void onebit_compress_worker_kernel(const fl
     AccWin acc;
     if (mx) {
         const double w = window_of(mx);
-        if (gr.first())
-            for (int k = 0; k < 4; ++k)
-                acc.add(ua[k], w);
-        if (gr.both())
-            for (int k = 0; k < 4; ++k)
-                acc.add(ub[k], w);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (gr.has(k))
+                for (int q = 0; q < 4; ++q)
+                    acc.add(u[k][q], w);
         if (ragged)
 #pragma unroll
             for (int k = 0; k < 7; ++k)
@@ -721,7 +772,8 @@ __global__ void onebit_state_init_kernel(zero_onebit_state_t* ob)
 // Workspace: the per-workgroup maxima and window sums of A and of C, the
 // fold's per-workgroup maxima and sums, and the wide pass's partials.
 struct Plan {
-    uint64_t grid1;                 // one-shot kernels (A, C, E)
+    uint64_t grid1;                 // one-shot kernel E (2 groups of 4 per thread)
+    uint64_t grid_ac;               // one-shot kernels A and C (kGroupsAC groups of 4 per thread)
     uint64_t gridf;                 // the folds (B, D)
     uint64_t off_max_a, off_part_a, off_max_c, off_part_c, off_fmax, off_fpart, off_wide, bytes;
 };
@@ -732,17 +784,20 @@ Plan plan(uint64_t n)
     const uint64_t nvec = n >> 3;
     p.grid1 = (nvec + kBlock - 1) / kBlock;
     if (p.grid1 < 1) p.grid1 = 1;
+    const uint64_t ng = 2 * nvec, per_ac = uint64_t(kGroupsAC) * kBlock;
+    p.grid_ac = (ng + per_ac - 1) / per_ac;
+    if (p.grid_ac < 1) p.grid_ac = 1;
     // two window sums per thread (one round of loads) where that takes at most
     // 256 workgroups; eight per thread measured 1 us slower on the gpt2 shard
     const uint64_t per = uint64_t(kNormBlock) * 2;
-    p.gridf = (p.grid1 + per - 1) / per;
+    p.gridf = (p.grid_ac + per - 1) / per;
     if (p.gridf > kNormMaxBlocks) p.gridf = kNormMaxBlocks;
     auto up = [](uint64_t b) { return (b + 255) / 256 * 256; };
     p.off_max_a = 0;
-    p.off_part_a = p.off_max_a + up(p.grid1 * 4);
-    p.off_max_c = p.off_part_a + up(p.grid1 * sizeof(NormPartial));
-    p.off_part_c = p.off_max_c + up(p.grid1 * 4);
-    p.off_fmax = p.off_part_c + up(p.grid1 * sizeof(NormPartial));
+    p.off_part_a = p.off_max_a + up(p.grid_ac * 4);
+    p.off_max_c = p.off_part_a + up(p.grid_ac * sizeof(NormPartial));
+    p.off_part_c = p.off_max_c + up(p.grid_ac * 4);
+    p.off_fmax = p.off_part_c + up(p.grid_ac * sizeof(NormPartial));
     p.off_fpart = p.off_fmax + up(p.gridf * 4);
     p.off_wide = p.off_fpart + up(p.gridf * sizeof(NormPartial));
     p.bytes = p.off_wide + up(wide::grid(n) * sizeof(wide::WidePartial));
@@ -796,7 +851,7 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v3
     wide::WidePartial* part_w = reinterpret_cast<wide::WidePartial*>(ws + pl.off_wide);
     const dim3 gw(uint32_t(wide::grid(n)));
     hipStream_t s = (hipStream_t)stream;
-    const dim3 g1(uint32_t(pl.grid1)), gf(uint32_t(pl.gridf));
+    const dim3 g1(uint32_t(pl.grid1)), gac(uint32_t(pl.grid_ac)), gf(uint32_t(pl.gridf));
     const uint32_t cap = lds_reservation(kOneShotCap);
     const uint32_t cap_ac0 = lds_reservation(kOneShotCapAC);
     const uint32_t cap_ac = cap_ac0 > 512 ? cap_ac0 - 512 : 0;   // room for A's and C's static LDS
@@ -804,11 +859,11 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v3
     int rc = adam_step_gated(p16, p32, m32, v32, grad16, n, dev_state, stream, warmup);
     if (rc != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_momentum_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, grad16, n, dev_state,
+    hipLaunchKernelGGL(onebit_momentum_kernel, gac, dim3(kBlock), cap_ac, s, m32, err_w, grad16, n, dev_state,
                        warmup, max_a, part_a);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_scale_kernel<kWorker>, gf, dim3(kNormBlock), 0, s, max_a, part_a, pl.grid1, n,
+    hipLaunchKernelGGL(onebit_scale_kernel<kWorker>, gf, dim3(kNormBlock), 0, s, max_a, part_a, pl.grid_ac, n,
                        dev_state, warmup, dev_onebit, fmax, fpart);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
@@ -816,11 +871,11 @@ extern "C" int zero_onebit_step(uint16_t* p16, float* p32, float* m32, float* v3
                        WorkerValues{m32, err_w}, n, ScaleFinish<kWorker>{dev_onebit, n}, part_w);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_compress_worker_kernel, g1, dim3(kBlock), cap_ac, s, m32, err_w, err_s, bits_w, n,
+    hipLaunchKernelGGL(onebit_compress_worker_kernel, gac, dim3(kBlock), cap_ac, s, m32, err_w, err_s, bits_w, n,
                        dev_state, warmup, dev_onebit, max_c, part_c);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
-    hipLaunchKernelGGL(onebit_scale_kernel<kServer>, gf, dim3(kNormBlock), 0, s, max_c, part_c, pl.grid1, n,
+    hipLaunchKernelGGL(onebit_scale_kernel<kServer>, gf, dim3(kNormBlock), 0, s, max_c, part_c, pl.grid_ac, n,
                        dev_state, warmup, dev_onebit, fmax, fpart);
     if ((rc = launch_status()) != ZERO_OK)
         return rc;
