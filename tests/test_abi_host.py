@@ -293,3 +293,37 @@ def test_onebit_validation(Z):
     assert L.zero_onebit_state_init(0, None) == E.ZERO_EINVAL
     assert L.zero_onebit_state_init(FAKE + 4, None) == E.ZERO_EALIGN
     assert C.sizeof(Z.OneBitState) == 72
+
+
+def test_buckets_overlap_check_against_pairwise_model(Z):
+    """The multi-bucket call's overlap check (sorted by start, neighbours
+    compared) against a brute-force pairwise model on random segment sets cut
+    into random buckets: any two nonempty segments sharing a destination
+    element -> ZERO_EINVAL; a segment past the destination -> ZERO_ERANGE
+    (the range check runs first).  Only sets that must be rejected are
+    passed, so nothing is launched."""
+    from hypothesis import HealthCheck, given, settings, strategies as hs
+    L, E = Z.lib(), Z._lib
+
+    def overlaps(segs):
+        live = [(d, d + c) for d, c in segs if c]
+        return any(a0 < b1 and b0 < a1 for i, (a0, a1) in enumerate(live) for b0, b1 in live[i + 1:])
+
+    @settings(max_examples=300, deadline=None, suppress_health_check=list(HealthCheck))
+    @given(hs.lists(hs.tuples(hs.integers(0, 300), hs.integers(0, 40)), min_size=1, max_size=12),
+           hs.integers(1, 4), hs.integers(0, 2 ** 32 - 1))
+    def check(segs, nbuckets, cut_seed):
+        n = 256
+        if not overlaps(segs) and all(d + c <= n for d, c in segs if c):
+            return                                           # a valid set would launch: not here
+        rng = np.random.default_rng(cut_seed)
+        cuts = np.sort(rng.integers(0, len(segs) + 1, nbuckets - 1))
+        counts = np.diff(np.concatenate([[0], cuts, [len(segs)]])).astype(np.uint32)
+        arr, k = Z.make_segments([(FAKE, 0, d, c) for d, c in segs])
+        cnt = (C.c_uint32 * len(counts))(*counts.tolist())
+        want = E.ZERO_ERANGE if any(d + c > n for d, c in segs if c) else E.ZERO_EINVAL
+        for part in (0, FAKE):
+            rc = L.zero_flatten_buckets(arr, cnt, len(counts), FAKE, n, Z.ZERO_F16, 0, part, 1 << 20, None)
+            assert rc == want, (segs, counts.tolist(), rc, want)
+
+    check()
