@@ -347,15 +347,16 @@ def test_standalone_norm_multi_workgroup_fold(dtype):
         H.compare_state(s, ost, None)
 
 
-def test_standalone_norm_beyond_256_workgroups():
+@pytest.mark.parametrize("n,grid", [((1 << 30) + 1, 257), ((1 << 31) + 12345, 513)])
+def test_standalone_norm_beyond_256_workgroups(n, grid):
     """Above 2^30 elements the standalone norm's grid grows past one
-    workgroup per CU (no thread sums more than 4096 values): 513 workgroups
-    here, whose partials the last workgroup folds in three batches.  The
+    workgroup per CU (no thread sums more than 4096 values): 257 workgroups
+    at 2^30 + 1 (the last workgroup folds the partials in two batches, the
+    second holding one) and 513 at 2^31 + 12,345 (three batches).  The
     partition is one value everywhere but at planted positions, so its exact
     sum is a closed form; the 128-bit sum, its rounding and the decision must
     match it bit for bit."""
     from fractions import Fraction
-    n = (1 << 31) + 12345
     rng = np.random.default_rng(92)
     pos = np.unique(rng.integers(0, n, 64))
     bits = rng.integers(0, 0x7C00, pos.size, dtype=np.uint16) | (rng.integers(0, 2, pos.size, dtype=np.uint16) << 15)
@@ -368,12 +369,12 @@ def test_standalone_norm_beyond_256_workgroups():
         return (m | (1024 if f else 0)) ** 2 << (2 * e + 48)
     exact = (n - pos.size) * (1 << 46) + sum(units(b) for b in bits)
     ws = torch.empty(Z.zero_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
-    assert Z.zero_norm_workspace_bytes(n) >= 513 * Z.NORM_PARTIAL_BYTES
+    assert Z.zero_norm_workspace_bytes(n) >= grid * Z.NORM_PARTIAL_BYTES
     st = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
     Z.zero_step_state_init(st, 65536.0)
     ost = O.new_state(65536.0)
     for k in range(2):
-        H.log(f"standalone norm n={n} (513 workgroups) call {k}")
+        H.log(f"standalone norm n={n} ({grid} workgroups) call {k}")
         Z.zero_shard_norm_overflow(dev, n, Z.hparams(), st, ws)
         O.decide(ost, O.hparams(), float(Fraction(exact, 1 << 48)), 0)
         s = Z.read_state(st)
