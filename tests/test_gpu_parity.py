@@ -107,6 +107,37 @@ def test_decide_around_the_single_workgroup_limit(blocks):
         assert bytes(dev.state.cpu().numpy()) == bytes(st2.cpu().numpy())
 
 
+
+@pytest.mark.parametrize("case", ["never_grow", "no_backoff", "floor", "unit_growth"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_loss_scaler_edge_settings(case, fused):
+    """The dynamic loss scaler at the edges of its settings, stepped against
+    the oracle with overflows injected at steps 2, 3 (a NaN), 4 and 9:
+    growth_interval 0 (the scale never grows), backoff 1 (an overflow skips
+    the step and keeps the scale), a floor above 1 (repeated overflows stop
+    at min_scale), growth 1 every clean step (a growth that leaves the scale
+    unchanged).  Every state field bitwise each step, and the trajectory the
+    setting implies."""
+    from dataclasses import replace
+    w = _small(f"scaler-{case}", 20_003, seed=60)
+    settings = {"never_grow": dict(growth_interval=0), "no_backoff": dict(backoff=1.0),
+                "floor": dict(min_scale=2.0 ** 14), "unit_growth": dict(growth=1.0, growth_interval=1)}[case]
+    w.hp = replace(w.hp, **settings)
+    w.scale0 = 2.0 ** 16
+    w.inject = {2: shardgen.F16_POS_INF, 3: shardgen.F16_NAN_SENTINEL, 4: shardgen.F16_POS_INF,
+                9: shardgen.F16_POS_INF}
+    r = H.start(w, fused=fused)
+    scales = []
+    for _ in range(12):
+        H.step(r)
+        scales.append(r.dev.read_state().loss_scale)
+    assert r.st.skipped_total == 4 and r.st.step == 8
+    want = {"never_grow": 2.0 ** 12, "no_backoff": 2.0 ** 16, "floor": 2.0 ** 14, "unit_growth": 2.0 ** 12}[case]
+    assert scales[-1] == want, scales
+    if case != "no_backoff":
+        assert all(b <= a for a, b in zip(scales, scales[1:])), scales       # never grows
+
+
 @pytest.mark.parametrize("any_order", [False, True])
 @pytest.mark.parametrize("fused", [False, True])
 def test_many_segments_over_launch_limit(fused, any_order):
