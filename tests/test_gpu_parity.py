@@ -295,6 +295,47 @@ def test_fp16_copy_rounding_sweep():
     assert np.array_equal(H.bits16(dev.p16), O.f16_from_f32(p))
 
 
+
+@pytest.mark.parametrize("bits", [0x0000, 0x8000])
+@pytest.mark.parametrize("fused", [False, True])
+def test_all_zero_gradient(bits, fused):
+    """A gradient of +0.0 (or -0.0) everywhere, clipping on: the exact sum is
+    0, the norm 0 and the clip coefficient 1 (the threshold over a zero norm
+    never reaches the state), m and v stay zero and the update is the weight
+    decay alone.  Three steps on a ragged shard in three segments; every
+    state field, p16 and p32/m32/v32 over the whole shard, bit for bit,
+    against the oracle."""
+    n = 70_001
+    rng = np.random.default_rng(61)
+    segs = [(0, 0, 0, 20_000), (1, 3, 20_000, 30_001), (0, 20_000, 50_001, 20_000)]
+    g = np.full(n, bits, np.uint16)
+    srcs = [np.full(40_000, bits, np.uint16), np.full(30_004, bits, np.uint16)]
+    p32 = rng.normal(0.0, 0.02, n).astype(np.float32)
+    p16, m32, v32 = shardgen.to_f16_bits(p32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    dev = Z.ShardStep(n, fused=fused)
+    dev.p32.copy_(torch.from_numpy(p32))
+    dev.p16.copy_(torch.from_numpy(p16.view(np.float16)))
+    dev.init_state(65536.0)
+    dsrcs = [H.to_dev16(x) for x in srcs]
+    dev.set_segments(dsrcs, segs)
+    hp_o, hp_d = O.hparams(max_grad_norm=1.0), Z.hparams(max_grad_norm=1.0)
+    st = O.new_state(65536.0)
+    for k in range(3):
+        H.log(f"zero gradient {bits:#06x} fused={fused} step {k + 1}")
+        dev.step(hp_d)
+        s, o = O.norm_overflow(g)
+        assert (s, o) == (0.0, 0)
+        O.decide(st, hp_o, s, o)
+        O.adam_update(st, p16, p32, m32, v32, g)
+        torch.cuda.synchronize()
+        H.compare_state(dev.read_state(), st, 0)
+        assert np.array_equal(H.bits16(dev.grad16), g)
+        assert np.array_equal(H.bits16(dev.p16), p16)
+        for name, ref in (("p32", p32), ("m32", m32), ("v32", v32)):
+            assert np.array_equal(getattr(dev, name).cpu().numpy().view(np.uint32), ref.view(np.uint32)), name
+    assert st.gmul == np.float32(1.0 / 65536.0) and not m32.any() and not v32.any()
+
+
 def test_skip_and_resume_bitwise():
     w = _small("resume", 100_000, seed=9)
     w.inject = {2: 0xFC00}
