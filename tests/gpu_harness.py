@@ -154,18 +154,39 @@ def start(w: shardgen.Workload, sample: Optional[int] = None, seed: int = 77, fu
 
 def step(r: Run, check: bool = True, check_full_cast: bool = True, exact: bool = True) -> dict:
     """One step on both sides; returns a few timings/values for the log."""
+    pending = prepare(r)
+    enqueue(r, pending)
+    return finish(r, pending, check, check_full_cast, exact)
+
+
+def prepare(r: Run) -> tuple:
+    """The next step's gradient sources, drawn on the host and uploaded
+    (synchronously) to the device."""
     r.k += 1
-    k, w = r.k, r.w
     t0 = time.time()
-    gpart = shardgen.grad_partition(w, k, r.st.loss_scale)
-    srcs = shardgen.source_tensors(w.layout, gpart)
+    gpart = shardgen.grad_partition(r.w, r.k, r.st.loss_scale)
+    srcs = shardgen.source_tensors(r.w.layout, gpart)
     del gpart
     dsrcs = [to_dev16(s) for s in srcs]
-    t1 = time.time()
-    log(f"{w.name} n={w.n} step {k}: launch (segments={len(w.layout.segments)}, bucket={w.bucket_elems}, "
+    return srcs, dsrcs, t0, time.time()
+
+
+def enqueue(r: Run, pending: tuple, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """The device step on `stream` (torch's current stream if None); returns
+    without waiting."""
+    w, dsrcs = r.w, pending[1]
+    log(f"{w.name} n={w.n} step {r.k}: launch (segments={len(w.layout.segments)}, bucket={w.bucket_elems}, "
         f"fused={r.dev.fused})")
-    r.dev.set_segments(dsrcs, w.layout.segments, w.bucket_elems)
-    r.dev.step(r.hp_d)
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        r.dev.set_segments(dsrcs, w.layout.segments, w.bucket_elems)
+        r.dev.step(r.hp_d)
+
+
+def finish(r: Run, pending: tuple, check: bool = True, check_full_cast: bool = True, exact: bool = True) -> dict:
+    """The oracle's side of the step, a device-wide synchronisation, and the
+    comparison."""
+    srcs, dsrcs, t0, t1 = pending
+    k, w = r.k, r.w
     # oracle: its own flatten of the same sources, then the exact reduction and decision
     grad = np.empty(w.n, np.uint16)
     O.flatten(srcs, w.layout.segments, grad)

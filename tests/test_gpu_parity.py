@@ -336,6 +336,33 @@ def test_all_zero_gradient(bits, fused):
     assert st.gmul == np.float32(1.0 / 65536.0) and not m32.any() and not v32.any()
 
 
+
+def test_two_shards_on_two_streams():
+    """Calls on different streams with disjoint buffers may run at once: two
+    shards (the fused path in five any-order buckets, and the separate path)
+    are prepared first, then enqueued back to back on two streams of default
+    priority, so that their kernels overlap on the GPU; three steps, with an
+    overflow on the second step of the second shard.  Each matches the
+    oracle as if it ran alone (sampled p/m/v, the whole flattened gradient,
+    the state and p16 = fp16(p32) over the whole shard)."""
+    w1 = _small("streams-a", 24_000_011, seed=81)
+    w1.bucket_elems = 5_000_000
+    w2 = _small("streams-b", 20_000_003, seed=82)
+    w2.inject = {2: shardgen.F16_POS_INF}
+    r1 = H.start(w1, sample=1 << 16, fused=True)
+    r2 = H.start(w2, sample=1 << 16, fused=False)
+    torch.cuda.synchronize()                       # the set-up, on the default stream, is done
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        p1, p2 = H.prepare(r1), H.prepare(r2)
+        H.enqueue(r1, p1, s1)
+        H.enqueue(r2, p2, s2)
+        H.finish(r1, p1)
+        H.finish(r2, p2)
+    assert r1.st.skipped_total == 0 and r2.st.skipped_total == 1 and r2.st.step == 2
+    assert r1.stats["fp32_not_bitwise"] == 0 and r2.stats["fp32_not_bitwise"] == 0
+
+
 def test_skip_and_resume_bitwise():
     w = _small("resume", 100_000, seed=9)
     w.inject = {2: 0xFC00}
