@@ -103,3 +103,42 @@ def test_noalloc_at_its_largest_size():
     H.compare_state(Z.read_state(st_na), ref, exact)
     del dg, ws
     torch.cuda.empty_cache()
+
+
+def test_noalloc_under_graph_capture():
+    """Code under HIP graph capture is one of the callers this entry point is
+    for: the call is captured once (after one eager call, which looks up the
+    scratch array's address) and replayed four times, with new gradient
+    values copied in eagerly between the replays (an inf in one of them);
+    after each replay the state equals, byte for byte, that of the workspace
+    form run eagerly on a twin state."""
+    n = 3 * (1 << 20) + 7
+    hp = Z.hparams()
+    st_g = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    st_e = torch.zeros(Z.STATE_BYTES, dtype=torch.uint8, device="cuda")
+    dg = torch.zeros(n, dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(16, Z.zero_norm_workspace_bytes(n)), dtype=torch.uint8, device="cuda")
+    Z.zero_step_state_init(st_g, 2.0 ** 16)
+    Z.zero_shard_norm_overflow_noalloc(dg, n, hp, st_g)          # eager: the one-time address lookup
+    Z.zero_step_state_init(st_g, 2.0 ** 16)
+    Z.zero_step_state_init(st_e, 2.0 ** 16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            Z.zero_shard_norm_overflow_noalloc(dg, n, hp, st_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert Z.read_state(st_g).step == 0                          # capturing ran nothing
+    for k in range(4):
+        g16 = _grad(n, 200 + k, (777_777, 0x7C00) if k == 2 else None)
+        dg.copy_(H.to_dev16(g16))
+        torch.cuda.synchronize()
+        H.log(f"noalloc graph replay {k + 1}")
+        g.replay()
+        Z.zero_shard_norm_overflow(dg, n, hp, st_e, ws)
+        a, b = _state_bytes(st_e), _state_bytes(st_g)
+        assert a == b, f"replay {k + 1}: states differ"
+    assert Z.read_state(st_g).skipped_total == 1
