@@ -320,6 +320,7 @@ def test_buckets_overlap_check_against_pairwise_model(Z):
         cuts = np.sort(rng.integers(0, len(segs) + 1, nbuckets - 1))
         counts = np.diff(np.concatenate([[0], cuts, [len(segs)]])).astype(np.uint32)
         arr, k = Z.make_segments([(FAKE, 0, d, c) for d, c in segs])
+        assert k == len(segs) == int(counts.sum())
         cnt = (C.c_uint32 * len(counts))(*counts.tolist())
         want = E.ZERO_ERANGE if any(d + c > n for d, c in segs if c) else E.ZERO_EINVAL
         for part in (0, FAKE):
