@@ -451,7 +451,7 @@ size_t zero_onebit_workspace_bytes(uint64_t n);
  * sgn(x) = +1 for x >= 0 (zeros too), -1 otherwise; bit k of byte j of a
  * bits array is element 8j+k, 1 for +1.  S(x) = fp32(sqrt(sum/n)) with the
  * sum of squares exact and rounded once to binary64.  The fast sum works in
- * windows: each workgroup of 2048 elements rounds its squares to multiples
+ * windows: each workgroup of 4096 elements rounds its squares to multiples
  * of 2^(2E_b-80), 2^E_b <= its max|x| < 2^(E_b+1), and a fold moves those
  * integer sums onto the window of the largest E_b, rounding each to the
  * nearest unit; it keeps the result when the binary64 rounding is the same
