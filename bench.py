@@ -51,7 +51,7 @@ WIDEN_BYTES = 6          # read fp16 source, write fp32 partition
 ACCUM_BYTES = 10         # read fp16 source and fp32 partition, write fp32 partition
 # 1-bit Adam compression stage, per parameter: momentum (with the worker window
 # sums) 14, worker compression (with the server window sums) 16 + 1/8, server
-# compression + update 26 + 1/4; the two folds read a few bytes per 2048
+# compression + update 26 + 1/4; the two folds read a few bytes per 4096
 ONEBIT_BYTES = 14 + 16.125 + 26.25
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "zero_partitioned_mixed_flatten_amd", "csrc")

@@ -195,9 +195,9 @@ __device__ __forceinline__ NormPartial window_partial(AccWin acc)
 // The window of a block maximum given as bits: 2^(40-E).
 __device__ __forceinline__ double window_of(uint32_t mx) { return ldexp(1.0, 40 - exponent_of(mx)); }
 
-// The two groups of 4 elements a thread of a one-shot kernel owns (see the
-// layout note above), out of ng = 2*floor(n/8); ragged0 = 4*ng is the first
-// element done one by one.
+// The two groups of 4 elements a thread of E owns (see the layout note
+// above; A and C take GroupsN), out of ng = 2*floor(n/8); ragged0 = 4*ng is
+// the first element done one by one.
 struct Groups {
     uint64_t ng, ja, jb, ragged0;
     __device__ explicit Groups(uint64_t n)
